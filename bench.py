@@ -1,0 +1,343 @@
+"""Benchmark of the NVFP4-forward / MXFP8-backward expert-layer hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of the small MoE layer
+workload (4096 tokens, d_model 1024, 8 experts, top-2 uniform routing, FFN
+1024 -> 2048, bf16 inputs; backward at the same shapes with dY ~ N(0, 1e-6)):
+
+  nvfp4_quantize(X, per token) -> nvfp4_quantize(W, per expert) -> moe_permute
+  -> moe_fwd_grouped_gemm -> mxfp8_requant_sr(X_perm) -> mxfp8_requant_sr(W)
+  -> mxfp8_quantize(dY, row-wise) -> mxfp8_quantize(dY, grouped column-wise)
+  -> moe_bwd_dgrad -> moe_bwd_wgrad
+
+Inputs are seeded synthetic tensors already resident in HBM. `value` is the
+step's GEMM work (forward + dgrad + wgrad FLOPs) divided by the step time, in
+TFLOP/s; per-kernel times (HIP events on the launch stream), rates and
+fractions of MI355X peaks are reported beside it, together with the expert-
+share forward GEMMs (48 local experts, 32768 tokens top-8 Zipf), the decode
+GEMMs and the 1 GiB streaming quantize/requant.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--cpu-seconds S]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 MoE grouped-GEMM fwd TFLOPS + quant/requant GB/s, % of MI355X peak"
+PEAK = {"fp4": 10.1e15, "fp8": 5.0e15, "f16": 2.5e15, "hbm": 8.0e12}
+
+# algorithmic bytes per element
+B_QUANT_BF16 = 2 + 0.5 + 1 / 16          # bf16 in, NVFP4 codes + scales out
+B_REQUANT = 0.5 + 1 / 16 + 1 + 1 / 32    # NVFP4 in, MXFP8 out
+B_DYQ = 2 + 1 + 1 / 32                   # bf16 in, MXFP8 out (one orientation)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="0 skips the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def dev_tensor(a, torch):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+class Timer:
+    """HIP events on the current (launch) stream around named stages."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.ev.setdefault(name, []).append((s, e))
+
+    def ms(self):
+        return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.ev.items()}
+
+
+def main_step_bench(args, torch):
+    from precision_moe_numerics_nvfp4_amd.layer import ExpertLayerStep
+    from workloads import gen
+
+    w = gen.small_moe()
+    T, K, N, E, k = w["T"], w["K"], w["N"], w["E"], w["k"]
+    dy = gen.backward_dy(T * k, N)
+    L = ExpertLayerStep(T, K, N, E, k)
+    x_d, w_d = dev_tensor(w["x"], torch), dev_tensor(w["w"], torch)
+    t_d, dy_d = dev_tensor(w["topk"], torch), dev_tensor(dy, torch)
+
+    stages = [
+        ("nvfp4_quantize_x", lambda: L.quantize_x(x_d)),
+        ("nvfp4_quantize_w", lambda: L.quantize_w(w_d)),
+        ("moe_permute", lambda: L.permute(t_d)),
+        ("moe_fwd_grouped_gemm", L.forward_gemm),
+        ("mxfp8_requant_sr_x", L.requant_x),
+        ("mxfp8_requant_sr_w", L.requant_w),
+        ("mxfp8_quantize_dy", lambda: L.quantize_dy(dy_d)),
+        ("moe_bwd_dgrad", L.dgrad),
+        ("moe_bwd_wgrad", L.wgrad),
+    ]
+    for _ in range(args.warmup):
+        L.step(x_d, w_d, t_d, dy_d)
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` whole steps, bracketed by device syncs
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L.step(x_d, w_d, t_d, dy_d)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    # per-stage times: a second pass with events around each stage
+    tm = Timer(torch)
+    for _ in range(args.steps):
+        for name, fn in stages:
+            tm.run(name, fn)
+    torch.cuda.synchronize()
+    st = tm.ms()
+
+    M = T * k   # top-k distinct experts, all local
+    gemm_flop = 2.0 * M * N * K
+    work = {
+        "nvfp4_quantize_x": ("hbm", T * K * B_QUANT_BF16 + 4 * T),
+        "nvfp4_quantize_w": ("hbm", E * N * K * B_QUANT_BF16 + 4 * E),
+        "moe_permute": ("hbm", 4 * T * k + 8 * M + 2 * M * (K * (0.5 + 1 / 16) + 4)),
+        "moe_fwd_grouped_gemm": ("fp4", gemm_flop),
+        "mxfp8_requant_sr_x": ("hbm", M * K * B_REQUANT),
+        "mxfp8_requant_sr_w": ("hbm", E * N * K * B_REQUANT),
+        "mxfp8_quantize_dy": ("hbm", 2 * M * N * B_DYQ),
+        "moe_bwd_dgrad": ("fp8", gemm_flop),
+        "moe_bwd_wgrad": ("fp8", gemm_flop),
+    }
+    kernels = {}
+    for name, (kind, amount) in work.items():
+        sec = st[name] * 1e-3
+        if kind == "hbm":
+            kernels[name] = {"ms": round(st[name], 4), "GB/s": round(amount / sec / 1e9, 1),
+                             "frac_hbm": round(amount / sec / PEAK["hbm"], 4)}
+        else:
+            rate = amount / sec
+            kernels[name] = {"ms": round(st[name], 4), "TFLOP/s": round(rate / 1e12, 1),
+                             f"frac_{kind}_peak": round(rate / PEAK[kind], 4)}
+            if kind == "fp4":
+                kernels[name]["frac_f16_pipe"] = round(rate / PEAK["f16"], 4)
+    dom = max(st, key=lambda n: st[n])
+    kind, amount = work[dom]
+    sec = st[dom] * 1e-3
+    if kind == "hbm":
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / sec / 1e9, 1),
+                "peak": 8000.0, "unit": "GB/s", "frac": round(amount / sec / PEAK["hbm"], 4),
+                "traffic": None, "algorithmic_bytes_per_launch": amount}
+    else:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(amount / sec / 1e12, 2),
+                "peak": PEAK[kind] / 1e12, "unit": "TFLOP/s",
+                "frac": round(amount / sec / PEAK[kind], 4), "traffic": None,
+                "algorithmic_flop_per_launch": amount, "operand_dtype": kind}
+    value = 3 * gemm_flop / (ms_step * 1e-3) / 1e12
+    cfg = {"workload": "small MoE layer, forward + backward: 4096 tokens, d_model 1024, 8 experts, "
+                       "top-2 uniform routing, FFN up-projection 1024->2048, bf16 inputs; "
+                       "backward at the same shapes, dY ~ N(0, 1e-6)",
+           "tokens": T, "d_model": K, "ffn": N, "experts": E, "top_k": k, "routed_rows": M}
+    return dict(value=value, ms_step=ms_step, kernels=kernels, roofline=roof, config=cfg,
+                inputs=(w, dy))
+
+
+def _time(torch, fn, reps):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def extras(torch, reps=10):
+    import precision_moe_numerics_nvfp4_amd as nv
+    from workloads import gen
+    out = {}
+    # expert share: 48 of 384 experts local, 32768 tokens, top-8 Zipf, 4096 -> 1536 -> 4096
+    w3 = gen.expert_share()
+    T, K, F, E = w3["T"], w3["K"], w3["N"], w3["E"]
+    x = dev_tensor(w3["x"], torch)
+    w1, w2 = dev_tensor(w3["w1"], torch), dev_tensor(w3["w2"], torch)
+    topk = dev_tensor(w3["topk"], torch)
+    del w3
+    xq = nv.nvfp4_quantize(x)
+    w1q = nv.nvfp4_quantize(w1, rows_per_group=F)
+    w2q = nv.nvfp4_quantize(w2, rows_per_group=K)
+    perm = nv.moe_permute(topk, 144, E, *xq)
+    torch.cuda.synchronize()
+    M = int(perm["offsets"][-1].item())
+    h = dev_tensor(gen.expert_share_hidden(M, F), torch)       # stand-in for act(Y1), [M, F]
+    hq = nv.nvfp4_quantize(h)
+    y1 = torch.empty((T * 8, F), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    t1 = _time(torch, lambda: nv.moe_fwd_grouped_gemm(perm["codes"], perm["scales"], perm["outer"],
+                                                      *w1q, perm["offsets"], y=y1), reps)
+    t2 = _time(torch, lambda: nv.moe_fwd_grouped_gemm(*hq, *w2q, perm["offsets"], y=y2), reps)
+    tq = _time(torch, lambda: nv.nvfp4_quantize(x, None, *xq), reps)
+    tp = _time(torch, lambda: nv.moe_permute(topk, 144, E, *xq, out=perm), reps)
+    fl = 2.0 * M * F * K
+    out["expert_share_fwd"] = {
+        "routed_rows_local": M,
+        "gemm1_4096x1536": {"ms": round(t1, 4), "TFLOP/s": round(fl / t1 / 1e9, 1),
+                            "frac_fp4_peak": round(fl / t1 / 1e-3 / PEAK["fp4"], 4),
+                            "frac_f16_pipe": round(fl / t1 / 1e-3 / PEAK["f16"], 4)},
+        "gemm2_1536x4096": {"ms": round(t2, 4), "TFLOP/s": round(fl / t2 / 1e9, 1),
+                            "frac_fp4_peak": round(fl / t2 / 1e-3 / PEAK["fp4"], 4),
+                            "frac_f16_pipe": round(fl / t2 / 1e-3 / PEAK["f16"], 4)},
+        "quantize_x_32768x4096": {"ms": round(tq, 4),
+                                  "GB/s": round(T * K * B_QUANT_BF16 / tq / 1e6, 1)},
+        "permute_gather": {"ms": round(tp, 4)},
+    }
+    del x, w1, w2, h, xq, w1q, hq, perm, y1, y2
+    torch.cuda.empty_cache()
+    # decode: 512 tokens top-8 uniform over 384, 48 local, weights pre-quantized
+    w5 = gen.decode()
+    x5 = dev_tensor(w5["x"], torch)
+    topk5 = dev_tensor(w5["topk"], torch)
+    w1q = nv.nvfp4_quantize(dev_tensor(w5["w1"], torch), rows_per_group=F)
+    w2q5 = nv.nvfp4_quantize(dev_tensor(w5["w2"], torch), rows_per_group=K)
+    xq5 = nv.nvfp4_quantize(x5)
+    perm5 = nv.moe_permute(topk5, 144, E, *xq5)
+    torch.cuda.synchronize()
+    M5 = int(perm5["offsets"][-1].item())
+    hq5 = nv.nvfp4_quantize(dev_tensor(gen.expert_share_hidden(M5, F, cfg=5), torch))
+    yd1 = torch.empty((512 * 8, F), dtype=torch.bfloat16, device="cuda")
+    yd2 = torch.empty((M5, K), dtype=torch.bfloat16, device="cuda")
+    td = _time(torch, lambda: (nv.moe_fwd_grouped_gemm(perm5["codes"], perm5["scales"], perm5["outer"],
+                                                       *w1q, perm5["offsets"], y=yd1),
+                               nv.moe_fwd_grouped_gemm(*hq5, *w2q5, perm5["offsets"], y=yd2)), reps)
+    wbytes = 2 * E * F * K * (0.5 + 1 / 16)
+    out["decode_fwd"] = {"routed_rows_local": M5, "ms_both_gemms": round(td, 4),
+                         "weight_GB/s": round(wbytes / td / 1e6, 1),
+                         "frac_hbm": round(wbytes / td / 1e-3 / PEAK["hbm"], 4)}
+    del w1q, w2q5, hq5, yd1, yd2, perm5, xq5, x5
+    torch.cuda.empty_cache()
+    # streaming: 1 GiB bf16 [262144 x 2048] per-token quantize, then requant of its transpose
+    rows, cols = 262144, 2048
+    xs = dev_tensor(gen.streaming(rows, cols), torch)
+    q = nv.nvfp4_quantize(xs)
+    off = torch.tensor([0, rows], dtype=torch.int64, device="cuda")
+    o8 = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+    e8 = torch.empty((cols, rows // 32), dtype=torch.uint8, device="cuda")
+    tq = _time(torch, lambda: nv.nvfp4_quantize(xs, None, *q), reps)
+    tr = _time(torch, lambda: nv.mxfp8_requant_sr(*q, off, off, rows, 0x5EED0005, 2, out=o8, out_e8=e8),
+               reps)
+    n = rows * cols
+    out["streaming_1GiB"] = {
+        "quantize": {"ms": round(tq, 4), "GB/s": round(n * B_QUANT_BF16 / tq / 1e6, 1),
+                     "frac_hbm": round(n * B_QUANT_BF16 / tq / 1e-3 / PEAK["hbm"], 4)},
+        "requant_sr": {"ms": round(tr, 4), "GB/s": round(n * B_REQUANT / tr / 1e6, 1),
+                       "frac_hbm": round(n * B_REQUANT / tr / 1e-3 / PEAK["hbm"], 4)},
+    }
+    return out
+
+
+def cpu_baseline(inputs, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the first T_s tokens (same widths, experts, routing and dY recipe)."""
+    from oracle import gemm as GM
+    from oracle import mxfp8 as MX
+    from oracle import nvfp4 as Q
+    from oracle import permute as PM
+    w, dy = inputs
+    K, N, E, k = w["K"], w["N"], w["E"], w["k"]
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    def run(T_s):
+        x = w["x"][:T_s]
+        topk = w["topk"][:T_s]
+        t0 = time.perf_counter()
+        xc, xs, xo = Q.quantize(x)
+        wc, ws, wo = Q.quantize(w["w"], rows_per_group=N)
+        off, pad, rt, rs = PM.permute(topk, 0, E)
+        ac, asc, ao = PM.gather_rows(rt, xc, xs, xo)
+        GM.fwd_grouped(ac, asc, ao, wc, ws, wo, off, N)
+        P = int(pad[-1])
+        xq8, xe8 = MX.requant_sr(ac, asc, ao, off, pad, P, 0x5EED0004, 0)
+        woff = np.arange(E + 1) * N
+        wq8, we8 = MX.requant_sr(wc, ws, wo, woff, woff, E * N, 0x5EED0004, 1, rows_per_group=N)
+        M = int(off[-1])
+        dys = dy[:M]
+        dq, de = MX.quantize_rowwise(dys)
+        dtq, dte = MX.quantize_colwise_grouped(dys, off, pad, P)
+        GM.dgrad_grouped(dq, de, wq8, we8, off, N)
+        GM.wgrad_grouped(dtq, dte, xq8, xe8, pad)
+        return time.perf_counter() - t0, M
+
+    # a 512-token probe sizes the sample so the timed run takes about budget_s
+    dt0, _ = run(512)
+    T_s = 512
+    while T_s * 2 <= w["T"] and dt0 * (T_s * 2) / 512 <= budget_s:
+        T_s *= 2
+    dt, M = run(T_s)
+    flop = 3 * 2.0 * M * N * K
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {T_s} of {w['T']} tokens ({M} routed rows) of the same workload, whole "
+                      f"step (weight quantize/requant at full size), {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+                                   "(the expert-parallel design is described, not built)"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from precision_moe_numerics_nvfp4_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from precision_moe_numerics_nvfp4_amd import build as _b
+        _b.build()
+    print("bench: small MoE layer step", file=sys.stderr, flush=True)
+    r = main_step_bench(args, torch)
+    line = {
+        "metric": METRIC, "value": round(r["value"], 3), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4-fwd/mxfp8-bwd, f32 accumulate", "data": "synthetic",
+        "config": r["config"], "roofline": r["roofline"], "kernels": r["kernels"],
+    }
+    if not args.no_extra:
+        print("bench: expert-share, decode and streaming extras", file=sys.stderr, flush=True)
+        line["extra"] = extras(torch)
+    if args.cpu_seconds > 0:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(r["inputs"], args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

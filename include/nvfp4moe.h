@@ -1,0 +1,230 @@
+/*
+ * nvfp4moe.h -- C ABI of the native 4-bit MoE expert layer for AMD MI355X (gfx950).
+ *
+ * The method (Thinking Machines, "End-to-End 4-Bit Training"; cited by the title
+ * and section of the page that describes each step):
+ *   forward:  NVFP4-quantize activations (one FP32 outer scale per token) and
+ *             expert weights (one per expert), group routed tokens by expert,
+ *             run the expert grouped GEMM on the NVFP4 operands;
+ *   backward: dequantize the saved NVFP4 activations and weights, transpose in
+ *             float32, re-quantize to MXFP8 with stochastic rounding, quantize
+ *             dY to MXFP8, run the dgrad and wgrad grouped GEMMs in MXFP8.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or synchronises; it validates arguments on the host, then
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *     returns. Results are ready when the stream reaches that point.
+ *   - Row-major everywhere; dimensions are int64_t element counts.
+ *   - Argument errors return before any HIP call (NVFP4MOE_EINVAL for null
+ *     pointers, negative sizes and bad enums; NVFP4MOE_EUNSUPPORTED for sizes or
+ *     alignments the kernels do not handle). Launch failures return
+ *     NVFP4MOE_EHIP. Faults inside kernels surface at the caller's next sync.
+ *   - Inputs must be finite (no NaN/Inf); this is a precondition, not checked.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Group offsets (`offsets`, `padded_offsets`) live on the device: they are
+ *     produced by moe_permute and never copied to the host, so grids are sized
+ *     for the capacity (`m_cap`, `P`) and kernels read the real extents.
+ *   - Calls are stateless apart from a per-process device-property cache, and
+ *     may be issued concurrently on different streams with disjoint outputs.
+ *
+ * Formats (NVFP4 and MXFP8 as named on "Inkling 2 Small uses four-bit
+ * training ..." (ai-primer), section "Block scales and per-token activations"):
+ *   NVFP4  codes  uint8 [rows, cols/2]: E2M1 (sign|2-bit exponent|1-bit
+ *                 mantissa), element 2j in bits 3..0, element 2j+1 in bits 7..4;
+ *          scales uint8 [rows, cols/16]: OCP E4M3FN, one per 16 consecutive
+ *                 elements of a row;
+ *          outer  float [rows] (per token) or [groups] (per expert).
+ *          value = e2m1 * scale * outer.
+ *   MXFP8  elems  uint8 [rows, cols]: OCP E4M3FN;
+ *          scales uint8 [rows, cols/32]: E8M0 (2^(c-127)), one per 32
+ *                 consecutive elements of a row.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4MOE_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define NVFP4MOE_API __attribute__((visibility("default")))
+#else
+#define NVFP4MOE_API
+#endif
+
+enum nvfp4moe_status {
+    NVFP4MOE_OK = 0,
+    NVFP4MOE_EINVAL = 1,        /* null pointer, negative size, unknown enum */
+    NVFP4MOE_EUNSUPPORTED = 2,  /* size/alignment not handled by the kernels */
+    NVFP4MOE_EWORKSPACE = 3,    /* workspace smaller than required */
+    NVFP4MOE_EHIP = 4           /* a HIP launch/runtime call failed */
+};
+
+enum nvfp4moe_dtype { NVFP4MOE_F32 = 0, NVFP4MOE_BF16 = 1 };
+
+enum nvfp4moe_outer_mode { NVFP4MOE_OUTER_PER_ROW = 0, NVFP4MOE_OUTER_PER_GROUP = 1 };
+
+enum nvfp4moe_orientation { NVFP4MOE_ROWWISE = 0, NVFP4MOE_COLWISE_GROUPED = 1 };
+
+/* Version of this ABI (NVFP4MOE_ABI_VERSION). */
+NVFP4MOE_API int nvfp4moe_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+NVFP4MOE_API const char* nvfp4moe_status_string(int status);
+
+/*
+ * NVFP4 quantization of activations (per token) or weights (per expert).
+ * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), section
+ * "Block scales and per-token activations": 16 values share one E4M3 scale;
+ * an FP32 outer scale per expert for weights and per token for activations.
+ *
+ * x        [rows, cols] float32 (x_dtype NVFP4MOE_F32) or bfloat16 (NVFP4MOE_BF16).
+ * outer_mode NVFP4MOE_OUTER_PER_ROW: one outer scale per row, outer[rows].
+ *          NVFP4MOE_OUTER_PER_GROUP: each run of rows_per_group rows (one
+ *          expert of a weight stored [E*N, K] with rows_per_group = N) shares
+ *          one, outer[rows/rows_per_group]; outer doubles as scratch.
+ * Per group of rows: A = max|x|; s = A/2688; block scale
+ * S = E4M3_RNE(max|x_block| / (6*s)) (saturating); code = E2M1_RNE(x * (1/(S*s)))
+ * (saturating); A == 0 or S == 0 gives signed-zero codes; outer = s.
+ * codes [rows, cols/2], scales [rows, cols/16], outer as above.
+ * Requires cols % 32 == 0 (EUNSUPPORTED otherwise); rows may be 0.
+ */
+NVFP4MOE_API int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                   int outer_mode, int64_t rows_per_group,
+                   uint8_t* codes, uint8_t* scales, float* outer, void* stream);
+
+/* Bytes of device workspace moe_permute needs for T tokens, top-k, n_local experts. */
+NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int k, int n_local);
+
+/*
+ * Token-to-expert grouping and gather of the NVFP4 activation rows.
+ * Pages: "Thinking Machines' Inkling 2 Small Trains a 594B Model in 68 Hours"
+ * (hermes-ai), section "594B weights, 17B at work" (8 of 384 experts per token);
+ * "Inkling 2 Small uses four-bit training ..." (ai-primer), section "Quantized
+ * NVLink and BBBK" (tokens reach their experts already in NVFP4).
+ *
+ * topk_ids [T, k] int32 expert ids; ids outside [e0, e0+n_local) are not local
+ * and are dropped. Outputs (device):
+ *   offsets[n_local+1]        int64, exclusive scan of rows per local expert;
+ *   padded_offsets[n_local+1] int64, exclusive scan of rows rounded up to 32;
+ *   row_token[T*k], row_slot[T*k] int32: row r < offsets[n_local] holds pair
+ *     (token, slot); rows of one expert are ordered by t*k+slot ascending;
+ *   xperm_codes [T*k, K/2], xperm_scales [T*k, K/16], xperm_outer [T*k]: the
+ *     NVFP4 row of row_token[r] copied to row r.
+ * Entries at or beyond offsets[n_local] are left untouched.
+ * workspace: device memory of at least nvfp4moe_permute_workspace_size() bytes.
+ * Requires K % 32 == 0, 1 <= n_local <= 1024, 1 <= k <= 64.
+ */
+NVFP4MOE_API int moe_permute(const int32_t* topk_ids, int64_t T, int k, int e0, int n_local,
+                const uint8_t* xq_codes, const uint8_t* xq_scales, const float* xq_outer,
+                int64_t K,
+                int64_t* offsets, int64_t* padded_offsets,
+                int32_t* row_token, int32_t* row_slot,
+                uint8_t* xperm_codes, uint8_t* xperm_scales, float* xperm_outer,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * NVFP4 forward grouped GEMM.
+ * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), section
+ * "NVFP4 forward, MXFP8 backward" (expert-layer matmuls in NVFP4).
+ *
+ * a_*: X_perm NVFP4 [m_cap, K] with per-row outer a_outer[m_cap];
+ * b_*: W NVFP4 stored [G, N, K] (K contiguous) with per-expert outer b_outer[G];
+ * offsets[G+1] (device): rows [offsets[g], offsets[g+1]) use expert g.
+ * y [m_cap, N], y_dtype NVFP4MOE_F32 or NVFP4MOE_BF16 (round to nearest even):
+ *   y[r, n] = a_outer[r] * b_outer[g] * sum_k (e2m1*S)_A[r,k] * (e2m1*S)_B[g,n,k]
+ * with exact products and float32 accumulation. Rows >= offsets[G] untouched.
+ * Requires N % 128 == 0, K % 128 == 0, offsets[G] <= m_cap.
+ */
+NVFP4MOE_API int moe_fwd_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                         const uint8_t* b_codes, const uint8_t* b_scales, const float* b_outer,
+                         const int64_t* offsets, int G, int64_t m_cap, int64_t N, int64_t K,
+                         void* y, int y_dtype, void* stream);
+
+/*
+ * Backward re-quantization of a saved NVFP4 tensor: dequantize (float32) ->
+ * grouped transpose -> MXFP8 with stochastic rounding.
+ * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), section
+ * "Stochastic rounding across transposes".
+ *
+ * codes/scales/outer: NVFP4 [rows, cols]; outer_mode/rows_per_group as in
+ *   nvfp4_quantize (per row for activations, per group for weights).
+ * offsets[G+1], padded_offsets[G+1] (device int64): input rows
+ *   [offsets[g], offsets[g+1]) become output columns starting at
+ *   padded_offsets[g]; columns up to the next multiple of 32 are zero. For a
+ *   weight [E*N, K] use offsets = padded_offsets = {0, N, 2N, ...} (N % 32 == 0).
+ * out_e4m3 [cols, P], out_e8m0 [cols, P/32]; P is the row pitch (P % 32 == 0,
+ *   P >= padded_offsets[G]); columns >= padded_offsets[G] are untouched.
+ * Block of 32 along the output row: e = smallest exponent with
+ *   max|v| <= 448*2^e (clamped to [-127,127]); y = v*2^-e; element rounded to
+ *   E4M3 stochastically with the 16-bit draw of Philox4x32-10 keyed by
+ *   (seed lo, seed hi), counter (q lo, q hi, tag, 0), q = idx>>3, for the
+ *   output's linear index idx = col*P + p (half idx&1 of word (idx&7)>>1).
+ * Requires cols % 128 == 0.
+ */
+NVFP4MOE_API int mxfp8_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                     int outer_mode, int64_t rows_per_group, int64_t rows, int64_t cols,
+                     const int64_t* offsets, const int64_t* padded_offsets, int G, int64_t P,
+                     uint64_t seed, uint32_t tag,
+                     uint8_t* out_e4m3, uint8_t* out_e8m0, void* stream);
+
+/*
+ * MXFP8 quantization of the output gradient dY with round-to-nearest-even.
+ * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), section
+ * "NVFP4 forward, MXFP8 backward" (gradients computed with MXFP8 matmuls).
+ *
+ * x [rows, cols] float32 or bfloat16.
+ * NVFP4MOE_ROWWISE: out_e4m3 [rows, cols], out_e8m0 [rows, cols/32] (blocks along
+ *   cols); offsets/padded_offsets/G/P ignored.
+ * NVFP4MOE_COLWISE_GROUPED: out_e4m3 [cols, P], out_e8m0 [cols, P/32], the same
+ *   grouped transpose and padding as mxfp8_requant_sr.
+ * Block exponent as in mxfp8_requant_sr; elements E4M3 round-to-nearest-even.
+ * Requires cols % 128 == 0.
+ */
+NVFP4MOE_API int mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int orientation,
+                   const int64_t* offsets, const int64_t* padded_offsets, int G, int64_t P,
+                   uint8_t* out_e4m3, uint8_t* out_e8m0, void* stream);
+
+/*
+ * MXFP8 dgrad grouped GEMM (contraction over N).
+ * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), sections
+ * "NVFP4 forward, MXFP8 backward" and "Stochastic rounding across transposes".
+ *
+ * dy: MXFP8 [m_cap, N] (blocks along N); w: MXFP8 [K, G*N] (requantized weight,
+ * blocks along G*N); offsets[G+1] (device).
+ * dx[r, k] = sum_n dy[r, n] * w[k, g*N + n] for rows r of group g, float32
+ * accumulation; dx [m_cap, K] float32 or bfloat16; rows >= offsets[G] untouched.
+ * Requires N % 128 == 0, K % 128 == 0.
+ */
+NVFP4MOE_API int moe_bwd_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0,
+                  const uint8_t* w_e4m3, const uint8_t* w_e8m0,
+                  const int64_t* offsets, int G, int64_t m_cap, int64_t N, int64_t K,
+                  void* dx, int dx_dtype, void* stream);
+
+/*
+ * MXFP8 wgrad grouped GEMM (contraction over the tokens of each expert).
+ * Pages: as moe_bwd_dgrad.
+ *
+ * dyT: MXFP8 [N, P] (grouped transpose of dY); xT: MXFP8 [K, P] (requantized
+ * activations); padded_offsets[G+1] (device).
+ * dw[g, n, k] = sum over p in [padded_offsets[g], padded_offsets[g+1]) of
+ * dyT[n, p] * xT[k, p], float32 accumulation; dw [G, N, K] float32 (the stored
+ * weight layout). Groups with no tokens get zeros.
+ * Requires N % 128 == 0, K % 128 == 0, P % 32 == 0.
+ */
+NVFP4MOE_API int moe_bwd_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0,
+                  const uint8_t* xT_e4m3, const uint8_t* xT_e8m0,
+                  const int64_t* padded_offsets, int G, int64_t P, int64_t N, int64_t K,
+                  float* dw, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MOE_H */

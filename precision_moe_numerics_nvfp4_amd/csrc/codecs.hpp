@@ -1,0 +1,181 @@
+// Device codecs for the NVFP4 / MXFP8 expert layer on gfx950.
+//
+// Formats are the ones named on "Inkling 2 Small uses four-bit training ..."
+// (ai-primer), section "Block scales and per-token activations": E2M1 elements
+// with an E4M3 scale per 16 (NVFP4), E4M3 elements with an E8M0 scale per 32
+// (MXFP8). Every routine is exact integer/float bit manipulation whose result
+// is fixed by IEEE binary32 arithmetic (no fused multiply-add is relied on;
+// the library is compiled with -ffp-contract=off), so results are identical
+// on any conforming implementation of the same rules.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4moe {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t f2u(float x) { return __float_as_uint(x); }
+
+// 16-byte streaming load (read once: non-temporal hint).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float u2f(uint32_t x) { return __uint_as_float(x); }
+
+// bfloat16 bit pattern -> float32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return u2f(h << 16); }
+
+// float32 -> bfloat16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = f2u(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ----------------------------------------------------------------- E2M1
+
+// Magnitude and sign of a 4-bit E2M1 code as float32 (exact).
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t m = c & 7u;
+  // codes 2..7 are normal: exponent 126 + (m >> 1), mantissa bit m & 1,
+  // which is the bit pattern (m << 22) + 0x3F000000; codes 0 and 1 are 0, 0.5
+  const uint32_t nrm = (m << 22) + 0x3F000000u;
+  const uint32_t mag = (m >= 2u) ? nrm : (m == 1u ? 0x3F000000u : 0u);
+  return u2f(mag | ((c & 8u) << 28));
+}
+
+// Round to the nearest E2M1 value (ties to the even code), saturating at 6.
+// The code's sign bit is the sign bit of y (so -0 and tiny negatives give 8).
+// The thresholds are the midpoints of neighbouring grid values; a midpoint
+// goes to the neighbour whose code is even.
+__device__ __forceinline__ uint32_t e2m1_rne(float y) {
+  const float a = fabsf(y);
+  uint32_t m = (a > 0.25f) ? 1u : 0u;
+  m += (a >= 0.75f) ? 1u : 0u;
+  m += (a > 1.25f) ? 1u : 0u;
+  m += (a >= 1.75f) ? 1u : 0u;
+  m += (a > 2.5f) ? 1u : 0u;
+  m += (a >= 3.5f) ? 1u : 0u;
+  m += (a > 5.0f) ? 1u : 0u;
+  return m | ((f2u(y) >> 28) & 8u);
+}
+
+// ----------------------------------------------------------------- E4M3
+
+// Value of a non-negative E4M3FN code (0..0x7E) as float32 (exact).
+__device__ __forceinline__ float e4m3_pos_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float sub = (float)m * 0.001953125f;            // m * 2^-9, exact
+  const float nrm = u2f(((e + 120u) << 23) | (m << 20));
+  return e ? nrm : sub;
+}
+
+// Round a non-negative float32 to E4M3FN, nearest-even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_rne_sat_pos(float t) {
+  if (t >= 448.0f) return 0x7Eu;
+  if (t < 0.015625f)                                     // below 2^-6: step 2^-9
+    return (uint32_t)__builtin_rintf(t * 512.0f);      // 0..8, exact product
+  uint32_t b = f2u(t);
+  b += 0x7FFFFu + ((b >> 20) & 1u);                     // round mantissa to 3 bits
+  return (b >> 20) - (120u << 3);                       // rebias exponent 127 -> 7
+}
+
+// Round |y| <= 448 to E4M3FN, nearest-even; sign from y.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t b = f2u(y);
+  const uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3C800000u) {
+    code = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);
+  } else {
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  code = code < 0x7Eu ? code : 0x7Eu;
+  return code | ((b >> 24) & 0x80u);
+}
+
+// Stochastic rounding of |y| <= 448 to E4M3FN with a 16-bit draw u.
+// With lo the grid value at or below |y| and D = (|y| - lo) / gap, the value
+// rounds up iff u + floor(D * 2^16) >= 2^16. Both ranges reduce to one
+// fixed-point form v = (code_of_lo << 16) | floor(D * 2^16):
+//   below 2^-6 (grid step 2^-9): v = floor(|y| * 2^25);
+//   above: the float32 bits shifted right by 4 and rebiased.
+// The result is then (v + u) >> 16. Sign from y.
+__device__ __forceinline__ uint32_t e4m3_sr(float y, uint32_t u) {
+  const uint32_t b = f2u(y);
+  const uint32_t a = b & 0x7FFFFFFFu;
+  const uint32_t vs = (uint32_t)(u2f(a) * 33554432.0f);  // truncating convert
+  const uint32_t vn = (a >> 4) - (960u << 16);
+  const uint32_t v = (a < 0x3C800000u) ? vs : vn;
+  return ((v + u) >> 16) | ((b >> 24) & 0x80u);
+}
+
+// ----------------------------------------------------------------- E8M0
+
+// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 gives -127.
+__device__ __forceinline__ int e8m0_ceil(float amax) {
+  const uint32_t b = f2u(amax);
+  if (b < 0x00800000u) return -127;                     // zero or subnormal
+  const int E = (int)(b >> 23) - 127;
+  const int e = ((b & 0x7FFFFFu) <= 0x600000u) ? E - 8 : E - 7;   // m <= 1.75
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^-e as float32 for e in [-127, 120] (always a normal number).
+__device__ __forceinline__ float exp2_neg(int e) { return u2f((uint32_t)(127 - e) << 23); }
+
+// ----------------------------------------------------------------- Philox
+
+struct Philox4 {
+  uint32_t w0, w1, w2, w3;
+};
+
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, SC'11): each round
+// multiplies words 0 and 2 by the two round constants into 64-bit products and
+// mixes their halves with words 1 and 3 and the key; the key is bumped by the
+// two Weyl constants between rounds.
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return Philox4{c0, c1, c2, c3};
+}
+
+// The eight 16-bit draws for output indices 8q .. 8q+7 (index 8q+i is half
+// i&1 of word i>>1, low half first), keyed by (seed, tag).
+struct Draws8 {
+  uint32_t w[4];
+  __device__ __forceinline__ uint32_t get(int i) const {
+    return (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+  }
+};
+
+__device__ __forceinline__ Draws8 draws8(uint64_t q, uint64_t seed, uint32_t tag) {
+  const Philox4 p = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), tag, 0u,
+                                  (uint32_t)seed, (uint32_t)(seed >> 32));
+  return Draws8{{p.w0, p.w1, p.w2, p.w3}};
+}
+
+// ----------------------------------------------------------------- misc
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace nvfp4moe

@@ -1,0 +1,61 @@
+// Launchers shared between the C-ABI layer (api.hip) and the kernel files.
+// Each launcher assumes its arguments were validated by the C-ABI layer and
+// only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4moe {
+
+// quant.hip
+hipError_t launch_nvfp4_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                 bool per_group, int64_t rows_per_group, uint8_t* codes,
+                                 uint8_t* scales, float* outer, hipStream_t stream);
+hipError_t launch_mxfp8_quantize_rowwise(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                         uint8_t* out_e4m3, uint8_t* out_e8m0,
+                                         hipStream_t stream);
+
+// permute.hip
+size_t permute_workspace_bytes(int64_t T, int k, int n_local);
+hipError_t launch_permute(const int32_t* topk_ids, int64_t T, int k, int e0, int n_local,
+                          const uint8_t* xq_codes, const uint8_t* xq_scales,
+                          const float* xq_outer, int64_t K, int64_t* offsets,
+                          int64_t* padded_offsets, int32_t* row_token, int32_t* row_slot,
+                          uint8_t* xperm_codes, uint8_t* xperm_scales, float* xperm_outer,
+                          void* workspace, hipStream_t stream);
+
+// requant.hip: grouped-transpose MXFP8 quantizers
+hipError_t launch_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                             int64_t rows_per_group /* 0 = per row */, int64_t rows,
+                             int64_t cols, const int64_t* offsets,
+                             const int64_t* padded_offsets, int G, int64_t P, uint64_t seed,
+                             uint32_t tag, uint8_t* out_e4m3, uint8_t* out_e8m0,
+                             hipStream_t stream);
+hipError_t launch_mxfp8_quantize_colwise(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                         const int64_t* offsets,
+                                         const int64_t* padded_offsets, int G, int64_t P,
+                                         uint8_t* out_e4m3, uint8_t* out_e8m0,
+                                         hipStream_t stream);
+
+// gemm_fwd.hip
+hipError_t launch_fwd_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const float* a_outer, const uint8_t* b_codes,
+                                   const uint8_t* b_scales, const float* b_outer,
+                                   const int64_t* offsets, int G, int64_t m_cap, int64_t N,
+                                   int64_t K, void* y, bool y_bf16, hipStream_t stream);
+
+// gemm_bwd.hip
+hipError_t launch_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0, const uint8_t* w_e4m3,
+                        const uint8_t* w_e8m0, const int64_t* offsets, int G, int64_t m_cap,
+                        int64_t N, int64_t K, void* dx, bool dx_bf16, hipStream_t stream);
+hipError_t launch_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0,
+                        const uint8_t* xT_e4m3, const uint8_t* xT_e8m0,
+                        const int64_t* padded_offsets, int G, int64_t P, int64_t N, int64_t K,
+                        float* dw, hipStream_t stream);
+
+// Number of workgroups that fill the device (compute units x wgs_per_cu).
+int device_cu_count();
+
+}  // namespace nvfp4moe

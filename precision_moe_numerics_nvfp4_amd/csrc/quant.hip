@@ -1,0 +1,277 @@
+// NVFP4 quantization (per token / per expert) and row-wise MXFP8 quantization.
+//
+// NVFP4, after "Inkling 2 Small uses four-bit training ..." (ai-primer),
+// section "Block scales and per-token activations": per outer-scale group
+// A = max|x|, s = A / 2688, block scale S = E4M3_RNE(max|x_block| / (6 s)),
+// codes E2M1_RNE(x * (1 / (S s))). One wavefront owns one row: each lane owns
+// whole 16-element blocks (16 consecutive bfloat16 = 32 contiguous bytes, so
+// consecutive lanes read consecutive bytes), the row maximum is a wavefront
+// shuffle reduction, and every block is packed to 8 bytes of codes plus one
+// scale byte without leaving registers. For per-expert scales a first pass
+// reduces max|x| over each expert with one atomic max per workgroup (the
+// outer-scale buffer holds the float bits meanwhile), then the quantizer runs
+// with that maximum, then a tiny pass stores s = A / 2688.
+//
+// MXFP8 row-wise (dY, "NVFP4 forward, MXFP8 backward"): four lanes share one
+// 32-element block (8 elements each), reduce the block maximum with two
+// shuffles, pick the smallest exponent that keeps the block inside 448 and
+// round each element to nearest-even E4M3.
+#include "codecs.hpp"
+#include "internal.hpp"
+
+namespace nvfp4moe {
+
+namespace {
+
+template <bool BF16>
+struct Row16 {  // 16 consecutive input elements held as raw words
+  static constexpr int W = BF16 ? 8 : 16;
+  uint32_t w[W];
+  __device__ __forceinline__ float get(int j) const {
+    if constexpr (BF16) return (j & 1) ? u2f(w[j >> 1] & 0xFFFF0000u) : u2f(w[j >> 1] << 16);
+    else return u2f(w[j]);
+  }
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load16(const void* base, int64_t elem, Row16<BF16>& r) {
+  if constexpr (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    const uint4 a = ld_stream16(p), b = ld_stream16(p + 1);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 a = ld_stream16(p + i);
+      r.w[4 * i] = a.x; r.w[4 * i + 1] = a.y; r.w[4 * i + 2] = a.z; r.w[4 * i + 3] = a.w;
+    }
+  }
+}
+
+// One wavefront per row, 4 rows per workgroup; lane l owns blocks l, l+64, ...
+// gamax != nullptr: per-group mode, A is read from the group-max pass.
+template <bool BF16, int BPL>
+__global__ __launch_bounds__(256) void k_nvfp4_quantize(
+    const void* __restrict__ x, int64_t rows, int nb, const uint32_t* __restrict__ gamax,
+    int64_t rpg, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ outer) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // uniform per wavefront
+
+  Row16<BF16> v[BPL];
+  float bmax[BPL];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = lane + 64 * i;
+    bmax[i] = 0.0f;
+    if (b < nb) {
+      load16<BF16>(x, (row * nb + b) * 16, v[i]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) bmax[i] = fmaxf(bmax[i], fabsf(v[i].get(j)));
+    }
+    amax = fmaxf(amax, bmax[i]);
+  }
+  const float A = gamax ? u2f(gamax[row / rpg]) : wave_max(amax);
+  const float s = __fdiv_rn(A, 2688.0f);
+  const float d = __fmul_rn(6.0f, s);
+  if (!gamax && lane == 0) outer[row] = s;
+
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = lane + 64 * i;
+    if (b >= nb) continue;
+    uint32_t sc = 0;
+    if (A > 0.0f) sc = e4m3_rne_sat_pos(__fdiv_rn(bmax[i], d));
+    uint32_t lo = 0, hi = 0;
+    if (sc) {
+      const float r = __fdiv_rn(1.0f, __fmul_rn(e4m3_pos_to_f32(sc), s));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lo |= e2m1_rne(__fmul_rn(v[i].get(j), r)) << (4 * j);
+        hi |= e2m1_rne(__fmul_rn(v[i].get(j + 8), r)) << (4 * j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lo |= ((f2u(v[i].get(j)) >> 28) & 8u) << (4 * j);
+        hi |= ((f2u(v[i].get(j + 8)) >> 28) & 8u) << (4 * j);
+      }
+    }
+    const int64_t blk = row * nb + b;
+    *reinterpret_cast<uint2*>(codes + blk * 8) = make_uint2(lo, hi);
+    scales[blk] = (uint8_t)sc;
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// max|x| over each group of `per` contiguous elements; blockIdx.y = group.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_group_amax(const void* __restrict__ x, int64_t per,
+                                                    uint32_t* __restrict__ amax_bits) {
+  __shared__ float red[4];
+  const int64_t g = blockIdx.y;
+  const int64_t base = g * per;
+  float m = 0.0f;
+  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; e < per;
+       e += (int64_t)gridDim.x * 256 * 8) {
+    if constexpr (BF16) {
+      const uint4 a = ld_stream16(
+          reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base + e));
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = fmaxf(m, fabsf(u2f(w[j] << 16)));
+        m = fmaxf(m, fabsf(u2f(w[j] & 0xFFFF0000u)));
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + base + e);
+      const uint4 a = ld_stream16(p), b = ld_stream16(p + 1);
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(u2f(w[j])));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(amax_bits + g, f2u(m));  // non-negative floats order like their bits
+  }
+}
+
+__global__ void k_outer_from_amax(float* __restrict__ outer, int64_t G) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g < G) outer[g] = __fdiv_rn(outer[g], 2688.0f);
+}
+
+// Row-wise MXFP8: 4 lanes per 32-element block, 8 elements per lane.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_mx_rowwise(const void* __restrict__ x, int64_t nchunks,
+                                                    uint8_t* __restrict__ q,
+                                                    uint8_t* __restrict__ e8) {
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < ((nchunks + 63) & ~63LL);
+       c += (int64_t)gridDim.x * 256) {
+    const bool ok = c < nchunks;  // 8 elements per chunk
+    float v[8];
+    if (ok) {
+      if constexpr (BF16) {
+        const uint4 a = ld_stream16(
+            reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + c * 8));
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = u2f(w[j] << 16);
+          v[2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+        }
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + c * 8);
+        const uint4 a = ld_stream16(p), b = ld_stream16(p + 1);
+        v[0] = u2f(a.x); v[1] = u2f(a.y); v[2] = u2f(a.z); v[3] = u2f(a.w);
+        v[4] = u2f(b.x); v[5] = u2f(b.y); v[6] = u2f(b.z); v[7] = u2f(b.w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const int e = e8m0_ceil(m);
+    const float f = exp2_neg(e);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= e4m3_rne(__fmul_rn(v[j], f)) << (8 * j);
+      hi |= e4m3_rne(__fmul_rn(v[j + 4], f)) << (8 * j);
+    }
+    if (ok) {
+      *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(lo, hi);
+      if ((c & 3) == 0) e8[c >> 2] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+int g_cu_count = 0;
+
+}  // namespace
+
+int device_cu_count() {
+  // one cache per process; every MI355X has the same count
+  if (g_cu_count == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      g_cu_count = n;
+    else
+      g_cu_count = 256;
+  }
+  return g_cu_count;
+}
+
+template <bool BF16>
+static hipError_t quantize_impl(const void* x, int64_t rows, int64_t cols, bool per_group,
+                                int64_t rpg, uint8_t* codes, uint8_t* scales, float* outer,
+                                hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int nb = (int)(cols / 16);
+  const uint32_t* gamax = nullptr;
+  if (per_group) {
+    const int64_t G = rows / rpg;
+    uint32_t* bits = reinterpret_cast<uint32_t*>(outer);
+    k_fill_u32<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(bits, G, 0u);
+    const int64_t per = rpg * cols;
+    int64_t gx = (per + 256 * 8 * 8 - 1) / (256 * 8 * 8);
+    gx = gx < 1 ? 1 : (gx > 1024 ? 1024 : gx);
+    k_group_amax<BF16><<<dim3((unsigned)gx, (unsigned)G), 256, 0, stream>>>(x, per, bits);
+    gamax = bits;
+  }
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  if (nb <= 64)
+    k_nvfp4_quantize<BF16, 1><<<grid, 256, 0, stream>>>(x, rows, nb, gamax, rpg, codes, scales, outer);
+  else if (nb <= 128)
+    k_nvfp4_quantize<BF16, 2><<<grid, 256, 0, stream>>>(x, rows, nb, gamax, rpg, codes, scales, outer);
+  else if (nb <= 256)
+    k_nvfp4_quantize<BF16, 4><<<grid, 256, 0, stream>>>(x, rows, nb, gamax, rpg, codes, scales, outer);
+  else
+    k_nvfp4_quantize<BF16, 8><<<grid, 256, 0, stream>>>(x, rows, nb, gamax, rpg, codes, scales, outer);
+  if (per_group) {
+    const int64_t G = rows / rpg;
+    k_outer_from_amax<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(outer, G);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                 bool per_group, int64_t rpg, uint8_t* codes, uint8_t* scales,
+                                 float* outer, hipStream_t stream) {
+  return bf16 ? quantize_impl<true>(x, rows, cols, per_group, rpg, codes, scales, outer, stream)
+              : quantize_impl<false>(x, rows, cols, per_group, rpg, codes, scales, outer, stream);
+}
+
+hipError_t launch_mxfp8_quantize_rowwise(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                         uint8_t* q, uint8_t* e8, hipStream_t stream) {
+  const int64_t nchunks = rows * cols / 8;
+  if (nchunks == 0) return hipSuccess;
+  int64_t grid = (nchunks + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
+  if (grid > cap) grid = cap;
+  if (bf16)
+    k_mx_rowwise<true><<<(unsigned)grid, 256, 0, stream>>>(x, nchunks, q, e8);
+  else
+    k_mx_rowwise<false><<<(unsigned)grid, 256, 0, stream>>>(x, nchunks, q, e8);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4moe

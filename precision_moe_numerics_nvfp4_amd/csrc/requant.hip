@@ -1,0 +1,234 @@
+// Grouped transpose + MXFP8 quantization along the token dimension.
+//
+// Two users:
+//  * mxfp8_requant_sr: the saved NVFP4 activations / weights are dequantized
+//    to float32, transposed, and re-quantized to MXFP8 with stochastic
+//    rounding ("Inkling 2 Small uses four-bit training ...", section
+//    "Stochastic rounding across transposes");
+//  * mxfp8_quantize (COLWISE_GROUPED): dY is transposed and quantized with
+//    round-to-nearest-even, giving the wgrad operand.
+//
+// Output [cols, P]: input rows [offsets[g], offsets[g+1]) of group g land in
+// columns padded_offsets[g] + (r - offsets[g]); the rest of each group's
+// 32-aligned segment is zero, so every 32-element MXFP8 block of an output row
+// lies in one group.
+//
+// Tiling: a workgroup owns a 128-token x 128-column tile. The input rows are
+// staged in LDS in their stored form (4-bit codes + scales, or bf16/f32), so
+// HBM is read once, row-contiguously. Each thread then owns an 8-column x
+// 8-token micro-tile: it reads the 8 tokens' values of its 8 columns from LDS
+// (the transpose), four neighbouring threads cover one 32-token block and
+// reduce its maximum with two shuffles, and each thread writes 8 contiguous
+// output bytes per column (16 threads write one 128-byte output row segment).
+// The stochastic draws for those 8 bytes are exactly one Philox call, because
+// the draw index is the output's linear index and 8 consecutive indices share
+// one counter.
+#include "codecs.hpp"
+#include "internal.hpp"
+
+namespace nvfp4moe {
+
+namespace {
+
+constexpr int TP = 128;  // tokens per tile
+constexpr int TK = 128;  // columns per tile
+
+enum class Src { NVFP4, BF16, F32 };
+
+template <Src S>
+struct Tile;
+
+template <>
+struct Tile<Src::NVFP4> {
+  static constexpr int CPITCH = TK / 2 + 4;  // code bytes per staged row (+pad)
+  uint8_t codes[TP][CPITCH];
+  uint8_t scales[TP][TK / 16];
+  float outer[TP];
+};
+template <>
+struct Tile<Src::BF16> {
+  static constexpr int PITCH = TK + 8;       // bf16 elements per staged row (+pad)
+  uint16_t v[TP][PITCH];
+};
+template <>
+struct Tile<Src::F32> {
+  static constexpr int PITCH = TK + 4;
+  float v[TP][PITCH];
+};
+
+template <Src S, bool SR>
+__global__ __launch_bounds__(256) void k_transpose_mx(
+    const void* __restrict__ src, const uint8_t* __restrict__ src_scales,
+    const float* __restrict__ src_outer, int64_t rpg, int64_t cols,
+    const int64_t* __restrict__ offsets, const int64_t* __restrict__ padded, int G, int64_t P,
+    uint64_t seed, uint32_t tag, uint8_t* __restrict__ out, uint8_t* __restrict__ out_e8) {
+  __shared__ Tile<S> tile;
+  __shared__ int64_t row_of[TP];  // source row of each tile token, -1 = padding
+
+  const int tid = threadIdx.x;
+  const int64_t p0 = (int64_t)blockIdx.x * TP;
+  const int64_t k0 = (int64_t)blockIdx.y * TK;
+  const int64_t ptot = padded[G];
+  if (p0 >= ptot) return;  // uniform per workgroup
+
+  if (tid < TP) {
+    const int64_t p = p0 + tid;
+    int64_t r = -1;
+    if (p < ptot && p < P) {
+      int lo = 0, hi = G;  // last g with padded[g] <= p
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (padded[mid] <= p) lo = mid; else hi = mid;
+      }
+      const int64_t i = p - padded[lo];
+      if (i < offsets[lo + 1] - offsets[lo]) r = offsets[lo] + i;
+    }
+    row_of[tid] = r;
+  }
+  __syncthreads();
+
+  // ---- stage the input rows of this tile
+  if constexpr (S == Src::NVFP4) {
+    const uint8_t* codes = static_cast<const uint8_t*>(src);
+    {  // 64 code bytes per row: 2 threads x 32 bytes
+      const int t = tid >> 1, h = tid & 1;
+      const int64_t r = row_of[t];
+      uint4 a = make_uint4(0, 0, 0, 0), b = a;
+      if (r >= 0) {
+        const uint4* g = reinterpret_cast<const uint4*>(codes + r * (cols / 2) + k0 / 2 + h * 32);
+        a = ld_stream16(g);
+        b = ld_stream16(g + 1);
+      }
+      uint32_t* d = reinterpret_cast<uint32_t*>(&tile.codes[t][h * 32]);
+      d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+      d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+    }
+    if (tid < TP) {
+      const int64_t r = row_of[tid];
+      uint2 sc = make_uint2(0, 0);
+      float o = 0.0f;
+      if (r >= 0) {
+        sc = *reinterpret_cast<const uint2*>(src_scales + r * (cols / 16) + k0 / 16);
+        o = src_outer[rpg ? r / rpg : r];
+      }
+      *reinterpret_cast<uint2*>(&tile.scales[tid][0]) = sc;
+      tile.outer[tid] = o;
+    }
+  } else {
+    constexpr int EB = (S == Src::BF16) ? 2 : 4;        // bytes per element
+    constexpr int V16 = TK * EB / 16;                   // 16-byte vectors per row
+    for (int i = tid; i < TP * V16; i += 256) {
+      const int t = i / V16, c = i % V16;
+      const int64_t r = row_of[t];
+      uint4 a = make_uint4(0, 0, 0, 0);
+      if (r >= 0)
+        a = ld_stream16(reinterpret_cast<const uint4*>(
+            static_cast<const uint8_t*>(src) + (r * cols + k0) * EB) + c);
+      uint32_t* d = reinterpret_cast<uint32_t*>(
+          reinterpret_cast<uint8_t*>(&tile.v[t][0]) + c * 16);
+      d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+    }
+  }
+  __syncthreads();
+
+  // ---- micro-tile: 8 columns x 8 tokens per thread
+  const int pc = tid & 15;   // token chunk: tokens 8*pc .. 8*pc+7 of the tile
+  const int kc = tid >> 4;   // column chunk: columns 8*kc .. 8*kc+7
+  float v[8][8];             // [column][token]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = 8 * pc + i;
+    if constexpr (S == Src::NVFP4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile.codes[t][4 * kc]);
+      const float Sb = e4m3_pos_to_f32(tile.scales[t][kc >> 1]);
+      const float o = tile.outer[t];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float inner = __fmul_rn(e2m1_to_f32((w >> (4 * j)) & 15u), Sb);  // exact
+        v[j][i] = __fmul_rn(inner, o);
+      }
+    } else if constexpr (S == Src::BF16) {
+      const uint4 a = *reinterpret_cast<const uint4*>(&tile.v[t][8 * kc]);
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j][i] = u2f(w[j] << 16);
+        v[2 * j + 1][i] = u2f(w[j] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(&tile.v[t][8 * kc]);
+      const float4 b = *reinterpret_cast<const float4*>(&tile.v[t][8 * kc + 4]);
+      v[0][i] = a.x; v[1][i] = a.y; v[2][i] = a.z; v[3][i] = a.w;
+      v[4][i] = b.x; v[5][i] = b.y; v[6][i] = b.z; v[7][i] = b.w;
+    }
+  }
+
+  const int64_t p = p0 + 8 * pc;                 // first output column of this thread
+  const bool live = (p < ptot) && (p < P);        // whole 8-chunk shares liveness
+  const int64_t PB = P / 32;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const int e = e8m0_ceil(m);
+    const float f = exp2_neg(e);
+    const int64_t k = k0 + 8 * kc + j;
+    uint32_t lo = 0, hi = 0;
+    if constexpr (SR) {
+      const Draws8 u = draws8((uint64_t)(k * P + p) >> 3, seed, tag);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= e4m3_sr(__fmul_rn(v[j][i], f), u.get(i)) << (8 * i);
+        hi |= e4m3_sr(__fmul_rn(v[j][i + 4], f), u.get(i + 4)) << (8 * i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= e4m3_rne(__fmul_rn(v[j][i], f)) << (8 * i);
+        hi |= e4m3_rne(__fmul_rn(v[j][i + 4], f)) << (8 * i);
+      }
+    }
+    if (live) {
+      *reinterpret_cast<uint2*>(out + k * P + p) = make_uint2(lo, hi);
+      if ((pc & 3) == 0) out_e8[k * PB + (p >> 5)] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+template <Src S, bool SR>
+hipError_t run(const void* src, const uint8_t* sc, const float* so, int64_t rpg, int64_t rows,
+               int64_t cols, const int64_t* offsets, const int64_t* padded, int G, int64_t P,
+               uint64_t seed, uint32_t tag, uint8_t* out, uint8_t* out_e8, hipStream_t stream) {
+  (void)rows;
+  if (P == 0 || cols == 0 || G == 0) return hipSuccess;
+  const dim3 grid((unsigned)((P + TP - 1) / TP), (unsigned)(cols / TK));
+  k_transpose_mx<S, SR><<<grid, 256, 0, stream>>>(src, sc, so, rpg, cols, offsets, padded, G, P,
+                                                  seed, tag, out, out_e8);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                             int64_t rpg, int64_t rows, int64_t cols, const int64_t* offsets,
+                             const int64_t* padded, int G, int64_t P, uint64_t seed,
+                             uint32_t tag, uint8_t* out, uint8_t* out_e8, hipStream_t stream) {
+  return run<Src::NVFP4, true>(codes, scales, outer, rpg, rows, cols, offsets, padded, G, P, seed,
+                               tag, out, out_e8, stream);
+}
+
+hipError_t launch_mxfp8_quantize_colwise(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                         const int64_t* offsets, const int64_t* padded, int G,
+                                         int64_t P, uint8_t* out, uint8_t* out_e8,
+                                         hipStream_t stream) {
+  if (bf16)
+    return run<Src::BF16, false>(x, nullptr, nullptr, 0, rows, cols, offsets, padded, G, P, 0, 0,
+                                 out, out_e8, stream);
+  return run<Src::F32, false>(x, nullptr, nullptr, 0, rows, cols, offsets, padded, G, P, 0, 0,
+                              out, out_e8, stream);
+}
+
+}  // namespace nvfp4moe

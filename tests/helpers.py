@@ -1,0 +1,60 @@
+"""Shared test helpers: host<->device marshalling and oracle pipelines.
+
+The oracle is called on the same host arrays that are uploaded to the GPU.
+"""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def ensure_built():
+    """Build the HIP library if it is not there yet (tests load what is built)."""
+    from precision_moe_numerics_nvfp4_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        subprocess.run([sys.executable, "-m", "precision_moe_numerics_nvfp4_amd.build"],
+                       cwd=ROOT, check=True)
+    return binding.LIB_PATH
+
+
+def to_dev(a):
+    """numpy -> GPU tensor; uint16 arrays are bfloat16 bit patterns."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def from_dev(t):
+    """GPU tensor -> numpy; bfloat16 comes back as uint16 bit patterns."""
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def assert_gemm_close(y, ref64, groups, absbound=None, tol=1e-3, what="gemm", elementwise=True):
+    """Per group: max|y - ref| <= tol * max|ref| (the contract); with
+    `elementwise`, relative error <= tol where |ref| >= 1e-2 max|ref|; and,
+    when given, |y - ref| <= absbound elementwise (a summation error bound)."""
+    y = np.asarray(y, dtype=np.float64)
+    for (a, b) in groups:
+        if b <= a:
+            continue
+        r = ref64[a:b]
+        d = np.abs(y[a:b] - r)
+        m = np.abs(r).max()
+        assert d.max() <= tol * m + 1e-30, f"{what}: group [{a},{b}) normwise {d.max() / max(m, 1e-300):.3e}"
+        big = np.abs(r) >= 1e-2 * m
+        if elementwise and big.any():
+            rel = (d[big] / np.abs(r[big])).max()
+            assert rel <= tol, f"{what}: group [{a},{b}) elementwise {rel:.3e}"
+        if absbound is not None:
+            viol = d > absbound[a:b] * 1.0000001 + 1e-37
+            assert not viol.any(), f"{what}: {viol.sum()} elements exceed the summation error bound"

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every symbol the header declares, and
+rejects bad arguments on the host before touching the GPU (CPU only: no
+compute call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"NVFP4MOE_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    from precision_moe_numerics_nvfp4_amd import binding
+    return binding.lib()
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"nvfp4_quantize", "mxfp8_requant_sr", "moe_fwd_grouped_gemm", "moe_bwd_dgrad",
+            "moe_bwd_wgrad", "moe_permute", "mxfp8_quantize"} <= names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from precision_moe_numerics_nvfp4_amd import binding
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in binding.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version_and_status_strings(L):
+    from precision_moe_numerics_nvfp4_amd import binding
+    assert L.nvfp4moe_abi_version() == 1
+    for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported size or alignment"),
+                    (3, "workspace too small"), (4, "HIP launch or runtime error"), (99, "unknown status")]:
+        assert binding.status_string(s) == text
+
+
+def test_workspace_size(L):
+    assert L.nvfp4moe_permute_workspace_size(32768, 8, 48) >= 256 * 48 * 4
+    assert L.nvfp4moe_permute_workspace_size(-1, 8, 48) == 0
+    assert L.nvfp4moe_permute_workspace_size(10, 0, 48) == 0
+
+
+EINVAL, EUNSUP, EWS = 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: calls fail first
+FAKE_MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+
+
+def test_quantize_argument_errors(L):
+    q = L.nvfp4_quantize
+    assert q(None, 1, 4, 64, 0, 0, FAKE, FAKE, FAKE, None) == EINVAL          # null x
+    assert q(FAKE, 7, 4, 64, 0, 0, FAKE, FAKE, FAKE, None) == EINVAL          # bad dtype
+    assert q(FAKE, 1, -1, 64, 0, 0, FAKE, FAKE, FAKE, None) == EINVAL         # negative rows
+    assert q(FAKE, 1, 4, 64, 5, 0, FAKE, FAKE, FAKE, None) == EINVAL          # bad mode
+    assert q(FAKE, 1, 4, 64, 1, 0, FAKE, FAKE, FAKE, None) == EINVAL          # group of 0 rows
+    assert q(FAKE, 1, 4, 48, 0, 0, FAKE, FAKE, FAKE, None) == EUNSUP          # cols % 32
+    assert q(FAKE, 1, 6, 64, 1, 4, FAKE, FAKE, FAKE, None) == EUNSUP          # rows % group
+    assert q(FAKE_MIS, 1, 4, 64, 0, 0, FAKE, FAKE, FAKE, None) == EUNSUP      # alignment
+    assert q(None, 1, 0, 64, 0, 0, None, None, None, None) == 0               # empty is a no-op
+
+
+def test_gemm_and_requant_argument_errors(L):
+    g = L.moe_fwd_grouped_gemm
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 64, 256, 256, FAKE, 0, None) == EINVAL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 200, 256, FAKE, 0, None) == EUNSUP
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 256, 256, FAKE, 3, None) == EINVAL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, 256, FAKE, 0, None) == 0
+    r = L.mxfp8_requant_sr
+    assert r(FAKE, FAKE, FAKE, 0, 0, 64, 256, FAKE, FAKE, 1, 48, 1, 0, FAKE, FAKE, None) == EUNSUP
+    assert r(FAKE, FAKE, FAKE, 2, 0, 64, 256, FAKE, FAKE, 1, 64, 1, 0, FAKE, FAKE, None) == EINVAL
+    assert r(FAKE, FAKE, FAKE, 0, 0, 64, 256, None, FAKE, 1, 64, 1, 0, FAKE, FAKE, None) == EINVAL
+    d = L.moe_bwd_dgrad
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 256, FAKE, 0, None) == EUNSUP
+    w = L.moe_bwd_wgrad
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 40, 128, 128, FAKE, None) == EUNSUP
+    assert w(None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, FAKE, None) == EINVAL
+    m = L.mxfp8_quantize
+    assert m(FAKE, 1, 64, 256, 9, None, None, 0, 0, FAKE, FAKE, None) == EINVAL
+    assert m(FAKE, 1, 64, 48, 0, None, None, 0, 0, FAKE, FAKE, None) == EUNSUP
+
+
+def test_permute_argument_errors(L):
+    p = L.moe_permute
+    args = lambda T, k, nl, K, ws, wsb: (FAKE, T, k, 0, nl, FAKE, FAKE, FAKE, K, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+    need = L.nvfp4moe_permute_workspace_size(100, 2, 8)
+    assert p(*args(100, 2, 8, 256, FAKE, need - 1)) == EWS
+    assert p(*args(100, 2, 8, 48, FAKE, need)) == EUNSUP
+    assert p(*args(100, 2, 2000, 256, FAKE, 1 << 30)) == EUNSUP
+    assert p(*args(100, 0, 8, 256, FAKE, need)) == EINVAL
+    assert p(*args(100, 2, 8, 256, None, need)) == EINVAL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    from precision_moe_numerics_nvfp4_amd import binding
+    ensure_built()
+    with pytest.raises(ValueError):
+        binding.nvfp4_quantize(torch.zeros(4, 64))
+    with pytest.raises(TypeError):
+        binding.nvfp4_quantize([[0.0] * 64])
