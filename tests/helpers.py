@@ -58,3 +58,22 @@ def assert_gemm_close(y, ref64, groups, absbound=None, tol=1e-3, what="gemm", el
         if absbound is not None:
             viol = d > absbound[a:b] * 1.0000001 + 1e-37
             assert not viol.any(), f"{what}: {viol.sum()} elements exceed the summation error bound"
+
+
+def sr_mean_sd(v, e8):
+    """Analytic standard deviation of mean(SR(v)) - mean(v) for float values
+    v [R, C] re-quantized to E4M3 with E8M0 block exponents e8 [R, C/32]:
+    each element rounds up with probability D over a gap g, so its variance
+    is D (1 - D) g^2."""
+    from oracle import formats as F
+    v = np.asarray(v, dtype=np.float64)
+    R, C = v.shape
+    s = np.exp2(np.repeat(np.asarray(e8, dtype=np.float64) - 127, 32, axis=1))
+    a = np.abs(v) / s
+    lo_i = np.searchsorted(F.E4M3_GRID, a, side="right") - 1
+    at_max = lo_i >= 126
+    hi = F.E4M3_GRID[np.minimum(lo_i + 1, 126)]
+    gap = np.where(at_max, 1.0, hi - F.E4M3_GRID[lo_i])
+    D = (a - F.E4M3_GRID[lo_i]) / gap
+    var = np.where(at_max, 0.0, D * (1 - D)) * (gap * s) ** 2
+    return np.sqrt(var.sum()) / v.size
