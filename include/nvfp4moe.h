@@ -200,7 +200,8 @@ NVFP4MOE_API int mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_
  * blocks along G*N); offsets[G+1] (device).
  * dx[r, k] = sum_n dy[r, n] * w[k, g*N + n] for rows r of group g, float32
  * accumulation; dx [m_cap, K] float32 or bfloat16; rows >= offsets[G] untouched.
- * Requires N % 128 == 0, K % 128 == 0.
+ * Requires N % 128 == 0, K % 128 == 0, G * N <= 16711935 (tile offsets are
+ * 32-bit); otherwise NVFP4MOE_EUNSUPPORTED.
  */
 NVFP4MOE_API int moe_bwd_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0,
                   const uint8_t* w_e4m3, const uint8_t* w_e8m0,
@@ -216,7 +217,8 @@ NVFP4MOE_API int moe_bwd_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0,
  * dw[g, n, k] = sum over p in [padded_offsets[g], padded_offsets[g+1]) of
  * dyT[n, p] * xT[k, p], float32 accumulation; dw [G, N, K] float32 (the stored
  * weight layout). Groups with no tokens get zeros.
- * Requires N % 128 == 0, K % 128 == 0, P % 32 == 0.
+ * Requires N % 128 == 0, K % 128 == 0, P % 32 == 0, P <= 16711935 and
+ * G <= 16384; otherwise NVFP4MOE_EUNSUPPORTED.
  */
 NVFP4MOE_API int moe_bwd_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0,
                   const uint8_t* xT_e4m3, const uint8_t* xT_e8m0,

@@ -10,6 +10,11 @@ namespace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The MXFP8 GEMMs address a 256-row operand tile with 32-bit byte offsets.
+constexpr int64_t kMaxGemmRowBytes = (int64_t)0xFFFFFFFF / 257;
+// wgrad ranks the groups by size in shared memory.
+constexpr int kMaxWgradGroups = 16384;
+
 inline int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4MOE_OK : NVFP4MOE_EHIP; }
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -157,6 +162,7 @@ int moe_bwd_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0, const uint8_t*
   if (G == 0 || m_cap == 0 || K == 0) return NVFP4MOE_OK;
   REQUIRE(dy_e4m3 && dy_e8m0 && w_e4m3 && w_e8m0 && offsets && dx, NVFP4MOE_EINVAL);
   REQUIRE(N % 128 == 0 && K % 128 == 0 && N > 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE((int64_t)G * N <= kMaxGemmRowBytes, NVFP4MOE_EUNSUPPORTED);
   REQUIRE(aligned16(dy_e4m3) && aligned16(w_e4m3) && aligned16(dx), NVFP4MOE_EUNSUPPORTED);
   return hip_status(launch_dgrad(dy_e4m3, dy_e8m0, w_e4m3, w_e8m0, offsets, G, m_cap, N, K, dx,
                                  dx_dtype == NVFP4MOE_BF16, as_stream(stream)));
@@ -169,6 +175,7 @@ int moe_bwd_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0, const uint8_
   if (G == 0 || N == 0 || K == 0) return NVFP4MOE_OK;
   REQUIRE(dyT_e4m3 && dyT_e8m0 && xT_e4m3 && xT_e8m0 && padded_offsets && dw, NVFP4MOE_EINVAL);
   REQUIRE(N % 128 == 0 && K % 128 == 0 && P % 32 == 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(G <= kMaxWgradGroups && P <= kMaxGemmRowBytes, NVFP4MOE_EUNSUPPORTED);
   REQUIRE(aligned16(dyT_e4m3) && aligned16(xT_e4m3) && aligned16(dw), NVFP4MOE_EUNSUPPORTED);
   return hip_status(launch_wgrad(dyT_e4m3, dyT_e8m0, xT_e4m3, xT_e8m0, padded_offsets, G, P, N, K,
                                  dw, as_stream(stream)));

@@ -36,30 +36,35 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
 
 // ----------------------------------------------------------------- E2M1
 
-// Magnitude and sign of a 4-bit E2M1 code as float32 (exact).
-__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-  const uint32_t m = c & 7u;
-  // codes 2..7 are normal: exponent 126 + (m >> 1), mantissa bit m & 1,
-  // which is the bit pattern (m << 22) + 0x3F000000; codes 0 and 1 are 0, 0.5
-  const uint32_t nrm = (m << 22) + 0x3F000000u;
-  const uint32_t mag = (m >= 2u) ? nrm : (m == 1u ? 0x3F000000u : 0u);
-  return u2f(mag | ((c & 8u) << 28));
+// Eight floats -> eight E2M1 codes packed in a word (element j in bits
+// 4j..4j+3), rounded to nearest with ties to the even code, saturating at 6,
+// sign bit kept (so -0 and tiny negatives give code 8). This is
+// v_cvt_scalef32_pk_fp4_f32 with a unit scale, checked against the
+// threshold rule (a midpoint of neighbouring grid values goes to the one
+// with the even code) on every midpoint, its float32 neighbours, a dense
+// sweep of [0, 8) and saturating values, for both signs.
+__device__ __forceinline__ uint32_t e2m1x8_rne(const float* v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
 }
 
-// Round to the nearest E2M1 value (ties to the even code), saturating at 6.
-// The code's sign bit is the sign bit of y (so -0 and tiny negatives give 8).
-// The thresholds are the midpoints of neighbouring grid values; a midpoint
-// goes to the neighbour whose code is even.
-__device__ __forceinline__ uint32_t e2m1_rne(float y) {
-  const float a = fabsf(y);
-  uint32_t m = (a > 0.25f) ? 1u : 0u;
-  m += (a >= 0.75f) ? 1u : 0u;
-  m += (a > 1.25f) ? 1u : 0u;
-  m += (a >= 1.75f) ? 1u : 0u;
-  m += (a > 2.5f) ? 1u : 0u;
-  m += (a >= 3.5f) ? 1u : 0u;
-  m += (a > 5.0f) ? 1u : 0u;
-  return m | ((f2u(y) >> 28) & 8u);
+// Two E2M1 codes (one byte: element 2i low nibble) -> float32 values
+// (v_cvt_scalef32_pk_f32_fp4 with a unit scale decodes exactly).
+__device__ __forceinline__ void e2m1x2_to_f32(uint32_t word, int byte, float& lo, float& hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  f32x2_t v;
+  switch (byte) {
+    case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
+    case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
+    case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
+    default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
+  }
+  lo = v.x;
+  hi = v.y;
 }
 
 // ----------------------------------------------------------------- E4M3
@@ -82,35 +87,30 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_pos(float t) {
   return (b >> 20) - (120u << 3);                       // rebias exponent 127 -> 7
 }
 
-// Round |y| <= 448 to E4M3FN, nearest-even; sign from y.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t b = f2u(y);
-  const uint32_t a = b & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a < 0x3C800000u) {
-    code = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);
-  } else {
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  }
-  code = code < 0x7Eu ? code : 0x7Eu;
-  return code | ((b >> 24) & 0x80u);
+// Four values with |y| <= 448 -> E4M3FN bytes (first value in the low byte),
+// round to nearest even (ties to the even code), sign kept: v_cvt_pk_fp8_f32
+// (checked against a brute-force nearest-even search on subnormal ties and a
+// dense sweep of [-448, 448]).
+__device__ __forceinline__ uint32_t e4m3x4_rne(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
 }
 
-// Stochastic rounding of |y| <= 448 to E4M3FN with a 16-bit draw u.
-// With lo the grid value at or below |y| and D = (|y| - lo) / gap, the value
-// rounds up iff u + floor(D * 2^16) >= 2^16. Both ranges reduce to one
-// fixed-point form v = (code_of_lo << 16) | floor(D * 2^16):
-//   below 2^-6 (grid step 2^-9): v = floor(|y| * 2^25);
-//   above: the float32 bits shifted right by 4 and rebiased.
-// The result is then (v + u) >> 16. Sign from y.
-__device__ __forceinline__ uint32_t e4m3_sr(float y, uint32_t u) {
-  const uint32_t b = f2u(y);
-  const uint32_t a = b & 0x7FFFFFFFu;
-  const uint32_t vs = (uint32_t)(u2f(a) * 33554432.0f);  // truncating convert
-  const uint32_t vn = (a >> 4) - (960u << 16);
-  const uint32_t v = (a < 0x3C800000u) ? vs : vn;
-  return ((v + u) >> 16) | ((b >> 24) & 0x80u);
+// Stochastic rounding of four values |y| <= 448 to E4M3FN bytes (first value
+// in the low byte) with 16-bit draws u0..u3. With lo the grid value at or
+// below |y| and D = (|y| - lo) / gap, a value rounds up iff
+// u + floor(D * 2^16) >= 2^16; sign kept. v_cvt_sr_fp8_f32 implements exactly
+// this rule when the draw occupies the high 16 bits of its random operand
+// (checked against the rule on 2.6e5 values spanning the normal and subnormal
+// E4M3 ranges, grid values and both signs).
+__device__ __forceinline__ uint32_t e4m3x4_sr(float y0, float y1, float y2, float y3, uint32_t u0,
+                                              uint32_t u1, uint32_t u2, uint32_t u3) {
+  int w = __builtin_amdgcn_cvt_sr_fp8_f32(y0, u0 << 16, 0, 0);
+  w = __builtin_amdgcn_cvt_sr_fp8_f32(y1, u1 << 16, w, 1);
+  w = __builtin_amdgcn_cvt_sr_fp8_f32(y2, u2 << 16, w, 2);
+  w = __builtin_amdgcn_cvt_sr_fp8_f32(y3, u3 << 16, w, 3);
+  return (uint32_t)w;
 }
 
 // ----------------------------------------------------------------- E8M0
@@ -143,8 +143,9 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-way XORs in one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;

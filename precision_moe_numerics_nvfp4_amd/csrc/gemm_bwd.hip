@@ -8,15 +8,29 @@
 // MXFP8 (E4M3 elements, one E8M0 power of two per 32 along the contraction)
 // is exactly the operand format of v_mfma_scale_f32_32x32x64_f8f6f4: each of
 // its two 32-element k-blocks per row takes one E8M0 byte, so products are
-// exact and accumulation is float32.
+// exact and the block sums are combined in float32.
 // Both GEMMs are "row x row" contractions: each operand is stored with the
 // contraction dimension contiguous (that is what the re-quantization's
 // transpose is for), so one main loop serves both:
 //   dgrad: dX[r, k]    = sum_n dY8[r, n] * W8[k, g*N + n]    (rows r of expert g)
 //   wgrad: dW[g, n, k] = sum_p dYT8[n, p] * XT8[k, p]        (p in g's padded segment)
-// Workgroup tile 128 x 128, four wavefronts of 64 x 64 (2 x 2 MFMA tiles),
-// 128 contraction elements (4 MX blocks) per double-buffered LDS stage.
-// Contraction ranges are multiples of 32; a partial last stage is zero-filled.
+//
+// Structure. A workgroup of 4 wavefronts owns a 256 x 256 output tile; each
+// wavefront owns 128 x 128 (4 x 4 MFMA tiles, 256 accumulator registers).
+// The contraction advances 128 bytes (4 MX blocks) per stage, so every
+// operand row contributes one full 128-byte line per stage. Each thread loads
+// its 16-byte chunks of stage kt+1 into registers at the top of iteration kt
+// and stores them into the other LDS buffer after the MFMAs of stage kt have
+// been issued; 16-byte chunks are XOR-swizzled by row so the fragment reads
+// (32 rows at one offset) spread over the LDS banks. Rows past a group's end
+// are read from a valid row and their results discarded; contraction
+// elements past a ragged end (wgrad's last stage of a group) are masked to
+// zero when stored to LDS.
+//
+// Tile order. dgrad: live tiles only, XCD-contiguous (workgroup w runs on XCD
+// w % 8), m-tile fastest within (group, n-tile), so the workgroups an XCD runs
+// together share the B tile in its L2. wgrad: groups longest first (a tile's
+// cost is its group's token count).
 #include "codecs.hpp"
 #include "internal.hpp"
 
@@ -26,221 +40,387 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int RP = BK + 16;   // staged bytes per row (+pad)
-constexpr int SPB = BK / 32;  // scale bytes per row per stage
+constexpr int BK = 128;                       // contraction bytes (= elements) per stage
+constexpr int CPR = BK / 16;                  // 16-byte chunks per row per stage
+constexpr int SCB = BK / 32;                  // scale bytes per row per stage
+constexpr int kBufferWord3 = 0x00020000;      // raw buffer, 32-bit data format
 
-struct Stage {
-  uint8_t a[BM][RP];
-  uint8_t b[BN][RP];
-  uint8_t as[BM][SPB];
-  uint8_t bs[BN][SPB];
-};
+// The tile coordinates are the same for the whole workgroup; saying so keeps
+// buffer resources in scalar registers.
+__device__ __forceinline__ void* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int uniform_u32(int64_t n) {
+  return (int)__builtin_amdgcn_readfirstlane((uint32_t)(n < 0xFFFFFFFFll ? n : 0xFFFFFFFFll));
+}
+
+// byte offset of 16-byte chunk c of row r in a [rows][BK] stage buffer
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
 
 struct Operand {
   const uint8_t* q;    // elements, row-major
   const uint8_t* e;    // E8M0 scales, row-major
-  int64_t ld;          // elements per row (bytes)
+  int64_t ld;          // elements per row
   int64_t c0;          // first contraction element of this tile
   int64_t row0;        // first row of the tile
-  int64_t row_end;     // rows >= row_end are zero
+  int64_t row_end;     // rows >= row_end are not part of the result
 };
 
-// acc[i][j] += A[64 rows of wave] x B[64 rows of wave]^T over L contraction elements.
-__device__ __forceinline__ void mainloop(Stage* st, const Operand& A, const Operand& B, int64_t L,
-                                         f32x16 (&acc)[2][2]) {
+__device__ __forceinline__ int64_t xcd_tile(int64_t w, int64_t live) {
+  const int64_t x = w & 7, s = w >> 3;
+  const int64_t q = live >> 3, r = live & 7;
+  return x * q + (x < r ? x : r) + s;
+}
+
+// acc += A[rows of this wave] x B[rows of this wave]^T over L contraction
+// elements (L a multiple of 32). T x T workgroup tile (T = 256 or 128), 2 x 2
+// wavefronts of (T/2) x (T/2).
+template <int T>
+__device__ __forceinline__ void mainloop(uint8_t* smem, const Operand& A, const Operand& B,
+                                         int64_t L, f32x16 (&acc)[T / 64][T / 64]) {
+  constexpr int TM = T / 64, TN = T / 64;
+  constexpr int LD_CH = T * CPR / 256;                // 16-byte chunks per thread per operand
+  constexpr int SROWS = 2 * T / 256;                  // scale rows per thread (both operands)
+  uint8_t* sq = smem;                                 // [2 bufs][2 operands][T][BK]
+  uint8_t* ss = smem + 2 * 2 * T * BK;                // [2 bufs][2 operands][T][SCB]
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, r32 = lane & 31;
 
-  // thread t stages 64 bytes (4 x 16) of A row t/2 and of B row t/2, half t&1,
-  // and the 4 scale bytes of A row t (t < 128) or B row t-128.
-  const int lr = tid >> 1, lh = tid & 1;
-  const int64_t arow = A.row0 + lr;
-  const bool aok = arow < A.row_end;
-  const uint8_t* ag = A.q + (aok ? arow : 0) * A.ld + A.c0 + lh * 64;
-  const int64_t brow = B.row0 + lr;
-  const bool bok = brow < B.row_end;
-  const uint8_t* bg = B.q + (bok ? brow : 0) * B.ld + B.c0 + lh * 64;
-  const int sr = tid & 127;
-  const bool s_is_a = tid < 128;
-  const Operand& SO = s_is_a ? A : B;
-  const int64_t srow = SO.row0 + sr;
-  const bool sok = srow < SO.row_end;
-  const uint8_t* sg = SO.e + (sok ? srow : 0) * (SO.ld / 32) + SO.c0 / 32;
-
-  uint4 ra[4], rb[4];
-  uint32_t rs;
-  auto gload = [&](int64_t kt) {
-    const int64_t c = kt * BK;
+  // Loads go through buffer resources whose range ends at the operand's last
+  // valid row, so the over-read of a ragged contraction tail on that row, or
+  // of the stage after the last, returns zeros instead of touching memory
+  // past the tensor. Offsets are 32-bit (the host checks (T + 1) * ld < 2^32).
+  // Chunk i of operand o for this thread: row (tid >> 3) + 32 * i, chunk tid & 7.
+  // Scale row s of this thread: operand so[s], row sr[s].
+  const int crow = tid >> 3, cch = tid & 7;
+  __amdgpu_buffer_rsrc_t rq[2], re[2];
+  uint32_t off[2][LD_CH], eoff[SROWS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = (c + lh * 64 + i * 16) < L;     // L is a multiple of 32
-      ra[i] = (aok && in) ? *reinterpret_cast<const uint4*>(ag + c + i * 16) : make_uint4(0, 0, 0, 0);
-      rb[i] = (bok && in) ? *reinterpret_cast<const uint4*>(bg + c + i * 16) : make_uint4(0, 0, 0, 0);
-    }
-    rs = 0;
-    if (sok) {
+  for (int o = 0; o < 2; ++o) {
+    const Operand& X = o ? B : A;
+    const int64_t nrow = X.row_end - X.row0;
+    rq[o] = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X.q + X.row0 * X.ld), (short)0,
+                                              uniform_u32(nrow * X.ld), kBufferWord3);
+    re[o] = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X.e + X.row0 * (X.ld / 32)), (short)0,
+                                              uniform_u32(nrow * (X.ld / 32)), kBufferWord3);
 #pragma unroll
-      for (int i = 0; i < SPB; ++i)
-        if (c + 32 * i < L) rs |= (uint32_t)sg[kt * SPB + i] << (8 * i);
+    for (int i = 0; i < LD_CH; ++i) {
+      const int64_t r = crow + 32 * i;
+      const int64_t rr = r < nrow ? r : 0;      // a valid row
+      off[o][i] = (uint32_t)(rr * X.ld + X.c0 + cch * 16);
     }
-  };
-  auto sstore = [&](Stage& s) {
-    uint4* da = reinterpret_cast<uint4*>(&s.a[lr][lh * 64]);
-    uint4* db = reinterpret_cast<uint4*>(&s.b[lr][lh * 64]);
+  }
+  int sop[SROWS], srw[SROWS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      da[i] = ra[i];
-      db[i] = rb[i];
-    }
-    *reinterpret_cast<uint32_t*>(s_is_a ? &s.as[sr][0] : &s.bs[sr][0]) = rs;
-  };
+  for (int s2 = 0; s2 < SROWS; ++s2) {
+    const int id = tid + 256 * s2;            // 0 .. 2T-1
+    sop[s2] = __builtin_amdgcn_readfirstlane(id / T);   // the same for the whole wavefront
+    srw[s2] = id % T;
+    const Operand& X = sop[s2] ? B : A;
+    const int64_t nrow = X.row_end - X.row0;
+    const int64_t rs = srw[s2] < nrow ? srw[s2] : 0;
+    eoff[s2] = (uint32_t)(rs * (X.ld / 32) + X.c0 / 32);
+  }
 
   const int64_t nk = (L + BK - 1) / BK;
   if (nk == 0) return;
-  gload(0);
-  sstore(st[0]);
-  __syncthreads();
-  const int half = lane >> 5;
-  const int r32 = lane & 31;
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    Stage& cur = st[kt & 1];
-    if (kt + 1 < nk) gload(kt + 1);
+  u32x4 stq[2][LD_CH];
+  uint8_t sts[SROWS][SCB];   // combined only when stored, so the loads stay in flight
+  auto gload = [&](int64_t kt) {
+    // the whole offset goes in the vector operand: the range check covers
+    // only that part, not the scalar offset
+    const uint32_t so = (uint32_t)(kt * BK), se = (uint32_t)(kt * SCB);
 #pragma unroll
-    for (int ks = 0; ks < BK / 64; ++ks) {
-      // Operand layout of the 64-deep block-scaled MFMA: lane l supplies
-      // elements 16*(l/32) .. +15 of the step's MX block 0 in bytes 0-15 and
-      // the same elements of MX block 1 in bytes 16-31; its scale byte is the
-      // one of row l%32, MX block l/32.
-      const int blk = 2 * ks + half;           // MX block of this lane's scale
-      i32x8 af[2], bf[2];
-      int32_t asc[2], bsc[2];
+    for (int o = 0; o < 2; ++o)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + r32;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&cur.a[r][ks * 64 + half * 16]);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(&cur.a[r][ks * 64 + 32 + half * 16]);
-        af[i] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        asc[i] = cur.as[r][blk];
-      }
+      for (int i = 0; i < LD_CH; ++i)
+        stq[o][i] = __builtin_amdgcn_raw_buffer_load_b128(rq[o], (int)(off[o][i] + so), 0, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = wn * 64 + j * 32 + r32;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&cur.b[c][ks * 64 + half * 16]);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(&cur.b[c][ks * 64 + 32 + half * 16]);
-        bf[j] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        bsc[j] = cur.bs[c][blk];
-      }
+    for (int s2 = 0; s2 < SROWS; ++s2)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int b = 0; b < SCB; ++b)
+        sts[s2][b] = __builtin_amdgcn_raw_buffer_load_b8(sop[s2] ? re[1] : re[0],
+                                                         (int)(eoff[s2] + se + b), 0, 0);
+  };
+  auto sstore = [&](int buf, int64_t kt) {
+    // contraction elements at or past L are stored as zero (L is a multiple of 32)
+    const int64_t c = kt * BK + cch * 16;
+    const uint32_t m = c < L ? ~0u : 0u;
+    const int64_t rem = L - kt * BK;
+    const uint32_t smask = rem >= BK ? ~0u : (rem <= 0 ? 0u : ((1u << (8 * (rem / 32))) - 1u));
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af[i], bf[j], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/, 0, asc[i], 0, bsc[j]);
+    for (int o = 0; o < 2; ++o) {
+      uint8_t* d = sq + (buf * 2 + o) * T * BK;
+#pragma unroll
+      for (int i = 0; i < LD_CH; ++i)
+        *reinterpret_cast<u32x4*>(d + swz(crow + 32 * i, cch)) = stq[o][i] & m;
     }
-    if (kt + 1 < nk) sstore(st[(kt + 1) & 1]);
+#pragma unroll
+    for (int s2 = 0; s2 < SROWS; ++s2) {
+      uint8_t* d = ss + ((buf * 2 + sop[s2]) * T + srw[s2]) * SCB;
+#pragma unroll
+      for (int b = 0; b < SCB; ++b) d[b] = sts[s2][b] & (uint8_t)(smask >> (8 * b));
+    }
+  };
+
+  // Operand layout of the 64-deep block-scaled MFMA: lane l supplies elements
+  // 16*(l/32) .. +15 of the step's MX block 0 in bytes 0-15 and the same
+  // elements of MX block 1 in bytes 16-31; its scale is the one of row l%32,
+  // MX block l/32. A row's four stage scales are read as one word, shifted so
+  // that byte 2*ks of it is this lane's block of step ks (selected by op_sel).
+  struct Frag {
+    i32x8 a[TM], b[TN];
+  };
+  auto read_frags = [&](const uint8_t* qa, const uint8_t* qb, int ks, Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * TM * 32 + i * 32 + r32;
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(qa + swz(r, 4 * ks + half));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(qa + swz(r, 4 * ks + 2 + half));
+      f.a[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * TN * 32 + j * 32 + r32;
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(qb + swz(r, 4 * ks + half));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(qb + swz(r, 4 * ks + 2 + half));
+      f.b[j] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    }
+  };
+
+  gload(0);
+  sstore(0, 0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    // Stage kt+1 is loaded (and stored) even after the last stage: the read
+    // stays inside the buffer range and the LDS buffer is not read again.
+    // Keeping the body free of branches lets its parts be interleaved.
+    gload(kt + 1);
+    const uint8_t* qa = sq + (cur * 2 + 0) * T * BK;
+    const uint8_t* qb = sq + (cur * 2 + 1) * T * BK;
+    const uint32_t* sa = reinterpret_cast<const uint32_t*>(ss + (cur * 2 + 0) * T * SCB);
+    const uint32_t* sb = reinterpret_cast<const uint32_t*>(ss + (cur * 2 + 1) * T * SCB);
+    int32_t asc[TM], bsc[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) asc[i] = (int32_t)(sa[wm * TM * 32 + i * 32 + r32] >> (8 * half));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bsc[j] = (int32_t)(sb[wn * TN * 32 + j * 32 + r32] >> (8 * half));
+    Frag f0, f1;
+    read_frags(qa, qb, 0, f0);
+    read_frags(qa, qb, 1, f1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f0.a[i], f0.b[j], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/, 0, asc[i], 0, bsc[j]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f1.a[i], f1.b[j], acc[i][j], 0, 0, 2 /*byte 2*/, asc[i], 2, bsc[j]);
+    sstore(cur ^ 1, kt + 1);
+    // Issue order: next-stage loads, scale words and step-0 fragments, then
+    // step-0 MFMAs interleaved with the step-1 fragment reads, then step-1
+    // MFMAs interleaved with the LDS stores of the next stage.
+    constexpr int NL = 2 * LD_CH + SROWS * SCB;
+    constexpr int NR = 2 * (TM + TN);
+    constexpr int NM = TM * TN;
+    constexpr int NW = 2 * LD_CH + SROWS * SCB;
+    __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR + TM + TN, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, (NR + NM - 1) / NM, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, (NW + NM - 1) / NM, 0);
+    }
     __syncthreads();
   }
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void k_dgrad(const uint8_t* __restrict__ dy,
-                                               const uint8_t* __restrict__ dye,
-                                               const uint8_t* __restrict__ w,
-                                               const uint8_t* __restrict__ we,
-                                               const int64_t* __restrict__ offsets, int G,
-                                               int64_t N, int64_t K, void* __restrict__ dx) {
-  __shared__ Stage st[2];
-  // virtual m-tile -> (expert, first row)
-  int64_t vt = blockIdx.y;
-  int g = -1;
-  int64_t row0 = 0, row_end = 0;
-  for (int e = 0; e < G; ++e) {
-    const int64_t a = offsets[e], b = offsets[e + 1];
-    const int64_t nt = (b - a + BM - 1) / BM;
-    if (vt < nt) {
-      g = e;
-      row0 = a + vt * BM;
-      row_end = b;
-      break;
-    }
-    vt -= nt;
-  }
-  if (g < 0) return;
-  const int64_t k0 = (int64_t)blockIdx.x * BN;
-  Operand A{dy, dye, N, 0, row0, row_end};
-  Operand B{w, we, (int64_t)G * N, (int64_t)g * N, k0, k0 + BN};
-  f32x16 acc[2][2];
+template <int TM>
+__device__ __forceinline__ void zero(f32x16 (&acc)[TM][TM]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TM; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  mainloop(st, A, B, N, acc);
+}
+
+// Live dgrad tile t -> (group, first row, row end, n-tile over K).
+__device__ __forceinline__ bool dgrad_tile(const int64_t* __restrict__ offsets, int G, int64_t t,
+                                           int64_t ntn, int BM, int& g, int64_t& row0,
+                                           int64_t& row_end, int64_t& nt) {
+  for (int e = 0; e < G; ++e) {
+    const int64_t a = offsets[e], b = offsets[e + 1];
+    const int64_t mt = (b - a + BM - 1) / BM;
+    if (t < mt * ntn) {
+      g = e;
+      nt = t / mt;
+      row0 = a + (t % mt) * BM;
+      row_end = b;
+      return true;
+    }
+    t -= mt * ntn;
+  }
+  return false;
+}
+
+template <int T, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void k_dgrad(const uint8_t* __restrict__ dy,
+                                                  const uint8_t* __restrict__ dye,
+                                                  const uint8_t* __restrict__ w,
+                                                  const uint8_t* __restrict__ we,
+                                                  const int64_t* __restrict__ offsets, int G,
+                                                  int64_t N, int64_t K, void* __restrict__ dx) {
+  constexpr int BM = T, BN = T, TM = T / 64, TN = T / 64;
+  extern __shared__ uint8_t smem[];
+  const int64_t ntn = K / BN;
+  int64_t live = 0;
+  for (int e = 0; e < G; ++e) live += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+  live *= ntn;
+  if ((int64_t)blockIdx.x >= live) return;
+  int g;
+  int64_t row0, row_end, nt;
+  dgrad_tile(offsets, G, xcd_tile(blockIdx.x, live), ntn, BM, g, row0, row_end, nt);
+  const int64_t k0 = nt * BN;
+  Operand A{dy, dye, N, 0, row0, row_end};
+  Operand B{w, we, (int64_t)G * N, (int64_t)g * N, k0, k0 + BN};
+  f32x16 acc[TM][TN];
+  zero<TM>(acc);
+  mainloop<T>(smem, A, B, N, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, half = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = k0 + wn * 64 + j * 32 + (lane & 31);
+    for (int e = 0; e < 16; ++e) {
+      const int64_t row = row0 + wm * TM * 32 + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+      if (row >= row_end) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = row0 + wm * 64 + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-        if (row < row_end) {
-          if constexpr (OUT_BF16)
-            static_cast<uint16_t*>(dx)[row * K + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
-          else
-            static_cast<float*>(dx)[row * K + col] = acc[i][j][e];
-        }
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = k0 + wn * TN * 32 + j * 32 + (lane & 31);
+        if constexpr (OUT_BF16)
+          static_cast<uint16_t*>(dx)[row * K + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+        else
+          static_cast<float*>(dx)[row * K + col] = acc[i][j][e];
       }
     }
 }
 
-__global__ __launch_bounds__(256) void k_wgrad(const uint8_t* __restrict__ dyT,
-                                               const uint8_t* __restrict__ dyTe,
-                                               const uint8_t* __restrict__ xT,
-                                               const uint8_t* __restrict__ xTe,
-                                               const int64_t* __restrict__ padded, int64_t P,
-                                               int64_t N, int64_t K, float* __restrict__ dw) {
-  __shared__ Stage st[2];
-  const int g = blockIdx.z;
-  const int64_t n0 = (int64_t)blockIdx.x * BM;
-  const int64_t k0 = (int64_t)blockIdx.y * BN;
+template <int T>
+__global__ __launch_bounds__(256, 1) void k_wgrad(const uint8_t* __restrict__ dyT,
+                                                  const uint8_t* __restrict__ dyTe,
+                                                  const uint8_t* __restrict__ xT,
+                                                  const uint8_t* __restrict__ xTe,
+                                                  const int64_t* __restrict__ padded, int G,
+                                                  int64_t P, int64_t N, int64_t K,
+                                                  float* __restrict__ dw) {
+  constexpr int BM = T, BN = T, TM = T / 64, TN = T / 64;
+  extern __shared__ uint8_t smem[];
+  // A tile's cost grows with its group's token count, so the groups are taken
+  // longest first (ties by index): workgroups are dispatched in index order,
+  // and the longest tiles start first. Within a group, tiles are n-major; with
+  // tk a multiple of 8 every XCD keeps the same k-tiles of all n-tiles.
+  const int64_t tn = N / BM, tk = K / BN, per = tn * tk;
+  const int64_t rank = blockIdx.x / per, rem = blockIdx.x % per;
+  int g = 0;
+  if (G > 1) {
+    int* seg = reinterpret_cast<int*>(smem);    // [G] segment lengths, then the answer
+    for (int h = threadIdx.x; h < G; h += 256) seg[h] = (int)(padded[h + 1] - padded[h]);
+    __syncthreads();
+    for (int h = threadIdx.x; h < G; h += 256) {
+      const int lh = seg[h];
+      int rk = 0;
+      for (int e = 0; e < G; ++e) {
+        const int le = seg[e];
+        rk += (le > lh) | ((le == lh) & (e < h));
+      }
+      if (rk == rank) seg[G] = h;
+    }
+    __syncthreads();
+    g = seg[G];
+    __syncthreads();    // the main loop reuses the memory
+  }
+  const int64_t n0 = (rem / tk) * BM, k0 = (rem % tk) * BN;
   const int64_t c0 = padded[g];
   const int64_t L = padded[g + 1] - c0;
   Operand A{dyT, dyTe, P, c0, n0, n0 + BM};
   Operand B{xT, xTe, P, c0, k0, k0 + BN};
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  mainloop(st, A, B, L, acc);
+  f32x16 acc[TM][TN];
+  zero<TM>(acc);
+  mainloop<T>(smem, A, B, L, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, half = lane >> 5;
   float* out = dw + (int64_t)g * N * K;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = k0 + wn * 64 + j * 32 + (lane & 31);
+    for (int e = 0; e < 16; ++e) {
+      const int64_t row = n0 + wm * TM * 32 + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = n0 + wm * 64 + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = k0 + wn * TN * 32 + j * 32 + (lane & 31);
         out[row * K + col] = acc[i][j][e];
       }
     }
+}
+
+template <int T>
+constexpr size_t lds_bytes() { return (size_t)2 * 2 * T * BK + (size_t)2 * 2 * T * SCB; }
+
+template <typename Kern>
+hipError_t set_lds(Kern k, size_t bytes, bool& done) {
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+template <int T>
+hipError_t dgrad_t(const uint8_t* dy, const uint8_t* dye, const uint8_t* w, const uint8_t* we,
+                   const int64_t* offsets, int G, int64_t m_cap, int64_t N, int64_t K, void* dx,
+                   bool bf16, hipStream_t stream) {
+  static bool done[2] = {false, false};
+  const int64_t tiles = ((m_cap + T - 1) / T + G) * (K / T);   // bound on live tiles
+  auto k = bf16 ? k_dgrad<T, true> : k_dgrad<T, false>;
+  hipError_t e = set_lds(k, lds_bytes<T>(), done[bf16]);
+  if (e != hipSuccess) return e;
+  k<<<(unsigned)tiles, 256, lds_bytes<T>(), stream>>>(dy, dye, w, we, offsets, G, N, K, dx);
+  return hipGetLastError();
+}
+
+template <int T>
+hipError_t wgrad_t(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* xT, const uint8_t* xTe,
+                   const int64_t* padded, int G, int64_t P, int64_t N, int64_t K, float* dw,
+                   hipStream_t stream) {
+  static bool done = false;
+  hipError_t e = set_lds(k_wgrad<T>, lds_bytes<T>(), done);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = (int64_t)G * (N / T) * (K / T);
+  k_wgrad<T><<<(unsigned)tiles, 256, lds_bytes<T>(), stream>>>(dyT, dyTe, xT, xTe, padded, G, P, N,
+                                                             K, dw);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -249,21 +429,18 @@ hipError_t launch_dgrad(const uint8_t* dy, const uint8_t* dye, const uint8_t* w,
                         const uint8_t* we, const int64_t* offsets, int G, int64_t m_cap,
                         int64_t N, int64_t K, void* dx, bool dx_bf16, hipStream_t stream) {
   if (m_cap == 0 || G == 0) return hipSuccess;
-  const dim3 grid((unsigned)(K / BN), (unsigned)((m_cap + BM - 1) / BM + G));
-  if (dx_bf16)
-    k_dgrad<true><<<grid, 256, 0, stream>>>(dy, dye, w, we, offsets, G, N, K, dx);
-  else
-    k_dgrad<false><<<grid, 256, 0, stream>>>(dy, dye, w, we, offsets, G, N, K, dx);
-  return hipGetLastError();
+  if (K % 256 == 0 && m_cap >= 256 * (int64_t)G)
+    return dgrad_t<256>(dy, dye, w, we, offsets, G, m_cap, N, K, dx, dx_bf16, stream);
+  return dgrad_t<128>(dy, dye, w, we, offsets, G, m_cap, N, K, dx, dx_bf16, stream);
 }
 
 hipError_t launch_wgrad(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* xT,
                         const uint8_t* xTe, const int64_t* padded, int G, int64_t P, int64_t N,
                         int64_t K, float* dw, hipStream_t stream) {
   if (G == 0) return hipSuccess;
-  const dim3 grid((unsigned)(N / BM), (unsigned)(K / BN), (unsigned)G);
-  k_wgrad<<<grid, 256, 0, stream>>>(dyT, dyTe, xT, xTe, padded, P, N, K, dw);
-  return hipGetLastError();
+  if (N % 256 == 0 && K % 256 == 0)
+    return wgrad_t<256>(dyT, dyTe, xT, xTe, padded, G, P, N, K, dw, stream);
+  return wgrad_t<128>(dyT, dyTe, xT, xTe, padded, G, P, N, K, dw, stream);
 }
 
 }  // namespace nvfp4moe

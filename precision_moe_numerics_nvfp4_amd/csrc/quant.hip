@@ -89,11 +89,14 @@ __global__ __launch_bounds__(256) void k_nvfp4_quantize(
     uint32_t lo = 0, hi = 0;
     if (sc) {
       const float r = __fdiv_rn(1.0f, __fmul_rn(e4m3_pos_to_f32(sc), s));
+      float a[8], b[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        lo |= e2m1_rne(__fmul_rn(v[i].get(j), r)) << (4 * j);
-        hi |= e2m1_rne(__fmul_rn(v[i].get(j + 8), r)) << (4 * j);
+        a[j] = __fmul_rn(v[i].get(j), r);
+        b[j] = __fmul_rn(v[i].get(j + 8), r);
       }
+      lo = e2m1x8_rne(a);
+      hi = e2m1x8_rne(b);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -190,12 +193,10 @@ __global__ __launch_bounds__(256) void k_mx_rowwise(const void* __restrict__ x, 
     m = fmaxf(m, __shfl_xor(m, 2, 64));
     const int e = e8m0_ceil(m);
     const float f = exp2_neg(e);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= e4m3_rne(__fmul_rn(v[j], f)) << (8 * j);
-      hi |= e4m3_rne(__fmul_rn(v[j + 4], f)) << (8 * j);
-    }
+    const uint32_t lo = e4m3x4_rne(__fmul_rn(v[0], f), __fmul_rn(v[1], f), __fmul_rn(v[2], f),
+                                   __fmul_rn(v[3], f));
+    const uint32_t hi = e4m3x4_rne(__fmul_rn(v[4], f), __fmul_rn(v[5], f), __fmul_rn(v[6], f),
+                                   __fmul_rn(v[7], f));
     if (ok) {
       *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(lo, hi);
       if ((c & 3) == 0) e8[c >> 2] = (uint8_t)(e + 127);

@@ -143,9 +143,11 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
       const float Sb = e4m3_pos_to_f32(tile.scales[t][kc >> 1]);
       const float o = tile.outer[t];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float inner = __fmul_rn(e2m1_to_f32((w >> (4 * j)) & 15u), Sb);  // exact
-        v[j][i] = __fmul_rn(inner, o);
+      for (int j = 0; j < 4; ++j) {
+        float e0, e1;
+        e2m1x2_to_f32(w, j, e0, e1);
+        v[2 * j][i] = __fmul_rn(__fmul_rn(e0, Sb), o);       // e2m1 * S is exact
+        v[2 * j + 1][i] = __fmul_rn(__fmul_rn(e1, Sb), o);
       }
     } else if constexpr (S == Src::BF16) {
       const uint4 a = *reinterpret_cast<const uint4*>(&tile.v[t][8 * kc]);
@@ -179,17 +181,15 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
     uint32_t lo = 0, hi = 0;
     if constexpr (SR) {
       const Draws8 u = draws8((uint64_t)(k * P + p) >> 3, seed, tag);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_sr(__fmul_rn(v[j][i], f), u.get(i)) << (8 * i);
-        hi |= e4m3_sr(__fmul_rn(v[j][i + 4], f), u.get(i + 4)) << (8 * i);
-      }
+      lo = e4m3x4_sr(__fmul_rn(v[j][0], f), __fmul_rn(v[j][1], f), __fmul_rn(v[j][2], f),
+                     __fmul_rn(v[j][3], f), u.get(0), u.get(1), u.get(2), u.get(3));
+      hi = e4m3x4_sr(__fmul_rn(v[j][4], f), __fmul_rn(v[j][5], f), __fmul_rn(v[j][6], f),
+                     __fmul_rn(v[j][7], f), u.get(4), u.get(5), u.get(6), u.get(7));
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_rne(__fmul_rn(v[j][i], f)) << (8 * i);
-        hi |= e4m3_rne(__fmul_rn(v[j][i + 4], f)) << (8 * i);
-      }
+      lo = e4m3x4_rne(__fmul_rn(v[j][0], f), __fmul_rn(v[j][1], f), __fmul_rn(v[j][2], f),
+                      __fmul_rn(v[j][3], f));
+      hi = e4m3x4_rne(__fmul_rn(v[j][4], f), __fmul_rn(v[j][5], f), __fmul_rn(v[j][6], f),
+                      __fmul_rn(v[j][7], f));
     }
     if (live) {
       *reinterpret_cast<uint2*>(out + k * P + p) = make_uint2(lo, hi);

@@ -85,6 +85,11 @@ def test_gemm_and_requant_argument_errors(L):
     w = L.moe_bwd_wgrad
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 40, 128, 128, FAKE, None) == EUNSUP
     assert w(None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, FAKE, None) == EINVAL
+    # 32-bit tile offsets and the in-kernel group ranking bound the sizes
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 8192, 64, 2048, 256, FAKE, 0, None) == EUNSUP
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16711936 + 32 - 16711936 % 32, 128, 128, FAKE,
+             None) == EUNSUP
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 16385, 64, 128, 128, FAKE, None) == EUNSUP
     m = L.mxfp8_quantize
     assert m(FAKE, 1, 64, 256, 9, None, None, 0, 0, FAKE, FAKE, None) == EINVAL
     assert m(FAKE, 1, 64, 48, 0, None, None, 0, 0, FAKE, FAKE, None) == EUNSUP

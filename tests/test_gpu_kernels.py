@@ -364,7 +364,9 @@ def test_dgrad(nv, counts, N, K):
     assert_gemm_close(got[:M], ref, groups, bound, what="dgrad", elementwise=False)
 
 
-@pytest.mark.parametrize("counts,N,K", [([100, 0, 37, 250], 256, 384), ([64], 512, 256), ([129, 3], 128, 128)])
+@pytest.mark.parametrize("counts,N,K", [([100, 0, 37, 250], 256, 384), ([64], 512, 256), ([129, 3], 128, 128),
+                                         # unsorted sizes with ties (tiles are ranked by size)
+                                         ([40, 300, 0, 40, 130, 300, 7], 256, 512)])
 def test_wgrad(nv, counts, N, K):
     off, pad = _groups_from_counts(counts)
     G = len(counts)
