@@ -2,7 +2,7 @@
 
 A step is one pass of the whole path over one batch of the small MoE layer
 workload (4096 tokens, d_model 1024, 8 experts, top-2 uniform routing, FFN
-1024 -> 2048, bf16 inputs; backward at the same shapes with dY ~ N(0, 1e-6)):
+1024 -> 2048, bf16 inputs; backward at the same shapes with dY ~ N(0, std 1e-3)):
 
   nvfp4_quantize(X, per token) -> nvfp4_quantize(W, per expert) -> moe_permute
   -> moe_fwd_grouped_gemm -> mxfp8_requant_sr(X_perm) -> mxfp8_requant_sr(W)
@@ -56,23 +56,24 @@ def dev_tensor(a, torch):
     return torch.from_numpy(a).cuda()
 
 
-class Timer:
-    """HIP events on the current (launch) stream around named stages."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.ev = {}
-
-    def run(self, name, fn):
-        t = self.torch
-        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        self.ev.setdefault(name, []).append((s, e))
-
-    def ms(self):
-        return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.ev.items()}
+def graph_time(torch, fn, reps):
+    """Average GPU time of one fn() call: `reps` calls are captured into one
+    HIP graph (one launch, no host overhead between kernels) and replayed
+    between two HIP events on the current stream."""
+    fn()                                   # eager first call (kernel attributes)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
 
 
 def main_step_bench(args, torch):
@@ -82,7 +83,8 @@ def main_step_bench(args, torch):
     w = gen.small_moe()
     T, K, N, E, k = w["T"], w["K"], w["N"], w["E"], w["k"]
     dy = gen.backward_dy(T * k, N)
-    L = ExpertLayerStep(T, K, N, E, k)
+    # production output types: Y and dX in bf16, dW in float32
+    L = ExpertLayerStep(T, K, N, E, k, out_dtype=torch.bfloat16)
     x_d, w_d = dev_tensor(w["x"], torch), dev_tensor(w["w"], torch)
     t_d, dy_d = dev_tensor(w["topk"], torch), dev_tensor(dy, torch)
 
@@ -100,20 +102,30 @@ def main_step_bench(args, torch):
     for _ in range(args.warmup):
         L.step(x_d, w_d, t_d, dy_d)
     torch.cuda.synchronize()
+    eager = [t.clone() for t in (L.y, L.dx, L.dw, L.xT[0], L.dyT[0])]
+    # the step is launch-bound from Python (ten calls of 10-100 us kernels), so
+    # it is captured once into a HIP graph and replayed
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        L.step(x_d, w_d, t_d, dy_d)
+    for _ in range(2):
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, (L.y, L.dx, L.dw, L.xT[0], L.dyT[0])):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay of the step differs from the eager step")
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
     # timed region: exactly `steps` whole steps, bracketed by device syncs
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        L.step(x_d, w_d, t_d, dy_d)
+        graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    # per-stage times: a second pass with events around each stage
-    tm = Timer(torch)
-    for _ in range(args.steps):
-        for name, fn in stages:
-            tm.run(name, fn)
-    torch.cuda.synchronize()
-    st = tm.ms()
+    # per-stage times: each stage alone, `steps` launches per graph
+    st = {name: graph_time(torch, fn, args.steps) for name, fn in stages}
 
     M = T * k   # top-k distinct experts, all local
     gemm_flop = 2.0 * M * N * K
@@ -155,22 +167,15 @@ def main_step_bench(args, torch):
     value = 3 * gemm_flop / (ms_step * 1e-3) / 1e12
     cfg = {"workload": "small MoE layer, forward + backward: 4096 tokens, d_model 1024, 8 experts, "
                        "top-2 uniform routing, FFN up-projection 1024->2048, bf16 inputs; "
-                       "backward at the same shapes, dY ~ N(0, 1e-6)",
+                       "backward at the same shapes, dY ~ N(0, std 1e-3); Y and dX in bf16, "
+                       "dW in float32; one step = one HIP-graph replay of the ten calls",
            "tokens": T, "d_model": K, "ffn": N, "experts": E, "top_k": k, "routed_rows": M}
     return dict(value=value, ms_step=ms_step, kernels=kernels, roofline=roof, config=cfg,
                 inputs=(w, dy))
 
 
 def _time(torch, fn, reps):
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    fn()
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(reps):
-        fn()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / reps
+    return graph_time(torch, fn, reps)
 
 
 def extras(torch, reps=10):

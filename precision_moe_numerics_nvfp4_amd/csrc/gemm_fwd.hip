@@ -295,6 +295,332 @@ __global__ __launch_bounds__(256, 1) void k_fwd(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large tiles: raw NVFP4 staged in LDS, dequantized per wavefront.
+//
+// A workgroup of 4 wavefronts owns a 256 x 256 tile of one expert; each
+// wavefront owns 128 x 128 (4 x 4 MFMA tiles). The K loop moves 128 elements
+// per stage. The stage's raw bytes (64 code bytes and 8 scale bytes per row of
+// A and of B) go from global memory straight into LDS (buffer loads with the
+// LDS-destination bit: no registers, no VALU), NS stages in flight. Each
+// wavefront reads the raw codes of its fragment rows (32 bytes per lane and
+// row per stage), converts them to f16 right before the MFMAs that use them
+// (v_cvt_scalef32_pk_f16_fp4 at unit scale, then an exact v_pk_mul_f16 by the
+// block's E4M3 scale), so LDS carries 4.5 bits per element instead of 16.
+//
+// K order inside a stage. The f16 MFMA's lane (row r, half h) supplies 8
+// consecutive k of a 16-deep step; any permutation of k shared by A and B
+// leaves the dot product unchanged, so step s takes k = s*8..s*8+7 from lanes
+// with h = 0 and k = 64+s*8..+7 from lanes with h = 1. A lane then needs
+// bytes 32h..32h+31 of its row's 64 stage bytes (two 16-byte reads) and the
+// scales of blocks 4h..4h+3 (one 32-bit read).
+//
+// LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits at
+// position c ^ ((r >> 2) & 3), so the 16 lanes of a read phase (16 rows, one
+// chunk) hit 16 distinct 16-byte bank groups. A DMA load writes 16 bytes per
+// lane at consecutive positions, so each lane fetches the global chunk that
+// belongs at its position.
+constexpr int LBK = 128;                  // K elements per stage
+constexpr int LCB = LBK / 2;              // code bytes per row per stage
+constexpr int LSB = LBK / 16;             // scale bytes per row per stage
+constexpr int LT = 256;                   // tile rows (A) and columns (B)
+constexpr int kStageBytes = 2 * LT * LCB + 2 * LT * LSB;
+constexpr int kBufWord3 = 0x00020000;     // raw buffer, 32-bit data format
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void* first_lane_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
+template <int NS, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void k_fwd_lds4(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ao,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bo,
+    const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y) {
+  constexpr int TM = 4, TN = 4;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
+
+  const int64_t ntn = N / LT;
+  const int64_t live = live_tiles(offsets, G, LT, ntn);
+  if ((int64_t)blockIdx.x >= live) return;
+  int g;
+  int64_t row0, row_end, nt;
+  tile_of(offsets, G, xcd_tile(blockIdx.x, live), LT, ntn, g, row0, row_end, nt);
+  const int64_t n0 = nt * LT;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // uniform per wavefront
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int64_t KB = K / 2, KSB = K / 16;
+  const int arows = __builtin_amdgcn_readfirstlane(
+      (int)(row_end - row0 < LT ? row_end - row0 : LT));          // valid A rows
+
+  // buffer resources (tile-relative, uniform)
+  const __amdgpu_buffer_rsrc_t rac = __builtin_amdgcn_make_buffer_rsrc(
+      first_lane_ptr(ac + row0 * KB), (short)0, (int)(uint32_t)(arows * KB), kBufWord3);
+  const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
+      first_lane_ptr(as + row0 * KSB), (short)0, (int)(uint32_t)(arows * KSB), kBufWord3);
+  const int64_t brow0 = (int64_t)g * N + n0;
+  const __amdgpu_buffer_rsrc_t rbc = __builtin_amdgcn_make_buffer_rsrc(
+      first_lane_ptr(bc + brow0 * KB), (short)0, (int)(uint32_t)(LT * KB), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rbs = __builtin_amdgcn_make_buffer_rsrc(
+      first_lane_ptr(bs + brow0 * KSB), (short)0, (int)(uint32_t)(LT * KSB), kBufWord3);
+
+  // DMA offsets of this lane. Codes: instruction i of wavefront w fills rows
+  // (4i + w) * 16 + lane / 4 at position lane % 4; scales: instruction j
+  // fills rows (4j + w) * 32 + lane / 2, dword lane % 2. Rows past the group
+  // end read the tile's first row (results discarded).
+  uint32_t oac[4], obc[4], oas[2], obs[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (4 * i + wave) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int ra = r < arows ? r : 0;
+    oac[i] = (uint32_t)(ra * KB + c * 16);
+    obc[i] = (uint32_t)(r * KB + c * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (4 * j + wave) * 32 + (lane >> 1);
+    const int ra = r < arows ? r : 0;
+    oas[j] = (uint32_t)(ra * KSB + (lane & 1) * 4);
+    obs[j] = (uint32_t)(r * KSB + (lane & 1) * 4);
+  }
+  // Stage kt goes to LDS buffer kt % NS. A stage past the end (kt >= nk) is
+  // issued too, with offsets outside the buffer ranges: such loads return
+  // zeros without a memory access and keep the count of loads per stage, and
+  // so the wait counts, fixed.
+  auto issue = [&](int64_t kt, int64_t nk) {
+    uint8_t* st = lsm + (kt % NS) * kStageBytes;
+    const bool real = kt < nk;
+    const int64_t ks = real ? kt : 0;
+    const int so = (int)(ks * LCB), ss = (int)(ks * LSB);
+    const uint32_t away = real ? 0u : 0x40000000u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_void*)(st + (4 * i + wave) * 1024), 16,
+                                               oac[i] + away, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_void*)(st + LT * LCB + (4 * i + wave) * 1024),
+                                               16, obc[i] + away, so, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ras,
+                                               (lds_void*)(st + 2 * LT * LCB + (4 * j + wave) * 256),
+                                               4, oas[j] + away, ss, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rbs, (lds_void*)(st + 2 * LT * LCB + LT * LSB + (4 * j + wave) * 256), 4, obs[j] + away,
+          ss, 0, 0);
+    }
+  };
+  constexpr int kPerStage = 12;            // DMA instructions per stage and wavefront
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int64_t nk = K / LBK;
+
+  // per-lane LDS byte offsets of the fragment reads (stage-relative)
+  int fa[TM][2], fb[TN][2], sa_off[TM], sb_off[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * 128 + i * 32 + r32;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) fa[i][c] = r * LCB + (((2 * half + c) ^ ((r >> 2) & 3)) << 4);
+    sa_off[i] = 2 * LT * LCB + r * LSB + half * 4;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int r = wn * 128 + j * 32 + r32;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) fb[j][c] = LT * LCB + r * LCB + (((2 * half + c) ^ ((r >> 2) & 3)) << 4);
+    sb_off[j] = 2 * LT * LCB + LT * LSB + r * LSB + half * 4;
+  }
+
+  // Registers: c0/c1 = raw code chunks 0/1 of the lane's rows (steps 0-3 and
+  // 4-7), sc = raw scale words, sf[.][p] = f16 scales of blocks 2p, 2p+1.
+  u32x4 c0a[TM], c0b[TN], c1a[TM], c1b[TN];
+  uint32_t sca[TM], scb[TN];
+  f16x2 sfa[TM][2], sfb[TN][2];
+  auto read_chunk = [&](const uint8_t* st, int c, u32x4 (&xa)[TM], u32x4 (&xb)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) xa[i] = *reinterpret_cast<const u32x4*>(st + fa[i][c]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const u32x4*>(st + fb[j][c]);
+  };
+  auto read_scales = [&](const uint8_t* st) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sca[i] = *reinterpret_cast<const uint32_t*>(st + sa_off[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) scb[j] = *reinterpret_cast<const uint32_t*>(st + sb_off[j]);
+  };
+  auto cvt_scales = [&](int p) {       // E4M3 -> f16, exact
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      sfa[i][p] = p ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sca[i], 1.0f, true)
+                    : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sca[i], 1.0f, false);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      sfb[j][p] = p ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scb[j], 1.0f, true)
+                    : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scb[j], 1.0f, false);
+  };
+  auto deq = [&](uint32_t x, f16x2 sp, int hi) -> f16x8 {
+    const _Float16 S = hi ? sp[1] : sp[0];
+    const f16x2 s2 = {S, S};
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s2;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s2;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s2;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s2;
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  };
+  struct Frags {
+    f16x8 a[TM], b[TN];
+  };
+  // step s: raw word s % 4 of chunk s / 4; scale block s / 2 of the lane's four
+  auto deq_step = [&](int s, Frags& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      f.a[i] = deq((s < 4 ? c0a[i] : c1a[i])[s & 3], sfa[i][s >> 2], (s >> 1) & 1);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      f.b[j] = deq((s < 4 ? c0b[j] : c1b[j])[s & 3], sfb[j][s >> 2], (s >> 1) & 1);
+  };
+  // One region: the MFMAs of step s interleaved with the conversions of the
+  // next step; the scheduling barrier keeps other steps' conversions (and
+  // their registers) out of it.
+  auto region = [&](const Frags& cur, Frags& nxt, int s_next) {
+    __builtin_amdgcn_sched_barrier(0);
+    deq_step(s_next, nxt);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        // W fragment first: the lane then holds 4 consecutive output columns
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < TM * TN; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);    // 4 VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Pipeline. NS stages are in flight in LDS. Iteration kt reads chunk 1 of
+  // stage kt, runs steps 0-3; then (mid-stage) waits for stage kt+1's loads,
+  // synchronizes, reuses the buffer of stage kt (fully read by every
+  // wavefront) for stage kt+NS, and reads chunk 0 and the scales of stage
+  // kt+1; then runs steps 4-7, the last region converting step 0 of kt+1.
+  // LDS reads thus always overlap MFMAs, and there is one barrier per stage.
+  static_assert(kPerStage == 12, "wait counts assume 12 loads per stage and wavefront");
+  static_assert(NS == 3, "wait counts assume 3 stages in flight");
+#pragma unroll
+  for (int p = 0; p < NS; ++p) issue(p, nk);
+  asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");   // stage 0 landed
+  read_chunk(lsm, 0, c0a, c0b);
+  read_scales(lsm);
+  cvt_scales(0);
+  Frags f0, f1;
+  deq_step(0, f0);
+
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const uint8_t* st = lsm + (kt % NS) * kStageBytes;
+    read_chunk(st, 1, c1a, c1b);
+    cvt_scales(1);
+    region(f0, f1, 1);
+    region(f1, f0, 2);
+    region(f0, f1, 3);
+    region(f1, f0, 4);
+    {
+      // Every wavefront has finished reading stage kt, and stage kt+1 has
+      // landed once only stage kt+2's loads are pending. Branch-free: after
+      // the last stage this reads data that is never used.
+      asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      issue(kt + NS, nk);
+      const uint8_t* sn = lsm + ((kt + 1) % NS) * kStageBytes;
+      read_chunk(sn, 0, c0a, c0b);
+      read_scales(sn);
+      cvt_scales(0);
+    }
+    region(f0, f1, 5);
+    region(f1, f0, 6);
+    region(f0, f1, 7);
+    region(f1, f0, 0);       // step 0 of stage kt+1 (unused after the last stage)
+  }
+
+  // Epilogue. acc[i][j][4q+v] = Y[row, col] with row = wm*128 + i*32 + lane%32
+  // and col = wn*128 + j*32 + 8q + 4*half + v (the MFMAs took W first). Each
+  // wavefront stages one 32-row block at a time in LDS (row-major, scaled and
+  // converted), then writes it out 16 bytes per lane along the rows, so the
+  // global stores cover whole row segments.
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");   // stage buffers are free
+  constexpr int ES = OUT_BF16 ? 2 : 4;                   // output element bytes
+  constexpr int RS = 128 * ES + 16;                     // LDS row stride (padded)
+  uint8_t* ep = lsm + wave * (32 * RS);
+  const float sw = bo[g];
+  const int64_t col0 = n0 + wn * 128;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int rl = i * 32 + r32;                         // row within the wavefront's block
+    const int64_t row = row0 + wm * 128 + rl;
+    const float sx = row < row_end ? ao[row] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = __fmul_rn(__fmul_rn(acc[i][j][4 * q + t], sx), sw);
+        uint8_t* d = ep + r32 * RS + (j * 32 + 8 * q + 4 * half) * ES;
+        if constexpr (OUT_BF16) {
+          const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+          *reinterpret_cast<uint2*>(d) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    // 32 rows x 128 columns: each lane copies 16-byte pieces along the rows
+    constexpr int PPR = 128 * ES / 16;                  // pieces per row
+#pragma unroll
+    for (int it = 0; it < 32 * PPR / 64; ++it) {
+      const int pc = it * 64 + lane, r = pc / PPR, c = pc % PPR;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(ep + r * RS + c * 16);
+      const int64_t orow = row0 + wm * 128 + i * 32 + r;
+      if (orow < row_end)
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(y) + (orow * N + col0) * ES + c * 16) = val;
+    }
+  }
+}
+
+template <int NS>
+hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
+                       const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
+                       int64_t m_cap, int64_t N, int64_t K, void* y, bool y_bf16,
+                       hipStream_t stream) {
+  const size_t lds = (size_t)NS * kStageBytes;
+  const int64_t tiles = ((m_cap + LT - 1) / LT + G) * (N / LT);   // bound on live tiles
+  auto k = y_bf16 ? k_fwd_lds4<NS, true> : k_fwd_lds4<NS, false>;
+  static bool attr_set[2] = {false, false};
+  if (!attr_set[y_bf16]) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set[y_bf16] = true;
+  }
+  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_cfg(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
                       const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
@@ -325,8 +651,7 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
   if (m_cap <= 64 * (int64_t)G || N % 256 != 0)
     return launch_cfg<32, 128, 1, 4>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
                                      stream);
-  return launch_cfg<256, 256, 2, 2>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
-                                    stream);
+  return launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, stream);
 }
 
 }  // namespace nvfp4moe
