@@ -32,6 +32,7 @@
 // the four wavefronts split N instead of M.
 #include "codecs.hpp"
 #include "internal.hpp"
+#include "tiles.hpp"
 
 namespace nvfp4moe {
 
@@ -621,6 +622,290 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Few routed rows per expert (decode): weight streaming through LDS.
+//
+// Units of 16 routed rows of one expert by 64 outputs (64 weight rows) are
+// enumerated expert by expert. One persistent workgroup per compute unit
+// takes units round-robin and runs through their K stages (512 elements
+// each) as one stream: each stage's weight bytes (64 rows x 256 code bytes
+// + 32 scale bytes) and activation bytes (16 rows, same) go from HBM straight
+// into an LDS ring of SK_S stages (buffer loads with the LDS-destination
+// bit), so about 90 KB per compute unit are in flight without holding
+// registers. Eight wavefronts, two per SIMD so that one computes while the
+// other waits: wavefront w owns outputs 16 (w % 4) .. +15 and half of each
+// stage's K (sub-chunks 2 (w / 4) and 2 (w / 4) + 1 of 128 elements); it
+// converts its weight and activation codes to f16 and runs
+// v_mfma_f32_16x16x32_f16. The two halves' sums meet in LDS at the end of a
+// unit.
+//
+// K order inside a 128-element sub-chunk: A and B share one permutation of
+// k; the lanes with l / 16 = q supply k = 32q .. 32q+31, eight per step.
+// LDS rows hold 16 pieces of 16 bytes; piece p of row r sits at position
+// p ^ (r & 15), so the 16 rows read at one piece offset hit distinct banks.
+constexpr int SK_T = 16;                      // routed rows per unit
+constexpr int SK_N = 64;                      // outputs (weight rows) per unit
+constexpr int SK_K = 512;                     // K elements per stage
+constexpr int SK_S = 5;                       // stages in the LDS ring
+constexpr int SK_RB = SK_K / 2;               // code bytes per row per stage
+constexpr int SK_SB = SK_K / 16;              // scale bytes per row per stage
+constexpr int SK_WC = 0;                      // [64][256] weight codes
+constexpr int SK_XC = SK_WC + SK_N * SK_RB;   // [16][256] activation codes
+constexpr int SK_WS = SK_XC + SK_T * SK_RB;   // [64][32] weight scales
+constexpr int SK_XS = SK_WS + SK_N * SK_SB;   // [16][32] activation scales
+constexpr int SK_STAGE = SK_XS + SK_T * SK_SB;
+constexpr int SK_DMA = 5;                     // DMA instructions per stage and wavefront
+constexpr int SK_RED = 4 * 64 * 16;           // partial sums of the upper K halves
+constexpr int SK_MAXG = 1024;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x8 deq8(uint32_t x, f16x2 sp, int hi) {
+  const _Float16 S = hi ? sp[1] : sp[0];
+  const f16x2 s2 = {S, S};
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s2;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s2;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s2;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s2;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void k_fwd_stream(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ao,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bo,
+    const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
+  float* red = reinterpret_cast<float*>(lsm + SK_S * SK_STAGE);      // [4][64 lanes][4]
+  int64_t* off = reinterpret_cast<int64_t*>(lsm + SK_S * SK_STAGE + SK_RED);   // [G+1]
+  int* pre = reinterpret_cast<int*>(off + G + 1);                     // [G+1]
+  const int nnb = (int)(N / SK_N);
+  for (int e = threadIdx.x; e <= G; e += 512) off[e] = offsets[e];
+  tile_prefix(G, [&](int e) {
+    return (int)((offsets[e + 1] - offsets[e] + SK_T - 1) / SK_T) * nnb;
+  }, pre);
+  const int total = pre[G];
+  if ((int)blockIdx.x >= total) return;
+  const int nunits = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int nst = (int)(K / SK_K);                  // stages per unit
+  const int nall = nunits * nst;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wn = wave & 3, wk = wave >> 2;          // output block, K half
+  const int r = lane & 15, q = lane >> 4;
+  const int64_t KB = K / 2, KSB = K / 16;
+
+  struct Unit {
+    int g, nb;
+    int64_t row0, row_end;
+  };
+  auto rfl64 = [](int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  auto unit = [&](int j) {            // the same for the whole workgroup
+    const int t = (int)blockIdx.x + j * (int)gridDim.x;
+    Unit u;
+    u.g = __builtin_amdgcn_readfirstlane(tile_group(pre, G, t));
+    const int loc = t - pre[u.g];
+    u.nb = __builtin_amdgcn_readfirstlane(loc % nnb);
+    u.row0 = rfl64(off[u.g] + (int64_t)(loc / nnb) * SK_T);
+    u.row_end = rfl64(off[u.g + 1]);
+    return u;
+  };
+
+  // DMA lane offsets (stage- and unit-relative). Codes: instruction m fills
+  // rows 4m .. 4m+3 (lane: row 4m + lane/16, position lane%16). Scales:
+  // instruction m fills rows 8m .. 8m+7 (lane: row 8m + lane/8, dword lane%8).
+  // Wavefronts 4-7 repeat the activation loads of 0-3 (same bytes, same place).
+  int wrow_c[2], wpiece[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 4 * (2 * wave + i) + (lane >> 4);
+    wrow_c[i] = row;
+    wpiece[i] = (lane & 15) ^ (row & 15);
+  }
+  const int xrow_c = 4 * wn + (lane >> 4);
+  const int xpiece = (lane & 15) ^ (xrow_c & 15);
+  const int wrow_s = 8 * wave + (lane >> 3);
+  const int xrow_s = 8 * (wave & 1) + (lane >> 3);
+  const int sdw = (lane & 7) * 4;
+
+  // Issue cursor: stage ist of unit ij goes to ring buffer ibuf. The unit's
+  // buffer resources are rebuilt only when the cursor enters a new unit.
+  // Past the end of the stream the last stage is re-issued with offsets
+  // outside the ranges (zeros, no memory traffic), keeping the count per stage.
+  int ij = 0, ist = 0, ibuf = 0;
+  __amdgpu_buffer_rsrc_t rwc, rws, rxc, rxs;
+  int ixrows = 0;
+  auto set_unit = [&](int j) {
+    const Unit u = unit(j);
+    const int64_t wr0 = (int64_t)u.g * N + (int64_t)u.nb * SK_N;
+    ixrows = (int)(u.row_end - u.row0 < SK_T ? u.row_end - u.row0 : SK_T);
+    rwc = __builtin_amdgcn_make_buffer_rsrc(first_lane_ptr(bc + wr0 * KB), (short)0,
+                                            (int)(uint32_t)(SK_N * KB), kBufWord3);
+    rws = __builtin_amdgcn_make_buffer_rsrc(first_lane_ptr(bs + wr0 * KSB), (short)0,
+                                            (int)(uint32_t)(SK_N * KSB), kBufWord3);
+    rxc = __builtin_amdgcn_make_buffer_rsrc(first_lane_ptr(ac + u.row0 * KB), (short)0,
+                                            (int)(uint32_t)(ixrows * KB), kBufWord3);
+    rxs = __builtin_amdgcn_make_buffer_rsrc(first_lane_ptr(as + u.row0 * KSB), (short)0,
+                                            (int)(uint32_t)(ixrows * KSB), kBufWord3);
+  };
+  set_unit(0);
+  auto issue = [&]() {
+    const uint32_t away = ij < nunits ? 0u : 0x40000000u;
+    uint8_t* sb = lsm + ibuf * SK_STAGE;
+    const int cofs = ist * SK_RB, sofs = ist * SK_SB;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rwc, (lds_void*)(sb + SK_WC + (2 * wave + k) * 1024), 16,
+          (uint32_t)(wrow_c[k] * KB + wpiece[k] * 16) + away, cofs, 0, 0);
+    {
+      const int xr = xrow_c < ixrows ? xrow_c : 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rxc, (lds_void*)(sb + SK_XC + wn * 1024), 16,
+                                               (uint32_t)(xr * KB + xpiece * 16) + away, cofs, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, (lds_void*)(sb + SK_WS + wave * 256), 4,
+                                             (uint32_t)(wrow_s * KSB + sdw) + away, sofs, 0, 0);
+    {
+      const int xr = xrow_s < ixrows ? xrow_s : 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_void*)(sb + SK_XS + (wave & 1) * 256), 4,
+                                               (uint32_t)(xr * KSB + sdw) + away, sofs, 0, 0);
+    }
+    ibuf = ibuf + 1 == SK_S ? 0 : ibuf + 1;
+    if (ij < nunits && ++ist == nst) {
+      ist = 0;
+      if (++ij < nunits) set_unit(ij);
+      else ist = nst - 1;                     // stay on the last stage
+    }
+  };
+
+  // fragment read offsets (stage-relative): weight row 16 wn + r and
+  // activation row r, sub-chunks 2 wk and 2 wk + 1
+  const int wr = 16 * wn + r;
+  int wfo[2], xfo[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int sc = 2 * wk + h;
+    wfo[h] = SK_WC + wr * SK_RB + (((4 * sc + q) ^ (wr & 15)) << 4);
+    xfo[h] = SK_XC + r * SK_RB + (((4 * sc + q) ^ (r & 15)) << 4);
+  }
+  const int wso = SK_WS + wr * SK_SB + q * 2 + wk * 16, xso = SK_XS + r * SK_SB + q * 2 + wk * 16;
+
+  static_assert(SK_DMA == 5 && SK_S == 5, "the wait count assumes 5 loads per stage, 5 stages");
+#pragma unroll
+  for (int p = 0; p < SK_S - 1; ++p) issue();
+
+  f32x4 part[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) part[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // compute cursor: stage cst of unit cj, in ring buffer cbuf
+  int cj = 0, cst = 0, cbuf = 0;
+  Unit cu = unit(0);
+  float sx = 0.0f, sg = 0.0f;
+  for (int i = 0; i < nall; ++i) {
+    // stage i has landed once only the 3 younger stages' loads are pending,
+    // and every wavefront is done with the buffer that stage i+4 reuses
+    asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory");
+    issue();
+    const int st = cst;
+    if (st == 0) {
+      // a new unit: its output scales, through scalar loads (uniform
+      // addresses), which a vector-memory wait would otherwise have to
+      // cover together with every load in flight
+      float sr[SK_T];
+#pragma unroll
+      for (int t = 0; t < SK_T; ++t) {
+        const int64_t row = rfl64(cu.row0 + t < cu.row_end ? cu.row0 + t : cu.row0);
+        sr[t] = __builtin_nontemporal_load(ao + row);
+      }
+      sx = sr[0];
+#pragma unroll
+      for (int t = 1; t < SK_T; ++t) sx = r == t ? sr[t] : sx;
+      sg = bo[cu.g];
+    }
+    const uint8_t* sb = lsm + cbuf * SK_STAGE;
+    cbuf = cbuf + 1 == SK_S ? 0 : cbuf + 1;
+    u32x4 wv[2], xv[2];
+    uint32_t wsc[2], xsc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      wv[h] = *reinterpret_cast<const u32x4*>(sb + wfo[h]);
+      xv[h] = *reinterpret_cast<const u32x4*>(sb + xfo[h]);
+      wsc[h] = *reinterpret_cast<const uint16_t*>(sb + wso + h * 8);
+      xsc[h] = *reinterpret_cast<const uint16_t*>(sb + xso + h * 8);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f16x2 sw2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsc[h], 1.0f, false);
+      const f16x2 sx2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xsc[h], 1.0f, false);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)    // k = 32q + 8k .. +7 of the sub-chunk: word k, block k/2
+        part[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(deq8(wv[h][k], sw2, k >> 1),
+                                                         deq8(xv[h][k], sx2, k >> 1), part[k],
+                                                         0, 0, 0);
+    }
+    if (st == nst - 1) {
+      // unit done: D[n][t] with n = 4q + v, t = r; the upper K half is added
+      // to the lower one through LDS
+      f32x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
+      if (wk == 1) *reinterpret_cast<f32x4*>(red + (wn * 64 + lane) * 4) = acc;
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (wk == 0) {
+        acc += *reinterpret_cast<const f32x4*>(red + (wn * 64 + lane) * 4);
+        const Unit u = cu;
+        const int64_t row = u.row0 + r;
+        if (row < u.row_end) {
+          float o[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] = __fmul_rn(__fmul_rn(acc[v], sx), sg);
+          const int64_t col = (int64_t)u.nb * SK_N + 16 * wn + 4 * q;
+          if constexpr (OUT_BF16) {
+            const uint32_t lo = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + row * N + col) =
+                make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(y) + row * N + col) =
+                make_float4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) part[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      cst = 0;
+      if (++cj < nunits) cu = unit(cj);
+    } else {
+      ++cst;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing (unused) loads
+}
+
+hipError_t launch_stream(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
+                         const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
+                         int64_t m_cap, int64_t N, int64_t K, void* y, bool y_bf16,
+                         hipStream_t stream) {
+  auto k = y_bf16 ? k_fwd_stream<true> : k_fwd_stream<false>;
+  const size_t base = (size_t)SK_S * SK_STAGE + SK_RED;
+  const size_t lds = base + (size_t)(G + 1) * (sizeof(int64_t) + sizeof(int));
+  static bool attr_set[2] = {false, false};
+  if (!attr_set[y_bf16]) {
+    const size_t maxl = base + (size_t)(SK_MAXG + 1) * 12;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)maxl);
+    if (e != hipSuccess) return e;
+    attr_set[y_bf16] = true;
+  }
+  const int64_t bound = ((m_cap + SK_T - 1) / SK_T + G) * (N / SK_N);   // units, upper bound
+  const int64_t slots = device_cu_count();
+  const int64_t grid = bound < slots ? bound : slots;
+  k<<<(unsigned)grid, 512, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_cfg(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
                       const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
@@ -647,7 +932,11 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
                                    const int64_t* offsets, int G, int64_t m_cap, int64_t N,
                                    int64_t K, void* y, bool y_bf16, hipStream_t stream) {
   if (m_cap == 0 || G == 0) return hipSuccess;
-  // few rows per expert (decode): 32-row tiles, the wavefronts split N
+  // a few rows per expert (decode): weight streaming, 16-row tiles
+  if (m_cap <= 32 * (int64_t)G && K % SK_K == 0 && N % SK_N == 0 && G <= SK_MAXG &&
+      ((m_cap + SK_T - 1) / SK_T + G) * (N / SK_N) < (int64_t)1 << 31)
+    return launch_stream(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, stream);
+  // 32-row tiles, the wavefronts split N
   if (m_cap <= 64 * (int64_t)G || N % 256 != 0)
     return launch_cfg<32, 128, 1, 4>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
                                      stream);

@@ -292,7 +292,10 @@ def _fwd_bound(ac, asc, ao, wc, ws, wo, off, N, K):
 
 @pytest.mark.parametrize("T,K,N,E,k", [(300, 512, 256, 4, 2), (64, 256, 512, 1, 1), (500, 384, 384, 6, 3),
                                          # 256-row tiles: one K stage; several m- and n-tiles, ragged ends
-                                         (700, 128, 512, 3, 2), (1000, 1024, 256, 2, 1)])
+                                         (700, 128, 512, 3, 2), (1000, 1024, 256, 2, 1),
+                                         # few rows per expert (weight streaming): one and two
+                                         # 16-row blocks per expert, one or three K chunks per wave
+                                         (100, 512, 256, 16, 2), (60, 1536, 128, 8, 4)])
 def test_fwd_grouped_gemm(nv, T, K, N, E, k):
     import torch
     ac, asc, ao, wc, ws, wo, off = _fwd_case(700 + T, T, K, N, E, k)
