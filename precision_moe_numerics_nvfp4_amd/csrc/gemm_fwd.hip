@@ -30,6 +30,8 @@
 //
 // Small groups (decode: a few rows per expert) use a 32-row variant in which
 // the four wavefronts split N instead of M.
+#include <type_traits>
+
 #include "codecs.hpp"
 #include "internal.hpp"
 #include "tiles.hpp"
@@ -345,13 +347,42 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   constexpr int TM = 4, TN = 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
 
-  const int64_t ntn = N / LT;
-  const int64_t live = live_tiles(offsets, G, LT, ntn);
-  if ((int64_t)blockIdx.x >= live) return;
-  int g;
-  int64_t row0, row_end, nt;
-  tile_of(offsets, G, xcd_tile(blockIdx.x, live), LT, ntn, g, row0, row_end, nt);
-  const int64_t n0 = nt * LT;
+  // Tiles: every group's full 256-row tiles first (group, n-tile, m-tile
+  // fastest), then every group's partial last m-tile; each part is split
+  // XCD-contiguously. The full tiles thus fill the first wave of workgroups
+  // and the cheaper partial ones (only their valid row blocks run MFMAs)
+  // come last.
+  const int ntn = (int)(N / LT);
+  int g, nt;
+  int64_t row0, row_end;
+  {
+    int* pre = reinterpret_cast<int*>(lsm);            // [2G+1], before any stage load
+    tile_prefix(2 * G, [&](int e) {
+      const int gg = e < G ? e : e - G;
+      const int64_t m = offsets[gg + 1] - offsets[gg];
+      return (int)(e < G ? m / LT : (m % LT != 0 ? 1 : 0)) * ntn;
+    }, pre);
+    const int nfull = pre[G], total = pre[2 * G];
+    if ((int)blockIdx.x >= total) return;
+    const int t = (int)blockIdx.x;
+    const int tt = t < nfull ? (int)xcd_tile(t, nfull)
+                             : nfull + (int)xcd_tile(t - nfull, total - nfull);
+    const int e = tile_group(pre, 2 * G, tt);
+    const int loc = tt - pre[e];
+    g = e < G ? e : e - G;
+    const int64_t o0 = offsets[g];
+    row_end = offsets[g + 1];
+    const int64_t fm = (row_end - o0) / LT;
+    if (e < G) {
+      nt = (int)(loc / fm);
+      row0 = o0 + (loc % fm) * LT;
+    } else {
+      nt = loc;
+      row0 = o0 + fm * LT;
+    }
+    __syncthreads();                                   // pre's memory is reused below
+  }
+  const int64_t n0 = (int64_t)nt * LT;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // uniform per wavefront
@@ -448,26 +479,35 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     sb_off[j] = 2 * LT * LCB + LT * LSB + r * LSB + half * 4;
   }
 
+  // The wavefront's rows of A: TA of its TM 32-row blocks hold valid rows
+  // (a partial tile has fewer); only those are read, converted and
+  // multiplied. TA = 0 keeps only the loads and barriers.
+  auto mainloop = [&](auto ta_c) {
+  constexpr int TA = decltype(ta_c)::value;
+  constexpr int TAA = TA > 0 ? TA : 1;            // array extent
   // Registers: c0/c1 = raw code chunks 0/1 of the lane's rows (steps 0-3 and
   // 4-7), sc = raw scale words, sf[.][p] = f16 scales of blocks 2p, 2p+1.
-  u32x4 c0a[TM], c0b[TN], c1a[TM], c1b[TN];
-  uint32_t sca[TM], scb[TN];
-  f16x2 sfa[TM][2], sfb[TN][2];
-  auto read_chunk = [&](const uint8_t* st, int c, u32x4 (&xa)[TM], u32x4 (&xb)[TN]) {
+  u32x4 c0a[TAA], c0b[TN], c1a[TAA], c1b[TN];
+  uint32_t sca[TAA], scb[TN];
+  f16x2 sfa[TAA][2], sfb[TN][2];
+  auto read_chunk = [&](const uint8_t* st, int c, u32x4 (&xa)[TAA], u32x4 (&xb)[TN]) {
+    if constexpr (TA == 0) return;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) xa[i] = *reinterpret_cast<const u32x4*>(st + fa[i][c]);
+    for (int i = 0; i < TA; ++i) xa[i] = *reinterpret_cast<const u32x4*>(st + fa[i][c]);
 #pragma unroll
     for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const u32x4*>(st + fb[j][c]);
   };
   auto read_scales = [&](const uint8_t* st) {
+    if constexpr (TA == 0) return;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sca[i] = *reinterpret_cast<const uint32_t*>(st + sa_off[i]);
+    for (int i = 0; i < TA; ++i) sca[i] = *reinterpret_cast<const uint32_t*>(st + sa_off[i]);
 #pragma unroll
     for (int j = 0; j < TN; ++j) scb[j] = *reinterpret_cast<const uint32_t*>(st + sb_off[j]);
   };
   auto cvt_scales = [&](int p) {       // E4M3 -> f16, exact
+    if constexpr (TA == 0) return;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TA; ++i)
       sfa[i][p] = p ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sca[i], 1.0f, true)
                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sca[i], 1.0f, false);
 #pragma unroll
@@ -485,12 +525,13 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
   };
   struct Frags {
-    f16x8 a[TM], b[TN];
+    f16x8 a[TAA], b[TN];
   };
   // step s: raw word s % 4 of chunk s / 4; scale block s / 2 of the lane's four
   auto deq_step = [&](int s, Frags& f) {
+    if constexpr (TA == 0) return;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TA; ++i)
       f.a[i] = deq((s < 4 ? c0a[i] : c1a[i])[s & 3], sfa[i][s >> 2], (s >> 1) & 1);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -500,16 +541,17 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   // next step; the scheduling barrier keeps other steps' conversions (and
   // their registers) out of it.
   auto region = [&](const Frags& cur, Frags& nxt, int s_next) {
+    if constexpr (TA == 0) return;
     __builtin_amdgcn_sched_barrier(0);
     deq_step(s_next, nxt);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TA; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         // W fragment first: the lane then holds 4 consecutive output columns
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int m = 0; m < TM * TN; ++m) {
+    for (int m = 0; m < TA * TN; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);    // 4 VALU
     }
@@ -556,6 +598,15 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     region(f1, f0, 6);
     region(f0, f1, 7);
     region(f1, f0, 0);       // step 0 of stage kt+1 (unused after the last stage)
+  }
+  };
+  {
+    const int act = (arows - wm * 128 + 31) >> 5;      // valid 32-row blocks of this wavefront
+    if (act >= 4) mainloop(std::integral_constant<int, 4>{});
+    else if (act == 3) mainloop(std::integral_constant<int, 3>{});
+    else if (act == 2) mainloop(std::integral_constant<int, 2>{});
+    else if (act == 1) mainloop(std::integral_constant<int, 1>{});
+    else mainloop(std::integral_constant<int, 0>{});
   }
 
   // Epilogue. acc[i][j][4q+v] = Y[row, col] with row = wm*128 + i*32 + lane%32
@@ -937,7 +988,7 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
       ((m_cap + SK_T - 1) / SK_T + G) * (N / SK_N) < (int64_t)1 << 31)
     return launch_stream(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, stream);
   // 32-row tiles, the wavefronts split N
-  if (m_cap <= 64 * (int64_t)G || N % 256 != 0)
+  if (m_cap <= 64 * (int64_t)G || N % 256 != 0 || G > 8192)
     return launch_cfg<32, 128, 1, 4>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
                                      stream);
   return launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, stream);
