@@ -17,6 +17,7 @@ share forward GEMMs (48 local experts, 32768 tokens top-8 Zipf), the decode
 GEMMs and the 1 GiB streaming quantize/requant.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--cpu-seconds S]
+       python bench.py --calibrate-copy     (reference kernel for the HBM byte counters)
 """
 
 import argparse
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="0 skips the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run three 256 MiB device copies (the known-size reference for "
+                         "HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -54,6 +58,39 @@ def dev_tensor(a, torch):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     return torch.from_numpy(a).cuda()
+
+
+# kernel source each bench stage runs (the HBM traffic record is void once it changes)
+STAGE_SOURCE = {
+    "moe_fwd_grouped_gemm": "gemm_fwd.hip", "moe_bwd_dgrad": "gemm_bwd.hip",
+    "moe_bwd_wgrad": "gemm_bwd.hip", "nvfp4_quantize_x": "quant.hip", "nvfp4_quantize_w": "quant.hip",
+    "mxfp8_requant_sr_x": "requant.hip", "mxfp8_requant_sr_w": "requant.hip",
+    "mxfp8_quantize_dy": "requant.hip", "moe_permute": "permute.hip",
+}
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of `stage` from the counter record in
+    profiles/hbm_traffic.md (rocprofv3 FETCH_SIZE and WRITE_SIZE runs, scaled
+    by a copy kernel's readings), or None when there is no record or the
+    kernel source has changed since it was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    src = STAGE_SOURCE.get(stage)
+    if not src or not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get(stage)
+    if not rec:
+        return None
+    code = os.path.join(ROOT, "precision_moe_numerics_nvfp4_amd", "csrc", src)
+    digest = hashlib.sha256(open(code, "rb").read()).hexdigest()[:16]
+    if rec.get("source_sha256_16") != digest:
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def graph_time(torch, fn, reps):
@@ -155,15 +192,21 @@ def main_step_bench(args, torch):
     dom = max(st, key=lambda n: st[n])
     kind, amount = work[dom]
     sec = st[dom] * 1e-3
+    traffic = measured_traffic(dom)
     if kind == "hbm":
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / sec / 1e9, 1),
                 "peak": 8000.0, "unit": "GB/s", "frac": round(amount / sec / PEAK["hbm"], 4),
-                "traffic": None, "algorithmic_bytes_per_launch": amount}
+                "traffic": traffic, "algorithmic_bytes_per_launch": amount}
     else:
+        # the forward GEMM takes NVFP4 operands but contracts exactly in f16 on
+        # the f16 MFMA (the FP4 MFMA's power-of-two block scales cannot carry
+        # NVFP4's E4M3 scales), so the f16 MFMA peak is its roofline
+        pipe = "f16" if kind == "fp4" else kind
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(amount / sec / 1e12, 2),
-                "peak": PEAK[kind] / 1e12, "unit": "TFLOP/s",
-                "frac": round(amount / sec / PEAK[kind], 4), "traffic": None,
-                "algorithmic_flop_per_launch": amount, "operand_dtype": kind}
+                "peak": PEAK[pipe] / 1e12, "unit": "TFLOP/s",
+                "frac": round(amount / sec / PEAK[pipe], 4), "traffic": traffic,
+                "algorithmic_flop_per_launch": amount, "operands": kind, "mfma_pipe": pipe,
+                "frac_of_operand_dtype_peak": round(amount / sec / PEAK[kind], 4)}
     value = 3 * gemm_flop / (ms_step * 1e-3) / 1e12
     cfg = {"workload": "small MoE layer, forward + backward: 4096 tokens, d_model 1024, 8 experts, "
                        "top-2 uniform routing, FFN up-projection 1024->2048, bf16 inputs; "
@@ -320,6 +363,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)                     # 256 MiB read, 256 MiB written
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": 256 << 20, "copies": 3}))
+        return
     from precision_moe_numerics_nvfp4_amd import binding
     if not os.path.exists(binding.LIB_PATH):
         from precision_moe_numerics_nvfp4_amd import build as _b

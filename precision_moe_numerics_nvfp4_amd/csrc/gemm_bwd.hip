@@ -33,6 +33,7 @@
 // cost is its group's token count).
 #include "codecs.hpp"
 #include "internal.hpp"
+#include "tiles.hpp"
 
 namespace nvfp4moe {
 
@@ -385,6 +386,306 @@ __global__ __launch_bounds__(256, 1) void k_wgrad(const uint8_t* __restrict__ dy
     }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles through an LDS ring filled by DMA.
+//
+// The operands' bytes go from global memory straight into LDS (buffer loads
+// with the LDS-destination bit), four 64-element stages in flight, so the
+// wavefronts hold no staging registers. A stage is 256 rows x 64 bytes of
+// each operand (16-byte pieces, piece c of row r at position
+// c ^ ((r >> 2) & 3), so the 16 rows of a read phase hit distinct banks) plus
+// the two scale bytes of each row (one byte per 4-byte LDS slot, as the
+// byte-wide DMA writes them). Each stage is one 64-deep MFMA step; the
+// fragments of stage kt+1 are read from LDS while the MFMAs of stage kt run.
+// A ragged contraction end (wgrad) is a multiple of 32: when the last stage
+// holds only its first MX block, the second block's bytes are zeroed in the
+// fragments and its scale set to 1.
+constexpr int DK = 64;                                // contraction elements per stage
+constexpr int DS = 4;                                 // stages in the ring
+constexpr int D_A = 0, D_B = 256 * DK;                // code planes [256][64]
+constexpr int D_SC = 2 * 256 * DK;                    // scale planes [op][byte][256 rows][4]
+constexpr int D_STAGE = D_SC + 2 * 2 * 256 * 4;       // 36 KiB
+constexpr int D_DMA = 12;                             // DMA instructions per stage and wavefront
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void mainloop_dma(uint8_t* lsm, const Operand& A, const Operand& B,
+                                             int64_t L, f32x16 (&acc)[4][4]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int64_t nk = (L + DK - 1) / DK;
+  if (nk == 0) return;
+
+  __amdgpu_buffer_rsrc_t rq[2], re[2];
+  int nrow[2];
+  int64_t ld[2], c0[2];
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    const Operand& X = o ? B : A;
+    const int64_t n = X.row_end - X.row0;
+    nrow[o] = __builtin_amdgcn_readfirstlane((int)(n < 256 ? n : 256));
+    ld[o] = X.ld;
+    c0[o] = X.c0;
+    rq[o] = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X.q + X.row0 * X.ld), (short)0,
+                                              uniform_u32(n * X.ld), kBufferWord3);
+    re[o] = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X.e + X.row0 * (X.ld / 32)), (short)0,
+                                              uniform_u32(n * (X.ld / 32)), kBufferWord3);
+  }
+  // lane offsets: code instruction i of this wavefront fills rows 16m .. 16m+15
+  // (m = 4i + wave; lane: row 16m + lane/4, position lane%4); scale instruction
+  // j fills byte (wave & 1) of rows 64j + lane of operand wave >> 1
+  uint32_t oq[2][4], oe[4];
+#pragma unroll
+  for (int o = 0; o < 2; ++o)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * (4 * i + wave) + (lane >> 2);
+      const int piece = (lane & 3) ^ ((row >> 2) & 3);
+      const int rr = row < nrow[o] ? row : 0;
+      oq[o][i] = (uint32_t)(rr * ld[o] + c0[o] + piece * 16);
+    }
+  const int so = wave >> 1, sb = wave & 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 64 * j + lane;
+    const int rr = row < nrow[so] ? row : 0;
+    oe[j] = (uint32_t)(rr * (ld[so] / 32) + c0[so] / 32 + sb);
+  }
+  // stage kt -> buffer kt % DS; past the end: offsets outside the ranges
+  // (zeros, no memory traffic) so every stage has the same load count
+  auto issue = [&](int64_t kt) {
+    uint8_t* st = lsm + (kt % DS) * D_STAGE;
+    const bool real = kt < nk;
+    const uint32_t away = real ? 0u : 0x40000000u;
+    const uint32_t kq = real ? (uint32_t)(kt * DK) : 0u, ke = real ? (uint32_t)(kt * 2) : 0u;
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rq[o], (lds_void*)(st + (o ? D_B : D_A) + (4 * i + wave) * 1024), 16,
+            oq[o][i] + kq + away, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          so ? re[1] : re[0], (lds_void*)(st + D_SC + ((so * 2 + sb) * 256 + 64 * j) * 4), 1,
+          oe[j] + ke + away, 0, 0, 0);
+  };
+
+  // fragment addresses (stage-relative)
+  int fa[4][2], fb[4][2], sa[4], sbo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + r32, rb = wn * 128 + i * 32 + r32;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      fa[i][c] = D_A + ra * DK + (((2 * c + half) ^ ((ra >> 2) & 3)) << 4);
+      fb[i][c] = D_B + rb * DK + (((2 * c + half) ^ ((rb >> 2) & 3)) << 4);
+    }
+    sa[i] = D_SC + ((0 * 2 + half) * 256 + ra) * 4;
+    sbo[i] = D_SC + ((1 * 2 + half) * 256 + rb) * 4;
+  }
+  struct Frag {
+    i32x8 a[4], b[4];
+    int32_t as[4], bs[4];
+  };
+  auto read = [&](int64_t kt, Frag& f) {
+    const uint8_t* st = lsm + (kt % DS) * D_STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + fa[i][0]);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + fa[i][1]);
+      f.a[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      const u32x4 y0 = *reinterpret_cast<const u32x4*>(st + fb[i][0]);
+      const u32x4 y1 = *reinterpret_cast<const u32x4*>(st + fb[i][1]);
+      f.b[i] = i32x8{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3],
+                     (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
+      f.as[i] = *reinterpret_cast<const uint8_t*>(st + sa[i]);
+      f.bs[i] = *reinterpret_cast<const uint8_t*>(st + sbo[i]);
+    }
+    // Contraction elements past L are zero: MX block 1 of a last stage that
+    // holds 32 elements, and whole stages past the end (the loop runs an even
+    // number of stages). No branch: masks.
+    const int64_t rem = L - kt * DK;
+    const int keep0 = rem > 0 ? -1 : 0, keep1 = rem > 32 ? -1 : 0;
+    const int keeps = half ? keep1 : keep0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f.a[i][e] &= keep0;
+        f.b[i][e] &= keep0;
+        f.a[i][e + 4] &= keep1;
+        f.b[i][e + 4] &= keep1;
+      }
+      f.as[i] = keeps ? f.as[i] : 127;
+      f.bs[i] = keeps ? f.bs[i] : 127;
+    }
+  };
+  auto mfmas = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        // B (output-column operand) first: the lane then holds 4 consecutive columns
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.b[j], f.a[i], acc[i][j], 0 /*E4M3*/, 0 /*E4M3*/, 0, f.bs[j], 0, f.as[i]);
+  };
+
+  static_assert(D_DMA == 12 && DS == 4, "the wait counts assume 12 loads per stage, 4 stages");
+#pragma unroll
+  for (int p = 0; p < DS - 1; ++p) issue(p);
+  asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");     // stage 0 landed
+  Frag f0, f1;
+  read(0, f0);
+  for (int64_t kt = 0; kt < nk; kt += 2) {
+    // stage kt+1 has landed once only stage kt+2's loads are pending; every
+    // wavefront is past its reads of stage kt-1, whose buffer stage kt+3 reuses
+    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    issue(kt + DS - 1);
+    read(kt + 1, f1);
+    mfmas(f0);
+    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    issue(kt + DS);
+    read(kt + 2, f0);
+    mfmas(f1);                         // all zero past the end
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");      // ring drained, LDS free
+}
+
+// Epilogue through LDS: acc[i][j][4q+v] = C[row, col] with row = wm*128 + i*32
+// + lane%32 and col = wn*128 + j*32 + 8q + 4*(lane/32) + v. Each wavefront
+// stages 32-row blocks in LDS, then writes 16 bytes per lane along the rows.
+template <typename OutT, typename Store>
+__device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)[4][4],
+                                               int64_t rows_left, Store store) {
+  constexpr int ES = sizeof(OutT);
+  constexpr int RS = 128 * ES + 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, half = lane >> 5, r32 = lane & 31;
+  uint8_t* ep = lsm + wave * (32 * RS);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint8_t* d = ep + r32 * RS + (j * 32 + 8 * q + 4 * half) * ES;
+        if constexpr (ES == 2) {
+          const uint32_t lo = f32_to_bf16_rne(acc[i][j][4 * q]) | (f32_to_bf16_rne(acc[i][j][4 * q + 1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[i][j][4 * q + 2]) | (f32_to_bf16_rne(acc[i][j][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(d) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(d) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                      acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+      }
+    constexpr int PPR = 128 * ES / 16;               // 16-byte pieces per row
+#pragma unroll
+    for (int it = 0; it < 32 * PPR / 64; ++it) {
+      const int pc = it * 64 + lane, r = pc / PPR, c = pc % PPR;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(ep + r * RS + c * 16);
+      const int lr = wm * 128 + i * 32 + r;          // tile row
+      if (lr < rows_left) store(lr, c * 16 / ES, val);
+    }
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict__ dy,
+                                                      const uint8_t* __restrict__ dye,
+                                                      const uint8_t* __restrict__ w,
+                                                      const uint8_t* __restrict__ we,
+                                                      const int64_t* __restrict__ offsets, int G,
+                                                      int64_t N, int64_t K, void* __restrict__ dx) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
+  const int ntn = (int)(K / 256);
+  int g, nt;
+  int64_t row0, row_end;
+  {
+    int* pre = reinterpret_cast<int*>(lsm);
+    tile_prefix(G, [&](int e) { return (int)((offsets[e + 1] - offsets[e] + 255) / 256) * ntn; }, pre);
+    const int total = pre[G];
+    if ((int)blockIdx.x >= total) return;
+    const int t = (int)xcd_tile(blockIdx.x, total);
+    g = tile_group(pre, G, t);
+    const int loc = t - pre[g];
+    const int64_t a = offsets[g];
+    row_end = offsets[g + 1];
+    const int mt = (int)((row_end - a + 255) / 256);
+    // Within a group, tiles go in blocks of 4 n-tiles, m-tiles then n-tiles
+    // inside a block, so the ~32 consecutive tiles one XCD runs together
+    // share 8 A tiles and 4 B tiles in its L2.
+    int mi, ni;
+    block_order(loc, mt, ntn, mi, ni);
+    nt = ni;
+    row0 = a + (int64_t)mi * 256;
+    __syncthreads();
+  }
+  const int64_t k0 = (int64_t)nt * 256;
+  Operand A{dy, dye, N, 0, row0, row_end};
+  Operand B{w, we, (int64_t)G * N, (int64_t)g * N, k0, k0 + 256};
+  f32x16 acc[4][4];
+  zero<4>(acc);
+  mainloop_dma(lsm, A, B, N, acc);
+  const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * 128;
+  if constexpr (OUT_BF16)
+    store_tile_lds<uint16_t>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dx) + (row0 + lr) * K + col0 + col) = v;
+    });
+  else
+    store_tile_lds<float>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
+      *reinterpret_cast<u32x4*>(static_cast<float*>(dx) + (row0 + lr) * K + col0 + col) = v;
+    });
+}
+
+__global__ __launch_bounds__(256, 1) void k_wgrad_dma(const uint8_t* __restrict__ dyT,
+                                                      const uint8_t* __restrict__ dyTe,
+                                                      const uint8_t* __restrict__ xT,
+                                                      const uint8_t* __restrict__ xTe,
+                                                      const int64_t* __restrict__ padded, int G,
+                                                      int64_t P, int64_t N, int64_t K,
+                                                      float* __restrict__ dw) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
+  // groups longest first (a tile's cost is its group's token count)
+  const int64_t tn = N / 256, tk = K / 256, per = tn * tk;
+  const int64_t rank = blockIdx.x / per, rem = blockIdx.x % per;
+  int g = 0;
+  if (G > 1) {
+    int* seg = reinterpret_cast<int*>(lsm);
+    for (int h = threadIdx.x; h < G; h += 256) seg[h] = (int)(padded[h + 1] - padded[h]);
+    __syncthreads();
+    for (int h = threadIdx.x; h < G; h += 256) {
+      const int lh = seg[h];
+      int rk = 0;
+      for (int e = 0; e < G; ++e) {
+        const int le = seg[e];
+        rk += (le > lh) | ((le == lh) & (e < h));
+      }
+      if (rk == rank) seg[G] = h;
+    }
+    __syncthreads();
+    g = seg[G];
+    __syncthreads();
+  }
+  const int64_t n0 = (rem / tk) * 256, k0 = (rem % tk) * 256;
+  const int64_t c0 = padded[g];
+  const int64_t L = padded[g + 1] - c0;
+  Operand A{dyT, dyTe, P, c0, n0, n0 + 256};
+  Operand B{xT, xTe, P, c0, k0, k0 + 256};
+  f32x16 acc[4][4];
+  zero<4>(acc);
+  mainloop_dma(lsm, A, B, L, acc);
+  float* out = dw + (int64_t)g * N * K;
+  const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * 128;
+  store_tile_lds<float>(lsm, acc, 256, [&](int lr, int col, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(out + (n0 + lr) * K + col0 + col) = v;
+  });
+}
+
 template <int T>
 constexpr size_t lds_bytes() { return (size_t)2 * 2 * T * BK + (size_t)2 * 2 * T * SCB; }
 
@@ -429,8 +730,16 @@ hipError_t launch_dgrad(const uint8_t* dy, const uint8_t* dye, const uint8_t* w,
                         const uint8_t* we, const int64_t* offsets, int G, int64_t m_cap,
                         int64_t N, int64_t K, void* dx, bool dx_bf16, hipStream_t stream) {
   if (m_cap == 0 || G == 0) return hipSuccess;
-  if (K % 256 == 0 && m_cap >= 256 * (int64_t)G)
-    return dgrad_t<256>(dy, dye, w, we, offsets, G, m_cap, N, K, dx, dx_bf16, stream);
+  if (K % 256 == 0 && m_cap >= 256 * (int64_t)G && G <= 8192) {
+    static bool done[2] = {false, false};
+    auto k = dx_bf16 ? k_dgrad_dma<true> : k_dgrad_dma<false>;
+    const size_t lds = (size_t)DS * D_STAGE;
+    hipError_t e = set_lds(k, lds, done[dx_bf16]);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((m_cap + 255) / 256 + G) * (K / 256);   // bound on live tiles
+    k<<<(unsigned)tiles, 256, lds, stream>>>(dy, dye, w, we, offsets, G, N, K, dx);
+    return hipGetLastError();
+  }
   return dgrad_t<128>(dy, dye, w, we, offsets, G, m_cap, N, K, dx, dx_bf16, stream);
 }
 
@@ -438,8 +747,15 @@ hipError_t launch_wgrad(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* 
                         const uint8_t* xTe, const int64_t* padded, int G, int64_t P, int64_t N,
                         int64_t K, float* dw, hipStream_t stream) {
   if (G == 0) return hipSuccess;
-  if (N % 256 == 0 && K % 256 == 0)
-    return wgrad_t<256>(dyT, dyTe, xT, xTe, padded, G, P, N, K, dw, stream);
+  if (N % 256 == 0 && K % 256 == 0) {
+    static bool done = false;
+    const size_t lds = (size_t)DS * D_STAGE;
+    hipError_t e = set_lds(k_wgrad_dma, lds, done);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = (int64_t)G * (N / 256) * (K / 256);
+    k_wgrad_dma<<<(unsigned)tiles, 256, lds, stream>>>(dyT, dyTe, xT, xTe, padded, G, P, N, K, dw);
+    return hipGetLastError();
+  }
   return wgrad_t<128>(dyT, dyTe, xT, xTe, padded, G, P, N, K, dw, stream);
 }
 

@@ -374,8 +374,12 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     row_end = offsets[g + 1];
     const int64_t fm = (row_end - o0) / LT;
     if (e < G) {
-      nt = (int)(loc / fm);
-      row0 = o0 + (loc % fm) * LT;
+      // blocks of 4 n-tiles, m then n inside a block: the ~32 tiles an XCD
+      // runs together share 8 A tiles and 4 weight tiles in its L2
+      int mi, ni;
+      block_order(loc, (int)fm, ntn, mi, ni);
+      nt = ni;
+      row0 = o0 + (int64_t)mi * LT;
     } else {
       nt = loc;
       row0 = o0 + fm * LT;

@@ -117,38 +117,47 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
 }
 
 // max|x| over each group of `per` contiguous elements; blockIdx.y = group.
+// 1024-thread workgroups, about one per compute unit, each thread keeping
+// eight 16-byte loads in flight; one atomic max per workgroup (atomics on
+// one address serialize, so there are few of them).
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_group_amax(const void* __restrict__ x, int64_t per,
-                                                    uint32_t* __restrict__ amax_bits) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(1024) void k_group_amax(const void* __restrict__ x, int64_t per,
+                                                     uint32_t* __restrict__ amax_bits) {
+  __shared__ float red[16];
+  constexpr int U = 8;                                // loads in flight per thread
   const int64_t g = blockIdx.y;
-  const int64_t base = g * per;
+  const uint8_t* base = static_cast<const uint8_t*>(x) + g * per * (BF16 ? 2 : 4);
+  const int64_t nl = per / (BF16 ? 8 : 4);            // 16-byte pieces in the group
+  const int64_t stride = (int64_t)gridDim.x * 1024;
   float m = 0.0f;
-  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; e < per;
-       e += (int64_t)gridDim.x * 256 * 8) {
-    if constexpr (BF16) {
-      const uint4 a = ld_stream16(
-          reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base + e));
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  for (int64_t i0 = (int64_t)blockIdx.x * 1024 + threadIdx.x; i0 < nl; i0 += stride * U) {
+    uint4 a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u * stride;
+      a[u] = i < nl ? ld_stream16(reinterpret_cast<const uint4*>(base) + i) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t w[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        m = fmaxf(m, fabsf(u2f(w[j] << 16)));
-        m = fmaxf(m, fabsf(u2f(w[j] & 0xFFFF0000u)));
+        if constexpr (BF16) {
+          m = fmaxf(m, fabsf(u2f(w[j] << 16)));
+          m = fmaxf(m, fabsf(u2f(w[j] & 0xFFFF0000u)));
+        } else {
+          m = fmaxf(m, fabsf(u2f(w[j])));
+        }
       }
-    } else {
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + base + e);
-      const uint4 a = ld_stream16(p), b = ld_stream16(p + 1);
-      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(u2f(w[j])));
     }
   }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    atomicMax(amax_bits + g, f2u(m));  // non-negative floats order like their bits
+  if (threadIdx.x < 64) {
+    m = threadIdx.x < 16 ? red[threadIdx.x] : 0.0f;
+    m = wave_max(m);
+    if (threadIdx.x == 0) atomicMax(amax_bits + g, f2u(m));  // non-negative floats order like their bits
   }
 }
 
@@ -157,49 +166,58 @@ __global__ void k_outer_from_amax(float* __restrict__ outer, int64_t G) {
   if (g < G) outer[g] = __fdiv_rn(outer[g], 2688.0f);
 }
 
-// Row-wise MXFP8: 4 lanes per 32-element block, 8 elements per lane.
+// Row-wise MXFP8: 4 lanes per 32-element block, 8 elements per lane; each
+// thread handles U chunks per round, U * 64 chunks apart, loads issued first.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_mx_rowwise(const void* __restrict__ x, int64_t nchunks,
                                                     uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ e8) {
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < ((nchunks + 63) & ~63LL);
-       c += (int64_t)gridDim.x * 256) {
-    const bool ok = c < nchunks;  // 8 elements per chunk
-    float v[8];
-    if (ok) {
+  constexpr int U = 4;
+  const int64_t padded = (nchunks + 63) & ~63LL;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < padded; c0 += stride * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * stride;
+      const bool ok = c < nchunks;  // 8 elements per chunk
       if constexpr (BF16) {
-        const uint4 a = ld_stream16(
-            reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + c * 8));
+        const uint4 a = ok ? ld_stream16(reinterpret_cast<const uint4*>(
+                                 static_cast<const uint16_t*>(x) + c * 8))
+                           : make_uint4(0, 0, 0, 0);
         const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v[2 * j] = u2f(w[j] << 16);
-          v[2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+          v[u][2 * j] = u2f(w[j] << 16);
+          v[u][2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
         }
       } else {
         const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + c * 8);
-        const uint4 a = ld_stream16(p), b = ld_stream16(p + 1);
-        v[0] = u2f(a.x); v[1] = u2f(a.y); v[2] = u2f(a.z); v[3] = u2f(a.w);
-        v[4] = u2f(b.x); v[5] = u2f(b.y); v[6] = u2f(b.z); v[7] = u2f(b.w);
+        const uint4 a = ok ? ld_stream16(p) : make_uint4(0, 0, 0, 0);
+        const uint4 b = ok ? ld_stream16(p + 1) : make_uint4(0, 0, 0, 0);
+        v[u][0] = u2f(a.x); v[u][1] = u2f(a.y); v[u][2] = u2f(a.z); v[u][3] = u2f(a.w);
+        v[u][4] = u2f(b.x); v[u][5] = u2f(b.y); v[u][6] = u2f(b.z); v[u][7] = u2f(b.w);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-    float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
-    const int e = e8m0_ceil(m);
-    const float f = exp2_neg(e);
-    const uint32_t lo = e4m3x4_rne(__fmul_rn(v[0], f), __fmul_rn(v[1], f), __fmul_rn(v[2], f),
-                                   __fmul_rn(v[3], f));
-    const uint32_t hi = e4m3x4_rne(__fmul_rn(v[4], f), __fmul_rn(v[5], f), __fmul_rn(v[6], f),
-                                   __fmul_rn(v[7], f));
-    if (ok) {
-      *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(lo, hi);
-      if ((c & 3) == 0) e8[c >> 2] = (uint8_t)(e + 127);
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * stride;
+      if (c >= padded) break;                       // uniform per wavefront
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][j]));
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      const int e = e8m0_ceil(m);
+      const float f = exp2_neg(e);
+      const uint32_t lo = e4m3x4_rne(__fmul_rn(v[u][0], f), __fmul_rn(v[u][1], f),
+                                     __fmul_rn(v[u][2], f), __fmul_rn(v[u][3], f));
+      const uint32_t hi = e4m3x4_rne(__fmul_rn(v[u][4], f), __fmul_rn(v[u][5], f),
+                                     __fmul_rn(v[u][6], f), __fmul_rn(v[u][7], f));
+      if (c < nchunks) {
+        *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(lo, hi);
+        if ((c & 3) == 0) e8[c >> 2] = (uint8_t)(e + 127);
+      }
     }
   }
 }
@@ -233,9 +251,13 @@ static hipError_t quantize_impl(const void* x, int64_t rows, int64_t cols, bool 
     uint32_t* bits = reinterpret_cast<uint32_t*>(outer);
     k_fill_u32<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(bits, G, 0u);
     const int64_t per = rpg * cols;
-    int64_t gx = (per + 256 * 8 * 8 - 1) / (256 * 8 * 8);
-    gx = gx < 1 ? 1 : (gx > 1024 ? 1024 : gx);
-    k_group_amax<BF16><<<dim3((unsigned)gx, (unsigned)G), 256, 0, stream>>>(x, per, bits);
+    // about one 1024-thread workgroup per compute unit over all groups
+    const int64_t pieces = per / (BF16 ? 8 : 4);
+    int64_t gx = ((int64_t)device_cu_count() + G - 1) / G;
+    const int64_t most = (pieces + 1023) / 1024;
+    if (gx > most) gx = most;
+    gx = gx < 1 ? 1 : (gx > 65535 ? 65535 : gx);
+    k_group_amax<BF16><<<dim3((unsigned)gx, (unsigned)G), 1024, 0, stream>>>(x, per, bits);
     gamax = bits;
   }
   const unsigned grid = (unsigned)((rows + 3) / 4);
@@ -265,7 +287,7 @@ hipError_t launch_mxfp8_quantize_rowwise(const void* x, bool bf16, int64_t rows,
                                          uint8_t* q, uint8_t* e8, hipStream_t stream) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
-  int64_t grid = (nchunks + 255) / 256;
+  int64_t grid = (nchunks + 1023) / 1024;               // about one round of 4 chunks per thread
   const int64_t cap = (int64_t)device_cu_count() * 16;
   if (grid > cap) grid = cap;
   if (bf16)

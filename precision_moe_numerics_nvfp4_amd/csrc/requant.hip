@@ -117,16 +117,25 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
   } else {
     constexpr int EB = (S == Src::BF16) ? 2 : 4;        // bytes per element
     constexpr int V16 = TK * EB / 16;                   // 16-byte vectors per row
-    for (int i = tid; i < TP * V16; i += 256) {
+    constexpr int NV = TP * V16 / 256;                  // vectors per thread
+    // all of the thread's loads are issued before any is stored
+    uint4 a[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int i = tid + 256 * n;
       const int t = i / V16, c = i % V16;
       const int64_t r = row_of[t];
-      uint4 a = make_uint4(0, 0, 0, 0);
-      if (r >= 0)
-        a = ld_stream16(reinterpret_cast<const uint4*>(
-            static_cast<const uint8_t*>(src) + (r * cols + k0) * EB) + c);
+      a[n] = r >= 0 ? ld_stream16(reinterpret_cast<const uint4*>(
+                          static_cast<const uint8_t*>(src) + (r * cols + k0) * EB) + c)
+                    : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int i = tid + 256 * n;
+      const int t = i / V16, c = i % V16;
       uint32_t* d = reinterpret_cast<uint32_t*>(
           reinterpret_cast<uint8_t*>(&tile.v[t][0]) + c * 16);
-      d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+      d[0] = a[n].x; d[1] = a[n].y; d[2] = a[n].z; d[3] = a[n].w;
     }
   }
   __syncthreads();

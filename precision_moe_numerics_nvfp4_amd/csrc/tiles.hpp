@@ -113,4 +113,15 @@ __device__ inline int tile_group(const int* pre, int G, int t) {
   return lo;
 }
 
+// Tile loc of an mt x nt grid, ordered in blocks of 4 columns (n-tiles):
+// inside a block the n index runs fastest, then m; blocks follow each other.
+// A run of 32 consecutive tiles then covers 8 rows x 4 columns of the grid.
+__device__ inline void block_order(int loc, int mt, int nt, int& mi, int& ni) {
+  const int nb = loc / (mt * 4);                  // block of 4 columns
+  const int r = loc - nb * mt * 4;
+  const int w = nt - nb * 4 < 4 ? nt - nb * 4 : 4;  // columns in this block
+  mi = r / w;
+  ni = nb * 4 + r % w;
+}
+
 }  // namespace nvfp4moe

@@ -19,7 +19,7 @@ per token, 48 experts per GPU at 8-way expert parallelism):
 3. one GPU's expert share: 32768 tokens routed top-8 over 384 experts with
    Zipf(1.1) popularity, experts 144..191 local; X bf16 [32768, 4096],
    W1 [48, 1536, 4096], W2 [48, 4096, 1536] ~ N(0, 0.02^2); H bf16 [M, 1536].
-4. backward at the workload-2 shapes: dY bf16 [8192, 2048] ~ N(0, 1e-6).
+4. backward at the workload-2 shapes: dY bf16 [8192, 2048] ~ N(0, sd 1e-3).
 5. decode: 512 tokens top-8 uniform over 384, experts 144..191 local,
    d_model 4096, FFN 1536; streaming: X bf16 [262144, 2048] ~ N(0,1).
 """
