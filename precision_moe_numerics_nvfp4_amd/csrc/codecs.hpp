@@ -113,6 +113,33 @@ __device__ __forceinline__ uint32_t e4m3x4_sr(float y0, float y1, float y2, floa
   return (uint32_t)w;
 }
 
+// The same two conversions with the division by the block scale folded into
+// the instruction: `scale` is a float32 whose exponent field is the block's
+// E8M0 code c (mantissa zero), and the result equals converting x * 2^(127-c)
+// after an exact float32 multiply. Checked on gfx950 for every code from 0
+// (2^-127) to 247 (2^120), with x in the normal, subnormal and below-half-step
+// ranges of the scaled value, at grid points, at 0 and 448, both signs, and
+// with x itself a float32 subnormal.
+// Each random operand holds its 16-bit draw in the high half and zeros below,
+// as for e4m3x4_sr.
+__device__ __forceinline__ uint32_t e4m3x4_sr_scaled(float x0, float x1, float x2, float x3,
+                                                     uint32_t r0, uint32_t r1, uint32_t r2,
+                                                     uint32_t r3, float scale) {
+  int w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, x0, r0, scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, x1, r1, scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, x2, r2, scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, x3, r3, scale, 3);
+  return (uint32_t)w;
+}
+__device__ __forceinline__ uint32_t e4m3x4_rne_scaled(float x0, float x1, float x2, float x3,
+                                                      float scale) {
+  typedef short s16x2_t __attribute__((ext_vector_type(2)));
+  s16x2_t w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x0, x1, scale, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x2, x3, scale, true);
+  return (uint32_t)(uint16_t)w[0] | ((uint32_t)(uint16_t)w[1] << 16);
+}
+
 // ----------------------------------------------------------------- E8M0
 
 // Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 gives -127.
@@ -122,6 +149,17 @@ __device__ __forceinline__ int e8m0_ceil(float amax) {
   const int E = (int)(b >> 23) - 127;
   const int e = ((b & 0x7FFFFFu) <= 0x600000u) ? E - 8 : E - 7;   // m <= 1.75
   return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// The same exponent as an E8M0 code c = e + 127, from the bits of a
+// non-negative float32 amax: adding 0x1FFFFF carries into the exponent field
+// exactly when the mantissa exceeds 0.75 (amax > 1.75 * 2^E), so the field
+// becomes E + 127 + [m > 0.75] and c = field - 8 (E + 119 is 448 = 1.75 * 2^8
+// away). Zero and subnormal amax give a field of 0 or 1, clamped to c = 0.
+// Finite amax gives c <= 247.
+__device__ __forceinline__ uint32_t e8m0_code_bits(uint32_t amax_bits) {
+  const uint32_t t = (amax_bits + 0x1FFFFFu) >> 23;
+  return (t > 8u ? t : 8u) - 8u;
 }
 
 // 2^-e as float32 for e in [-127, 120] (always a normal number).
@@ -172,6 +210,15 @@ __device__ __forceinline__ Draws8 draws8(uint64_t q, uint64_t seed, uint32_t tag
 }
 
 // ----------------------------------------------------------------- misc
+
+// Maximum over the four lanes of a quad (lanes 4q .. 4q+3, all active), on
+// the bits of non-negative floats (their order is the integer order); two
+// DPP quad permutations, no LDS traffic.
+__device__ __forceinline__ uint32_t quad_max_bits(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));  // lane ^ 1
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));  // lane ^ 2
+  return m;
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

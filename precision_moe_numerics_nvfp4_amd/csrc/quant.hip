@@ -203,20 +203,16 @@ __global__ __launch_bounds__(256) void k_mx_rowwise(const void* __restrict__ x, 
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + u * stride;
       if (c >= padded) break;                       // uniform per wavefront
-      float m = 0.0f;
+      float mf = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][j]));
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
-      m = fmaxf(m, __shfl_xor(m, 2, 64));
-      const int e = e8m0_ceil(m);
-      const float f = exp2_neg(e);
-      const uint32_t lo = e4m3x4_rne(__fmul_rn(v[u][0], f), __fmul_rn(v[u][1], f),
-                                     __fmul_rn(v[u][2], f), __fmul_rn(v[u][3], f));
-      const uint32_t hi = e4m3x4_rne(__fmul_rn(v[u][4], f), __fmul_rn(v[u][5], f),
-                                     __fmul_rn(v[u][6], f), __fmul_rn(v[u][7], f));
+      for (int j = 0; j < 8; ++j) mf = fmaxf(mf, fabsf(v[u][j]));
+      const uint32_t code = e8m0_code_bits(quad_max_bits(f2u(mf)));   // E8M0 byte = e + 127
+      const float scale = u2f(code << 23);
+      const uint32_t lo = e4m3x4_rne_scaled(v[u][0], v[u][1], v[u][2], v[u][3], scale);
+      const uint32_t hi = e4m3x4_rne_scaled(v[u][4], v[u][5], v[u][6], v[u][7], scale);
       if (c < nchunks) {
         *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(lo, hi);
-        if ((c & 3) == 0) e8[c >> 2] = (uint8_t)(e + 127);
+        if ((c & 3) == 0) e8[c >> 2] = (uint8_t)code;
       }
     }
   }

@@ -17,12 +17,27 @@
 // staged in LDS in their stored form (4-bit codes + scales, or bf16/f32), so
 // HBM is read once, row-contiguously. Each thread then owns an 8-column x
 // 8-token micro-tile: it reads the 8 tokens' values of its 8 columns from LDS
-// (the transpose), four neighbouring threads cover one 32-token block and
-// reduce its maximum with two shuffles, and each thread writes 8 contiguous
-// output bytes per column (16 threads write one 128-byte output row segment).
-// The stochastic draws for those 8 bytes are exactly one Philox call, because
-// the draw index is the output's linear index and 8 consecutive indices share
-// one counter.
+// (the transpose), four neighbouring lanes cover one 32-token block and
+// reduce its maximum with two quad DPP exchanges, and each thread writes 8
+// contiguous output bytes per column (16 threads write one 128-byte output
+// row segment). The stochastic draws for those 8 bytes are exactly one Philox
+// call, because the draw index is the output's linear index and 8 consecutive
+// indices share one counter. The block scale's division is folded into the
+// scaled conversion instructions (exact; see codecs.hpp).
+//
+// LDS layout: tile row r (token) lives in slot 16 * (r & 7) + (r >> 3). A
+// thread's 8 tokens are rows 8 * pc + i, so for a fixed i the 16 lanes pc =
+// 0..15 of a wavefront read 16 consecutive slots; with a code pitch of 18
+// words those land on distinct LDS banks (18 * pc mod 32 is 16 distinct even
+// values), as do the per-slot scale and outer arrays.
+//
+// Workgroup order: the grid is one-dimensional over the live tiles (those
+// below the padded total read on the device). Consecutive workgroup indices go
+// to different XCDs, so each XCD is given a contiguous band of tiles, column
+// tile fastest: the workgroups that read the same input rows (and the same
+// 128-byte lines of codes and scales) run together on one XCD and share its
+// L2, and the E8M0 bytes of neighbouring token tiles are written close in
+// time.
 #include "codecs.hpp"
 #include "internal.hpp"
 
@@ -35,19 +50,21 @@ constexpr int TK = 128;  // columns per tile
 
 enum class Src { NVFP4, BF16, F32 };
 
+__device__ __forceinline__ int slot_of(int r) { return 16 * (r & 7) + (r >> 3); }
+
 template <Src S>
 struct Tile;
 
 template <>
 struct Tile<Src::NVFP4> {
-  static constexpr int CPITCH = TK / 2 + 4;  // code bytes per staged row (+pad)
-  uint8_t codes[TP][CPITCH];
-  uint8_t scales[TP][TK / 16];
+  static constexpr int CW = 18;              // code words per slot (16 used)
+  uint32_t codes[TP * CW];
+  uint32_t scales[TP][TK / 64];              // 8 E4M3 bytes per slot
   float outer[TP];
 };
 template <>
 struct Tile<Src::BF16> {
-  static constexpr int PITCH = TK + 8;       // bf16 elements per staged row (+pad)
+  static constexpr int PITCH = TK + 8;       // bf16 elements per slot (+pad)
   uint16_t v[TP][PITCH];
 };
 template <>
@@ -55,6 +72,12 @@ struct Tile<Src::F32> {
   static constexpr int PITCH = TK + 4;
   float v[TP][PITCH];
 };
+
+__device__ __forceinline__ int64_t xcd_band(int64_t w, int64_t live) {
+  const int64_t x = w & 7, s = w >> 3;
+  const int64_t q = live >> 3, r = live & 7;
+  return x * q + (x < r ? x : r) + s;
+}
 
 template <Src S, bool SR>
 __global__ __launch_bounds__(256) void k_transpose_mx(
@@ -66,15 +89,18 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
   __shared__ int64_t row_of[TP];  // source row of each tile token, -1 = padding
 
   const int tid = threadIdx.x;
-  const int64_t p0 = (int64_t)blockIdx.x * TP;
-  const int64_t k0 = (int64_t)blockIdx.y * TK;
-  const int64_t ptot = padded[G];
-  if (p0 >= ptot) return;  // uniform per workgroup
+  const int64_t n_ct = cols / TK;
+  const int64_t plim = min(padded[G], P);
+  const int64_t live = (plim + TP - 1) / TP * n_ct;
+  if ((int64_t)blockIdx.x >= live) return;  // uniform per workgroup
+  const int64_t t_idx = xcd_band(blockIdx.x, live);
+  const int64_t p0 = (t_idx / n_ct) * TP;
+  const int64_t k0 = (t_idx % n_ct) * TK;
 
   if (tid < TP) {
     const int64_t p = p0 + tid;
     int64_t r = -1;
-    if (p < ptot && p < P) {
+    if (p < plim) {
       int lo = 0, hi = G;  // last g with padded[g] <= p
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -99,9 +125,9 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
         a = ld_stream16(g);
         b = ld_stream16(g + 1);
       }
-      uint32_t* d = reinterpret_cast<uint32_t*>(&tile.codes[t][h * 32]);
-      d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
-      d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+      uint2* d = reinterpret_cast<uint2*>(&tile.codes[slot_of(t) * Tile<S>::CW + 8 * h]);
+      d[0] = make_uint2(a.x, a.y); d[1] = make_uint2(a.z, a.w);
+      d[2] = make_uint2(b.x, b.y); d[3] = make_uint2(b.z, b.w);
     }
     if (tid < TP) {
       const int64_t r = row_of[tid];
@@ -111,8 +137,10 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
         sc = *reinterpret_cast<const uint2*>(src_scales + r * (cols / 16) + k0 / 16);
         o = src_outer[rpg ? r / rpg : r];
       }
-      *reinterpret_cast<uint2*>(&tile.scales[tid][0]) = sc;
-      tile.outer[tid] = o;
+      const int sl = slot_of(tid);
+      tile.scales[sl][0] = sc.x;
+      tile.scales[sl][1] = sc.y;
+      tile.outer[sl] = o;
     }
   } else {
     constexpr int EB = (S == Src::BF16) ? 2 : 4;        // bytes per element
@@ -133,9 +161,8 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
     for (int n = 0; n < NV; ++n) {
       const int i = tid + 256 * n;
       const int t = i / V16, c = i % V16;
-      uint32_t* d = reinterpret_cast<uint32_t*>(
-          reinterpret_cast<uint8_t*>(&tile.v[t][0]) + c * 16);
-      d[0] = a[n].x; d[1] = a[n].y; d[2] = a[n].z; d[3] = a[n].w;
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&tile.v[slot_of(t)][0]) + c * 16) =
+          a[n];
     }
   }
   __syncthreads();
@@ -146,11 +173,13 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
   float v[8][8];             // [column][token]
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int t = 8 * pc + i;
+    const int sl = 16 * i + pc;            // slot of token 8*pc + i
     if constexpr (S == Src::NVFP4) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile.codes[t][4 * kc]);
-      const float Sb = e4m3_pos_to_f32(tile.scales[t][kc >> 1]);
-      const float o = tile.outer[t];
+      const uint32_t w = tile.codes[sl * Tile<S>::CW + kc];
+      // E4M3 scale of the 16-block holding these 8 columns (exact decode)
+      const uint32_t sb = reinterpret_cast<const uint8_t*>(tile.scales[sl])[kc >> 1];
+      const float Sb = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0);
+      const float o = tile.outer[sl];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float e0, e1;
@@ -159,7 +188,7 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
         v[2 * j + 1][i] = __fmul_rn(__fmul_rn(e1, Sb), o);
       }
     } else if constexpr (S == Src::BF16) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&tile.v[t][8 * kc]);
+      const uint4 a = *reinterpret_cast<const uint4*>(&tile.v[sl][8 * kc]);
       const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -167,43 +196,46 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
         v[2 * j + 1][i] = u2f(w[j] & 0xFFFF0000u);
       }
     } else {
-      const float4 a = *reinterpret_cast<const float4*>(&tile.v[t][8 * kc]);
-      const float4 b = *reinterpret_cast<const float4*>(&tile.v[t][8 * kc + 4]);
+      const float4 a = *reinterpret_cast<const float4*>(&tile.v[sl][8 * kc]);
+      const float4 b = *reinterpret_cast<const float4*>(&tile.v[sl][8 * kc + 4]);
       v[0][i] = a.x; v[1][i] = a.y; v[2][i] = a.z; v[3][i] = a.w;
       v[4][i] = b.x; v[5][i] = b.y; v[6][i] = b.z; v[7][i] = b.w;
     }
   }
 
   const int64_t p = p0 + 8 * pc;                 // first output column of this thread
-  const bool live = (p < ptot) && (p < P);        // whole 8-chunk shares liveness
+  const bool live_p = p < plim;                  // whole 8-chunk shares liveness
   const int64_t PB = P / 32;
+  const int64_t kt = k0 + 8 * kc;                // first output row of this thread
+  uint8_t* o8 = out + kt * P + p;
+  uint8_t* oe = out_e8 + kt * PB + (p >> 5);
+  uint64_t q = (uint64_t)kt * (uint64_t)(P >> 3) + (uint64_t)(p >> 3);   // Philox counter
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float m = 0.0f;
+    float mf = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
-    const int e = e8m0_ceil(m);
-    const float f = exp2_neg(e);
-    const int64_t k = k0 + 8 * kc + j;
-    uint32_t lo = 0, hi = 0;
+    for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[j][i]));
+    const uint32_t m = quad_max_bits(f2u(mf));
+    const uint32_t code = e8m0_code_bits(m);
+    const float scale = u2f(code << 23);         // 2^(code - 127)
+    uint32_t lo, hi;
     if constexpr (SR) {
-      const Draws8 u = draws8((uint64_t)(k * P + p) >> 3, seed, tag);
-      lo = e4m3x4_sr(__fmul_rn(v[j][0], f), __fmul_rn(v[j][1], f), __fmul_rn(v[j][2], f),
-                     __fmul_rn(v[j][3], f), u.get(0), u.get(1), u.get(2), u.get(3));
-      hi = e4m3x4_sr(__fmul_rn(v[j][4], f), __fmul_rn(v[j][5], f), __fmul_rn(v[j][6], f),
-                     __fmul_rn(v[j][7], f), u.get(4), u.get(5), u.get(6), u.get(7));
+      const Draws8 u = draws8(q, seed, tag);
+      lo = e4m3x4_sr_scaled(v[j][0], v[j][1], v[j][2], v[j][3], u.w[0] << 16,
+                            u.w[0] & 0xFFFF0000u, u.w[1] << 16, u.w[1] & 0xFFFF0000u, scale);
+      hi = e4m3x4_sr_scaled(v[j][4], v[j][5], v[j][6], v[j][7], u.w[2] << 16,
+                            u.w[2] & 0xFFFF0000u, u.w[3] << 16, u.w[3] & 0xFFFF0000u, scale);
     } else {
-      lo = e4m3x4_rne(__fmul_rn(v[j][0], f), __fmul_rn(v[j][1], f), __fmul_rn(v[j][2], f),
-                      __fmul_rn(v[j][3], f));
-      hi = e4m3x4_rne(__fmul_rn(v[j][4], f), __fmul_rn(v[j][5], f), __fmul_rn(v[j][6], f),
-                      __fmul_rn(v[j][7], f));
+      lo = e4m3x4_rne_scaled(v[j][0], v[j][1], v[j][2], v[j][3], scale);
+      hi = e4m3x4_rne_scaled(v[j][4], v[j][5], v[j][6], v[j][7], scale);
     }
-    if (live) {
-      *reinterpret_cast<uint2*>(out + k * P + p) = make_uint2(lo, hi);
-      if ((pc & 3) == 0) out_e8[k * PB + (p >> 5)] = (uint8_t)(e + 127);
+    if (live_p) {
+      *reinterpret_cast<uint2*>(o8) = make_uint2(lo, hi);
+      if ((pc & 3) == 0) *oe = (uint8_t)code;
     }
+    o8 += P;
+    oe += PB;
+    q += (uint64_t)(P >> 3);
   }
 }
 
@@ -213,9 +245,9 @@ hipError_t run(const void* src, const uint8_t* sc, const float* so, int64_t rpg,
                uint64_t seed, uint32_t tag, uint8_t* out, uint8_t* out_e8, hipStream_t stream) {
   (void)rows;
   if (P == 0 || cols == 0 || G == 0) return hipSuccess;
-  const dim3 grid((unsigned)((P + TP - 1) / TP), (unsigned)(cols / TK));
-  k_transpose_mx<S, SR><<<grid, 256, 0, stream>>>(src, sc, so, rpg, cols, offsets, padded, G, P,
-                                                  seed, tag, out, out_e8);
+  const int64_t grid = (P + TP - 1) / TP * (cols / TK);
+  k_transpose_mx<S, SR><<<(unsigned)grid, 256, 0, stream>>>(src, sc, so, rpg, cols, offsets, padded,
+                                                            G, P, seed, tag, out, out_e8);
   return hipGetLastError();
 }
 

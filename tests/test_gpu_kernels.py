@@ -139,10 +139,14 @@ def test_nvfp4_quantize_per_expert(nv, bf16, E, N, K):
 
 # ------------------------------------------------------------------ permute
 
-@pytest.mark.parametrize("case", ["uniform", "zipf", "one_expert", "none_local", "single", "empty"])
-def test_moe_permute(nv, case):
+# up to 16384 routed pairs take the one-launch form, more the three-launch one;
+# K = 96 and 160 copy the scale rows bytewise, K = 256 in 16-byte pieces
+@pytest.mark.parametrize("case,K", [("uniform", 256), ("zipf", 256), ("one_expert", 256),
+                                    ("none_local", 256), ("single", 256), ("empty", 256),
+                                    ("many_experts", 256), ("uniform", 160), ("zipf", 96),
+                                    ("zipf_many", 256)])
+def test_moe_permute(nv, case, K):
     import torch
-    K = 256
     if case == "uniform":
         topk, e0, nl = gen.route_uniform(201, 1000, 64, 8), 16, 8
     elif case == "zipf":
@@ -151,6 +155,10 @@ def test_moe_permute(nv, case):
         topk, e0, nl = np.full((700, 1), 5, np.int32), 0, 8
     elif case == "none_local":
         topk, e0, nl = gen.route_uniform(203, 50, 16, 2), 100, 4
+    elif case == "zipf_many":          # three-launch form with 1024 local experts
+        topk, e0, nl = gen.route_zipf(206, 2500, k=8, n_experts=2048), 512, 1024
+    elif case == "many_experts":       # the largest local expert count, 1024
+        topk, e0, nl = gen.route_uniform(205, 900, 1024, 4), 0, 1024
     elif case == "single":
         topk, e0, nl = np.zeros((64, 1), np.int32), 0, 1
     else:
@@ -196,6 +204,10 @@ def test_requant_sr_activations(nv, counts, cols):
     x = gen.normal(300 + cols, 0, (M, cols))
     gen.with_outliers(x, 300 + cols, 6, frac=0.01)
     x[min(3, M - 1)] = 0.0
+    if len(counts) > 2:
+        # a whole group of tiny rows: outer scales near the bottom of float32,
+        # so its 32-token blocks take E8M0 codes down to 0 (2^-127)
+        x[off[2]:off[3]] *= np.float32(1e-37)
     qc, qs, qo = Q.quantize(gen.to_bf16_bits(x))
     P = int(pad[-1]) + 64                                  # extra columns stay untouched
     seed, tag = 0x5EED0004, 0
@@ -247,11 +259,13 @@ def test_mxfp8_quantize_rowwise(nv, bf16, rows, cols):
 
 
 @pytest.mark.parametrize("bf16,counts,cols", [(True, [37, 0, 100, 5], 256), (False, [64, 65], 512),
-                                              (True, [1000], 128)])
+                                              (True, [1000], 128), (False, [40, 3, 70], 256)])
 def test_mxfp8_quantize_colwise(nv, bf16, counts, cols):
     off, pad = _groups_from_counts(counts)
     M = int(off[-1])
     x = gen.normal(600 + cols, 3, (M, cols), std=1e-3)
+    if len(counts) > 2:
+        x[off[2]:off[3]] *= np.float32(1e-36)   # blocks with E8M0 codes near 0, subnormal inputs
     a = gen.to_bf16_bits(x) if bf16 else x
     P = int(pad[-1])
     q, e = nv.mxfp8_quantize(to_dev(a), "colwise", to_dev(off), to_dev(pad), P)
