@@ -348,28 +348,32 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
 
   // Tiles: every group's full 256-row tiles first (group, n-tile, m-tile
-  // fastest), then every group's partial last m-tile; each part is split
-  // XCD-contiguously. The full tiles thus fill the first wave of workgroups
-  // and the cheaper partial ones (only their valid row blocks run MFMAs)
-  // come last.
+  // fastest), then the partial last m-tiles of more than 128 rows, then those
+  // of at most 128; each part is split XCD-contiguously. Workgroups are
+  // dispatched in index order, so when the tiles outnumber the compute units
+  // the ones left for a second round are the cheapest (a partial tile runs
+  // MFMAs only for its valid row blocks).
   const int ntn = (int)(N / LT);
   int g, nt;
   int64_t row0, row_end;
   {
-    int* pre = reinterpret_cast<int*>(lsm);            // [2G+1], before any stage load
-    tile_prefix(2 * G, [&](int e) {
-      const int gg = e < G ? e : e - G;
-      const int64_t m = offsets[gg + 1] - offsets[gg];
-      return (int)(e < G ? m / LT : (m % LT != 0 ? 1 : 0)) * ntn;
+    int* pre = reinterpret_cast<int*>(lsm);            // [3G+1], before any stage load
+    tile_prefix(3 * G, [&](int e) {
+      const int part = e / G, gg = e - part * G;
+      const int64_t m = offsets[gg + 1] - offsets[gg], rem = m % LT;
+      const int n = part == 0 ? (int)(m / LT)
+                  : part == 1 ? (rem > LT / 2 ? 1 : 0) : (rem != 0 && rem <= LT / 2 ? 1 : 0);
+      return n * ntn;
     }, pre);
-    const int nfull = pre[G], total = pre[2 * G];
+    const int nfull = pre[G], nbig = pre[2 * G], total = pre[3 * G];
     if ((int)blockIdx.x >= total) return;
     const int t = (int)blockIdx.x;
     const int tt = t < nfull ? (int)xcd_tile(t, nfull)
-                             : nfull + (int)xcd_tile(t - nfull, total - nfull);
-    const int e = tile_group(pre, 2 * G, tt);
+                 : t < nbig  ? nfull + (int)xcd_tile(t - nfull, nbig - nfull)
+                             : nbig + (int)xcd_tile(t - nbig, total - nbig);
+    const int e = tile_group(pre, 3 * G, tt);
     const int loc = tt - pre[e];
-    g = e < G ? e : e - G;
+    g = e % G;
     const int64_t o0 = offsets[g];
     row_end = offsets[g + 1];
     const int64_t fm = (row_end - o0) / LT;
@@ -428,30 +432,41 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     obs[j] = (uint32_t)(r * KSB + (lane & 1) * 4);
   }
   // Stage kt goes to LDS buffer kt % NS. A stage past the end (kt >= nk) is
-  // issued too, with offsets outside the buffer ranges: such loads return
-  // zeros without a memory access and keep the count of loads per stage, and
-  // so the wait counts, fixed.
-  auto issue = [&](int64_t kt, int64_t nk) {
+  // issued too, through buffer resources of size 0: such loads return zeros
+  // without a memory access and keep the count of loads per stage, and so the
+  // wait counts, fixed. Choosing the resource (scalar registers) rather than
+  // adding an offset keeps each load's address register untouched, so no
+  // load waits for its predecessor to have read a shared one.
+  const __amdgpu_buffer_rsrc_t rnull = __builtin_amdgcn_make_buffer_rsrc(
+      first_lane_ptr(bc), (short)0, 0, kBufWord3);
+  // part 0: the A tile's codes and scales, 1: the weight tile's, 2: both
+  auto issue = [&](int64_t kt, int64_t nk, int part) {
     uint8_t* st = lsm + (kt % NS) * kStageBytes;
     const bool real = kt < nk;
     const int64_t ks = real ? kt : 0;
     const int so = (int)(ks * LCB), ss = (int)(ks * LSB);
-    const uint32_t away = real ? 0u : 0x40000000u;
+    const __amdgpu_buffer_rsrc_t xac = real ? rac : rnull, xbc = real ? rbc : rnull;
+    const __amdgpu_buffer_rsrc_t xas = real ? ras : rnull, xbs = real ? rbs : rnull;
+    if (part != 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_void*)(st + (4 * i + wave) * 1024), 16,
-                                               oac[i] + away, so, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_void*)(st + LT * LCB + (4 * i + wave) * 1024),
-                                               16, obc[i] + away, so, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xac, (lds_void*)(st + (4 * i + wave) * 1024), 16,
+                                                 oac[i], so, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xas, (lds_void*)(st + 2 * LT * LCB + (4 * j + wave) * 256), 4, oas[j], ss, 0, 0);
     }
+    if (part != 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ras,
-                                               (lds_void*)(st + 2 * LT * LCB + (4 * j + wave) * 256),
-                                               4, oas[j] + away, ss, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rbs, (lds_void*)(st + 2 * LT * LCB + LT * LSB + (4 * j + wave) * 256), 4, obs[j] + away,
-          ss, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xbc, (lds_void*)(st + LT * LCB + (4 * i + wave) * 1024), 16, obc[i], so, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xbs, (lds_void*)(st + 2 * LT * LCB + LT * LSB + (4 * j + wave) * 256), 4, obs[j], ss, 0,
+            0);
     }
   };
   constexpr int kPerStage = 12;            // DMA instructions per stage and wavefront
@@ -544,9 +559,17 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   // One region: the MFMAs of step s interleaved with the conversions of the
   // next step; the scheduling barrier keeps other steps' conversions (and
   // their registers) out of it.
-  auto region = [&](const Frags& cur, Frags& nxt, int s_next) {
-    if constexpr (TA == 0) return;
+  // `extra` (DMA issues or LDS reads of later steps) runs at the start of the
+  // region, its NV buffer loads and ND LDS reads spread one per MFMA so that
+  // their issue overlaps the matrix cores' work.
+  auto region = [&](const Frags& cur, Frags& nxt, int s_next, auto&& extra, auto nv_c, auto nd_c) {
+    constexpr int NV = decltype(nv_c)::value, ND = decltype(nd_c)::value;
+    if constexpr (TA == 0) {
+      extra();
+      return;
+    }
     __builtin_amdgcn_sched_barrier(0);
+    extra();
     deq_step(s_next, nxt);
 #pragma unroll
     for (int i = 0; i < TA; ++i)
@@ -558,20 +581,28 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     for (int m = 0; m < TA * TN; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);    // 4 VALU
+      if constexpr (NV > 0)
+        if (m < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 buffer load
+      if constexpr (ND > 0)
+        if (m < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  auto none = [] {};
+  using Z = std::integral_constant<int, 0>;
 
-  // Pipeline. NS stages are in flight in LDS. Iteration kt reads chunk 1 of
-  // stage kt, runs steps 0-3; then (mid-stage) waits for stage kt+1's loads,
-  // synchronizes, reuses the buffer of stage kt (fully read by every
-  // wavefront) for stage kt+NS, and reads chunk 0 and the scales of stage
-  // kt+1; then runs steps 4-7, the last region converting step 0 of kt+1.
-  // LDS reads thus always overlap MFMAs, and there is one barrier per stage.
+  // Pipeline. NS stages are in flight in LDS. Iteration kt runs steps 0-3,
+  // reading chunk 1 of stage kt under the MFMAs of step 0; then (mid-stage)
+  // waits for stage kt+1's loads and synchronizes: every wavefront has read
+  // stage kt, whose buffer is reused for stage kt+NS. Steps 4-7 use chunk 1
+  // and the upper scale halves only; under their MFMAs go the DMA issues of
+  // stage kt+NS (steps 4 and 5) and the reads of chunk 0 and the scales of
+  // stage kt+1 (step 6); the lower scale halves are converted before the last
+  // region, which converts step 0 of kt+1. One barrier per stage.
   static_assert(kPerStage == 12, "wait counts assume 12 loads per stage and wavefront");
   static_assert(NS == 3, "wait counts assume 3 stages in flight");
 #pragma unroll
-  for (int p = 0; p < NS; ++p) issue(p, nk);
+  for (int p = 0; p < NS; ++p) issue(p, nk, 2);
   asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");   // stage 0 landed
   read_chunk(lsm, 0, c0a, c0b);
   read_scales(lsm);
@@ -581,27 +612,22 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
 
   for (int64_t kt = 0; kt < nk; ++kt) {
     const uint8_t* st = lsm + (kt % NS) * kStageBytes;
-    read_chunk(st, 1, c1a, c1b);
+    const uint8_t* sn = lsm + ((kt + 1) % NS) * kStageBytes;
     cvt_scales(1);
-    region(f0, f1, 1);
-    region(f1, f0, 2);
-    region(f0, f1, 3);
-    region(f1, f0, 4);
-    {
-      // Every wavefront has finished reading stage kt, and stage kt+1 has
-      // landed once only stage kt+2's loads are pending. Branch-free: after
-      // the last stage this reads data that is never used.
-      asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      issue(kt + NS, nk);
-      const uint8_t* sn = lsm + ((kt + 1) % NS) * kStageBytes;
-      read_chunk(sn, 0, c0a, c0b);
-      read_scales(sn);
-      cvt_scales(0);
-    }
-    region(f0, f1, 5);
-    region(f1, f0, 6);
-    region(f0, f1, 7);
-    region(f1, f0, 0);       // step 0 of stage kt+1 (unused after the last stage)
+    region(f0, f1, 1, [&] { read_chunk(st, 1, c1a, c1b); }, Z{}, std::integral_constant<int, TA + TN>{});
+    region(f1, f0, 2, none, Z{}, Z{});
+    region(f0, f1, 3, none, Z{}, Z{});
+    region(f1, f0, 4, none, Z{}, Z{});
+    // Every wavefront has finished reading stage kt, and stage kt+1 has
+    // landed once only stage kt+2's loads are pending. Branch-free: after the
+    // last stage the reads below fetch data that is never used.
+    asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    region(f0, f1, 5, [&] { issue(kt + NS, nk, 0); }, std::integral_constant<int, 6>{}, Z{});
+    region(f1, f0, 6, [&] { issue(kt + NS, nk, 1); }, std::integral_constant<int, 6>{}, Z{});
+    region(f0, f1, 7, [&] { read_chunk(sn, 0, c0a, c0b); read_scales(sn); }, Z{},
+           std::integral_constant<int, 2 * (TA + TN)>{});
+    cvt_scales(0);
+    region(f1, f0, 0, none, Z{}, Z{});   // step 0 of stage kt+1 (unused after the last stage)
   }
   };
   {

@@ -338,6 +338,44 @@ def test_fwd_grouped_gemm(nv, T, K, N, E, k):
     assert np.all(np.abs(gb - ref) <= ulp * 1.0000001)
 
 
+def _fwd_counts_case(seed, counts, K, N):
+    """Expert groups of the given row counts (routed rows already grouped)."""
+    M, E = int(sum(counts)), len(counts)
+    xc, xs, xo = Q.quantize(gen.to_bf16_bits(gen.normal(seed, 0, (max(M, 1), K))))
+    wc, ws, wo = Q.quantize(gen.to_bf16_bits(gen.normal(seed, 1, (E * N, K), std=0.02)),
+                            rows_per_group=N)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return xc[:M], xs[:M], xo[:M], wc, ws, wo, off
+
+
+# Groups whose row count is just past a multiple of 256: tails of at most 32
+# rows (5, 32, 31, and a whole group of 20) run in the weight-streaming kernel
+# when K % 512 == 0, tails of 33 and 44 rows as partial 256-row tiles; with
+# K = 384 every tail is a partial tile.
+@pytest.mark.parametrize("counts,K,N", [([261, 544, 33, 20, 256, 0, 300, 287], 1024, 512),
+                                        ([261, 544, 33, 20, 256, 0, 300, 287], 384, 256),
+                                        ([257, 288, 300], 1536, 256)])
+def test_fwd_grouped_gemm_tails(nv, counts, K, N):
+    import torch
+    ac, asc, ao, wc, ws, wo, off = _fwd_counts_case(800 + K, counts, K, N)
+    M = int(off[-1])
+    cap = M + 8                                               # rows past M stay untouched
+    dac = torch.zeros((cap, K // 2), dtype=torch.uint8, device="cuda")
+    dac[:M] = to_dev(ac)
+    das = torch.zeros((cap, K // 16), dtype=torch.uint8, device="cuda")
+    das[:M] = to_dev(asc)
+    dao = torch.zeros((cap,), dtype=torch.float32, device="cuda")
+    dao[:M] = to_dev(ao)
+    y = torch.full((cap, N), float("nan"), dtype=torch.float32, device="cuda")
+    nv.moe_fwd_grouped_gemm(dac, das, dao, to_dev(wc), to_dev(ws), to_dev(wo), to_dev(off), y=y)
+    _sync()
+    got = from_dev(y)
+    assert np.all(np.isnan(got[M:]))
+    ref = GM.fwd_grouped(ac, asc, ao, wc, ws, wo, off, N, accum="fp64")
+    groups = [(off[g], off[g + 1]) for g in range(len(counts))]
+    assert_gemm_close(got[:M], ref, groups, _fwd_bound(ac, asc, ao, wc, ws, wo, off, N, K), what="fwd")
+
+
 def test_fwd_grouped_gemm_exact_case(nv):
     ac, asc, ao, wc, ws, wo, off = _fwd_case(731, 200, 256, 256, 3, 2, exact=True)
     y = nv.moe_fwd_grouped_gemm(to_dev(ac), to_dev(asc), to_dev(ao), to_dev(wc), to_dev(ws),
