@@ -221,6 +221,45 @@ def _time(torch, fn, reps):
     return graph_time(torch, fn, reps)
 
 
+def mxfp8_forward_compare(torch, reps):
+    import precision_moe_numerics_nvfp4_amd as nv
+    from workloads import gen
+    w = gen.small_moe()
+    T, K, N, E, k = w["T"], w["K"], w["N"], w["E"], w["k"]
+    x, wt = dev_tensor(w["x"], torch), dev_tensor(w["w"], torch)
+    topk = dev_tensor(w["topk"], torch)
+    xq = nv.nvfp4_quantize(x)
+    wq = nv.nvfp4_quantize(wt, rows_per_group=N)
+    perm = nv.moe_permute(topk, 0, E, *xq)
+    x8 = nv.mxfp8_quantize(x, "rowwise")
+    w8 = nv.mxfp8_quantize(wt, "rowwise")
+    g8 = nv.mxfp8_gather_rows(perm["row_token"], perm["offsets"], *x8)
+    y = torch.empty((T * k, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    M = int(perm["offsets"][-1].item())
+    t_nv = _time(torch, lambda: nv.moe_fwd_grouped_gemm(perm["codes"], perm["scales"], perm["outer"],
+                                                        *wq, perm["offsets"], y=y), reps)
+    t_mx = _time(torch, lambda: nv.moe_fwd_grouped_gemm_mxfp8(*g8, *w8, perm["offsets"], y=y), reps)
+    t_nv_path = _time(torch, lambda: (nv.nvfp4_quantize(x, None, *xq),
+                                      nv.moe_permute(topk, 0, E, *xq, out=perm),
+                                      nv.moe_fwd_grouped_gemm(perm["codes"], perm["scales"],
+                                                              perm["outer"], *wq, perm["offsets"],
+                                                              y=y)), reps)
+    t_mx_path = _time(torch, lambda: (nv.mxfp8_quantize(x, "rowwise", out=x8[0], out_e8=x8[1]),
+                                      nv.mxfp8_gather_rows(perm["row_token"], perm["offsets"], *x8,
+                                                           out=g8),
+                                      nv.moe_fwd_grouped_gemm_mxfp8(*g8, *w8, perm["offsets"], y=y)),
+                      reps)
+    fl = 2.0 * M * N * K
+    return {"routed_rows": M,
+            "gemm_nvfp4": {"ms": round(t_nv, 4), "TFLOP/s": round(fl / t_nv / 1e9, 1)},
+            "gemm_mxfp8": {"ms": round(t_mx, 4), "TFLOP/s": round(fl / t_mx / 1e9, 1),
+                           "frac_fp8_peak": round(fl / t_mx / 1e-3 / PEAK["fp8"], 4)},
+            "forward_nvfp4_quantize_permute_gemm": {"ms": round(t_nv_path, 4)},
+            "forward_mxfp8_quantize_gather_gemm": {"ms": round(t_mx_path, 4)},
+            "note": "weights quantized once outside the timed paths"}
+
+
 def extras(torch, reps=10):
     import precision_moe_numerics_nvfp4_amd as nv
     from workloads import gen
@@ -283,6 +322,11 @@ def extras(torch, reps=10):
                          "weight_GB/s": round(wbytes / td / 1e6, 1),
                          "frac_hbm": round(wbytes / td / 1e-3 / PEAK["hbm"], 4)}
     del w1q, w2q5, hq5, yd1, yd2, perm5, xq5, x5
+    torch.cuda.empty_cache()
+    # the all-MXFP8 forward (the reference the NVFP4 forward is compared against)
+    # on the small MoE layer: MXFP8 quantize of X and W (row-wise, RNE), the row
+    # gather in expert order, the grouped GEMM; next to the NVFP4 forward's
+    out["mxfp8_forward_small_moe"] = mxfp8_forward_compare(torch, reps)
     torch.cuda.empty_cache()
     # streaming: 1 GiB bf16 [262144 x 2048] per-token quantize, then requant of its transpose
     rows, cols = 262144, 2048

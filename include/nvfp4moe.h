@@ -209,6 +209,44 @@ NVFP4MOE_API int moe_bwd_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0,
                   void* dx, int dx_dtype, void* stream);
 
 /*
+ * All-MXFP8 forward grouped GEMM: the reference the NVFP4 forward is measured
+ * against, and the precision of the last expert layers.
+ * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), TL;DR
+ * (wall-clock savings reported against full MXFP8 training) and section
+ * "Expert precision and convolution caches" (expert layers 40-47 kept in
+ * MXFP8).
+ *
+ * x: MXFP8 [m_cap, K] (E4M3 elements, E8M0 scales [m_cap, K/32], blocks along
+ * K), rows grouped by expert as moe_permute orders them; w: MXFP8 weights
+ * stored [G, N, K] (scales [G, N, K/32]); offsets[G+1] (device).
+ * y[r, n] = sum_k x[r, k] * w[g, n, k] for rows r of group g, exact products,
+ * float32 accumulation; y [m_cap, N] float32 or bfloat16 (round to nearest
+ * even); rows >= offsets[G] untouched.
+ * Requires N % 128 == 0, K % 128 == 0, K <= 16711935, x, w, y 16-byte aligned;
+ * otherwise NVFP4MOE_EUNSUPPORTED.
+ */
+NVFP4MOE_API int moe_fwd_grouped_gemm_mxfp8(const uint8_t* x_e4m3, const uint8_t* x_e8m0,
+                               const uint8_t* w_e4m3, const uint8_t* w_e8m0,
+                               const int64_t* offsets, int G, int64_t m_cap, int64_t N, int64_t K,
+                               void* y, int y_dtype, void* stream);
+
+/*
+ * Gather of MXFP8 rows into expert order (the MXFP8 counterpart of
+ * moe_permute's row copy).
+ * Pages: as moe_permute.
+ *
+ * row_token[r] and offsets[G+1] as written by moe_permute (device); src: MXFP8
+ * [src_rows, K] (+ scales [src_rows, K/32]); dst row r (r < offsets[G]) gets
+ * src row row_token[r]; dst [m_cap, K] (+ [m_cap, K/32]); rows >= offsets[G]
+ * untouched; row indices outside [0, src_rows) are skipped.
+ * Requires K % 32 == 0, src and dst elements 16-byte aligned.
+ */
+NVFP4MOE_API int mxfp8_gather_rows(const int32_t* row_token, const int64_t* offsets, int G,
+                      int64_t m_cap, const uint8_t* src_e4m3, const uint8_t* src_e8m0,
+                      int64_t src_rows, int64_t K, uint8_t* dst_e4m3, uint8_t* dst_e8m0,
+                      void* stream);
+
+/*
  * MXFP8 wgrad grouped GEMM (contraction over the tokens of each expert).
  * Pages: as moe_bwd_dgrad.
  *

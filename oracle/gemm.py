@@ -19,6 +19,11 @@ Shapes (M = routed rows, G = groups/experts, row-major):
             dY8 MXFP8 [M, N] (blocks along n), W8 MXFP8 [K, G*N]
 * wgrad:    dW[g, n, k] = sum_p dYT8[n, p] * XT8[k, p] over p in group g's
             padded column segment; dYT8 [N, P], XT8 [K, P]
+* forward, all MXFP8 (the full-MXFP8 reference the NVFP4 forward is compared
+  against: page 2, TL;DR and section "Expert precision and convolution
+  caches"):
+            Y[r, n]     = sum_k X8[r, k] * W8[g, n, k]
+            X8 MXFP8 [M, K] (blocks along k), W8 MXFP8 stored [G, N, K]
 Rows r of group g are offsets[g] <= r < offsets[g+1].
 """
 
@@ -72,6 +77,25 @@ def dgrad_grouped(dy_e4m3, dy_e8m0, w_e4m3, w_e8m0, offsets, N, accum="fp32"):
         if b == a:
             continue
         out[a:b] = _mm(dY[a:b], W[:, g * N:(g + 1) * N].T, accum)
+    return out
+
+
+def fwd_grouped_mxfp8(x_e4m3, x_e8m0, w_e4m3, w_e8m0, offsets, N, accum="fp32"):
+    """All-MXFP8 forward grouped GEMM -> [M, N]; weights [G*N, K] or [G, N, K]."""
+    X = MX.dequantize(x_e4m3, x_e8m0)             # [M, K]
+    K = X.shape[1]
+    off = np.asarray(offsets, dtype=np.int64)
+    G = off.shape[0] - 1
+    W = MX.dequantize(np.asarray(w_e4m3).reshape(G * N, K),
+                      np.asarray(w_e8m0).reshape(G * N, K // 32)).reshape(G, N, K)
+    M = int(off[-1])
+    dt = np.float64 if accum == "fp64" else np.float32
+    out = np.zeros((M, N), dtype=dt)
+    for g in range(G):
+        a, b = int(off[g]), int(off[g + 1])
+        if b == a:
+            continue
+        out[a:b] = _mm(X[a:b], W[g].T, accum)
     return out
 
 

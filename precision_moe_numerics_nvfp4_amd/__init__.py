@@ -18,7 +18,9 @@ from .binding import (  # noqa: F401
     moe_bwd_dgrad,
     moe_bwd_wgrad,
     moe_fwd_grouped_gemm,
+    moe_fwd_grouped_gemm_mxfp8,
     moe_permute,
+    mxfp8_gather_rows,
     mxfp8_quantize,
     mxfp8_requant_sr,
     nvfp4_quantize,

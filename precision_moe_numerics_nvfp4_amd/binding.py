@@ -38,6 +38,9 @@ SIGNATURES = {
     "moe_bwd_dgrad": ([_p, _p, _p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p, _c_int, _p],
                       _c_int),
     "moe_bwd_wgrad": ([_p, _p, _p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p, _p], _c_int),
+    "moe_fwd_grouped_gemm_mxfp8": ([_p, _p, _p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p,
+                                    _c_int, _p], _c_int),
+    "mxfp8_gather_rows": ([_p, _p, _c_int, _c_i64, _p, _p, _c_i64, _c_i64, _p, _p, _p], _c_int),
 }
 
 _LIB = None
@@ -307,3 +310,47 @@ def moe_bwd_wgrad(dyT_e4m3, dyT_e8m0, xT_e4m3, xT_e8m0, padded_offsets, N, K, dw
                              _stream(dyT_e4m3))
     _check("moe_bwd_wgrad", st)
     return dw
+
+
+def moe_fwd_grouped_gemm_mxfp8(x_e4m3, x_e8m0, w_e4m3, w_e8m0, offsets, out_dtype=None, y=None):
+    """y [m_cap, N] from X8 [m_cap, K] and weights W8 [G*N, K] or [G, N, K] (MXFP8)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    _dev(x_e4m3, "x_e4m3", torch.uint8, 2)
+    _dev(x_e8m0, "x_e8m0", torch.uint8, 2)
+    _dev(w_e4m3, "w_e4m3", torch.uint8)
+    _dev(w_e8m0, "w_e8m0", torch.uint8)
+    _dev(offsets, "offsets", torch.int64, 1)
+    m_cap, K = x_e4m3.shape
+    G = offsets.shape[0] - 1
+    N = (w_e4m3.numel() // K) // G if G else 0
+    if w_e4m3.numel() != G * N * K or w_e8m0.numel() != G * N * (K // 32):
+        raise ValueError("weights must hold G*N rows of K elements (and K/32 scales)")
+    if y is None:
+        y = torch.empty((m_cap, N), dtype=out_dtype, device=x_e4m3.device)
+    st = lib().moe_fwd_grouped_gemm_mxfp8(_ptr(x_e4m3), _ptr(x_e8m0), _ptr(w_e4m3), _ptr(w_e8m0),
+                                          _ptr(offsets), G, m_cap, N, K, _ptr(y),
+                                          _out_dtype(y.dtype), _stream(x_e4m3))
+    _check("moe_fwd_grouped_gemm_mxfp8", st)
+    return y
+
+
+def mxfp8_gather_rows(row_token, offsets, src_e4m3, src_e8m0, m_cap=None, out=None):
+    """Rows of MXFP8 src [T, K] (+ [T, K/32]) in expert order: row r < offsets[-1]
+    is src row row_token[r]. Returns (dst_e4m3 [m_cap, K], dst_e8m0 [m_cap, K/32])."""
+    torch = _torch()
+    _dev(row_token, "row_token", torch.int32, 1)
+    _dev(offsets, "offsets", torch.int64, 1)
+    _dev(src_e4m3, "src_e4m3", torch.uint8, 2)
+    _dev(src_e8m0, "src_e8m0", torch.uint8, 2)
+    T, K = src_e4m3.shape
+    m_cap = row_token.shape[0] if m_cap is None else int(m_cap)
+    if out is None:
+        out = (torch.empty((m_cap, K), dtype=torch.uint8, device=src_e4m3.device),
+               torch.empty((m_cap, K // 32), dtype=torch.uint8, device=src_e4m3.device))
+    G = offsets.shape[0] - 1
+    st = lib().mxfp8_gather_rows(_ptr(row_token), _ptr(offsets), G, m_cap, _ptr(src_e4m3),
+                                 _ptr(src_e8m0), T, K, _ptr(out[0]), _ptr(out[1]),
+                                 _stream(src_e4m3))
+    _check("mxfp8_gather_rows", st)
+    return out

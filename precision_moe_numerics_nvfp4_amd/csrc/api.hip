@@ -181,4 +181,31 @@ int moe_bwd_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0, const uint8_
                                  dw, as_stream(stream)));
 }
 
+int moe_fwd_grouped_gemm_mxfp8(const uint8_t* x_e4m3, const uint8_t* x_e8m0,
+                               const uint8_t* w_e4m3, const uint8_t* w_e8m0,
+                               const int64_t* offsets, int G, int64_t m_cap, int64_t N, int64_t K,
+                               void* y, int y_dtype, void* stream) {
+  REQUIRE(G >= 0 && m_cap >= 0 && N >= 0 && K >= 0, NVFP4MOE_EINVAL);
+  REQUIRE(y_dtype == NVFP4MOE_F32 || y_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (G == 0 || m_cap == 0 || N == 0) return NVFP4MOE_OK;
+  REQUIRE(x_e4m3 && x_e8m0 && w_e4m3 && w_e8m0 && offsets && y, NVFP4MOE_EINVAL);
+  REQUIRE(N % 128 == 0 && K % 128 == 0 && K > 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(K <= kMaxGemmRowBytes, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(x_e4m3) && aligned16(w_e4m3) && aligned16(y), NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_fwd_mxfp8(x_e4m3, x_e8m0, w_e4m3, w_e8m0, offsets, G, m_cap, N, K, y,
+                                     y_dtype == NVFP4MOE_BF16, as_stream(stream)));
+}
+
+int mxfp8_gather_rows(const int32_t* row_token, const int64_t* offsets, int G, int64_t m_cap,
+                      const uint8_t* src_e4m3, const uint8_t* src_e8m0, int64_t src_rows,
+                      int64_t K, uint8_t* dst_e4m3, uint8_t* dst_e8m0, void* stream) {
+  REQUIRE(G >= 0 && m_cap >= 0 && src_rows >= 0 && K >= 0, NVFP4MOE_EINVAL);
+  if (G == 0 || m_cap == 0) return NVFP4MOE_OK;
+  REQUIRE(row_token && offsets && src_e4m3 && src_e8m0 && dst_e4m3 && dst_e8m0, NVFP4MOE_EINVAL);
+  REQUIRE(K % 32 == 0 && K > 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(src_e4m3) && aligned16(dst_e4m3), NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_gather_rows(row_token, offsets, G, m_cap, src_rows, src_e4m3, src_e8m0,
+                                       K, K / 32, dst_e4m3, dst_e8m0, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -14,6 +14,10 @@
 // transpose is for), so one main loop serves both:
 //   dgrad: dX[r, k]    = sum_n dY8[r, n] * W8[k, g*N + n]    (rows r of expert g)
 //   wgrad: dW[g, n, k] = sum_p dYT8[n, p] * XT8[k, p]        (p in g's padded segment)
+// The dgrad kernels take the second operand's layout as parameters (row
+// stride, and per group a contraction offset and a row offset), which also
+// covers the all-MXFP8 forward GEMM:
+//   fwd:   Y[r, n]     = sum_k X8[r, k] * W8[g*N + n, k]     (weights stored [G, N, K])
 //
 // Structure. A workgroup of 4 wavefronts owns a 256 x 256 output tile; each
 // wavefront owns 128 x 128 (4 x 4 MFMA tiles, 256 accumulator registers).
@@ -106,7 +110,8 @@ __device__ __forceinline__ void mainloop(uint8_t* smem, const Operand& A, const 
 #pragma unroll
   for (int o = 0; o < 2; ++o) {
     const Operand& X = o ? B : A;
-    const int64_t nrow = X.row_end - X.row0;
+    // the tile's rows only: a group may be longer, and the range must stay 32-bit
+    const int64_t nrow = X.row_end - X.row0 < T ? X.row_end - X.row0 : T;
     rq[o] = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X.q + X.row0 * X.ld), (short)0,
                                               uniform_u32(nrow * X.ld), kBufferWord3);
     re[o] = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X.e + X.row0 * (X.ld / 32)), (short)0,
@@ -284,15 +289,23 @@ __device__ __forceinline__ bool dgrad_tile(const int64_t* __restrict__ offsets, 
   return false;
 }
 
+// Second operand of the grouped row x row GEMM: group g's rows are
+// row_step * g + (output column), its contraction starts at c0_step * g.
+struct BLayout {
+  int64_t ld, c0_step, row_step;
+};
+
 template <int T, bool OUT_BF16>
 __global__ __launch_bounds__(256, 1) void k_dgrad(const uint8_t* __restrict__ dy,
                                                   const uint8_t* __restrict__ dye,
                                                   const uint8_t* __restrict__ w,
                                                   const uint8_t* __restrict__ we,
                                                   const int64_t* __restrict__ offsets, int G,
-                                                  int64_t N, int64_t K, void* __restrict__ dx) {
+                                                  int64_t L, int64_t ncols, BLayout bl,
+                                                  void* __restrict__ dx) {
   constexpr int BM = T, BN = T, TM = T / 64, TN = T / 64;
   extern __shared__ uint8_t smem[];
+  const int64_t N = L, K = ncols;                 // contraction, output columns
   const int64_t ntn = K / BN;
   int64_t live = 0;
   for (int e = 0; e < G; ++e) live += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
@@ -303,7 +316,8 @@ __global__ __launch_bounds__(256, 1) void k_dgrad(const uint8_t* __restrict__ dy
   dgrad_tile(offsets, G, xcd_tile(blockIdx.x, live), ntn, BM, g, row0, row_end, nt);
   const int64_t k0 = nt * BN;
   Operand A{dy, dye, N, 0, row0, row_end};
-  Operand B{w, we, (int64_t)G * N, (int64_t)g * N, k0, k0 + BN};
+  const int64_t br0 = (int64_t)g * bl.row_step + k0;
+  Operand B{w, we, bl.ld, (int64_t)g * bl.c0_step, br0, br0 + BN};
   f32x16 acc[TM][TN];
   zero<TM>(acc);
   mainloop<T>(smem, A, B, N, acc);
@@ -424,8 +438,8 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* lsm, const Operand& A, con
 #pragma unroll
   for (int o = 0; o < 2; ++o) {
     const Operand& X = o ? B : A;
-    const int64_t n = X.row_end - X.row0;
-    nrow[o] = __builtin_amdgcn_readfirstlane((int)(n < 256 ? n : 256));
+    const int64_t n = X.row_end - X.row0 < 256 ? X.row_end - X.row0 : 256;   // the tile's rows
+    nrow[o] = __builtin_amdgcn_readfirstlane((int)n);
     ld[o] = X.ld;
     c0[o] = X.c0;
     rq[o] = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X.q + X.row0 * X.ld), (short)0,
@@ -600,8 +614,10 @@ __global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict_
                                                       const uint8_t* __restrict__ w,
                                                       const uint8_t* __restrict__ we,
                                                       const int64_t* __restrict__ offsets, int G,
-                                                      int64_t N, int64_t K, void* __restrict__ dx) {
+                                                      int64_t L, int64_t ncols, BLayout bl,
+                                                      void* __restrict__ dx) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
+  const int64_t N = L, K = ncols;                 // contraction, output columns
   const int ntn = (int)(K / 256);
   int g, nt;
   int64_t row0, row_end;
@@ -627,7 +643,8 @@ __global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict_
   }
   const int64_t k0 = (int64_t)nt * 256;
   Operand A{dy, dye, N, 0, row0, row_end};
-  Operand B{w, we, (int64_t)G * N, (int64_t)g * N, k0, k0 + 256};
+  const int64_t br0 = (int64_t)g * bl.row_step + k0;
+  Operand B{w, we, bl.ld, (int64_t)g * bl.c0_step, br0, br0 + 256};
   f32x16 acc[4][4];
   zero<4>(acc);
   mainloop_dma(lsm, A, B, N, acc);
@@ -700,15 +717,36 @@ hipError_t set_lds(Kern k, size_t bytes, bool& done) {
 
 template <int T>
 hipError_t dgrad_t(const uint8_t* dy, const uint8_t* dye, const uint8_t* w, const uint8_t* we,
-                   const int64_t* offsets, int G, int64_t m_cap, int64_t N, int64_t K, void* dx,
-                   bool bf16, hipStream_t stream) {
+                   const int64_t* offsets, int G, int64_t m_cap, int64_t L, int64_t ncols,
+                   BLayout bl, void* dx, bool bf16, hipStream_t stream) {
   static bool done[2] = {false, false};
-  const int64_t tiles = ((m_cap + T - 1) / T + G) * (K / T);   // bound on live tiles
+  const int64_t tiles = ((m_cap + T - 1) / T + G) * (ncols / T);   // bound on live tiles
   auto k = bf16 ? k_dgrad<T, true> : k_dgrad<T, false>;
   hipError_t e = set_lds(k, lds_bytes<T>(), done[bf16]);
   if (e != hipSuccess) return e;
-  k<<<(unsigned)tiles, 256, lds_bytes<T>(), stream>>>(dy, dye, w, we, offsets, G, N, K, dx);
+  k<<<(unsigned)tiles, 256, lds_bytes<T>(), stream>>>(dy, dye, w, we, offsets, G, L, ncols, bl,
+                                                      dx);
   return hipGetLastError();
+}
+
+// Grouped row x row MXFP8 GEMM: out[r, c] = sum_l A[r, l] * B(g)[c, l] for the
+// rows r of group g, out [m_cap, ncols] row-major.
+hipError_t launch_rowxrow(const uint8_t* a, const uint8_t* ae, const uint8_t* b,
+                          const uint8_t* be, const int64_t* offsets, int G, int64_t m_cap,
+                          int64_t L, int64_t ncols, BLayout bl, void* out, bool out_bf16,
+                          hipStream_t stream) {
+  if (m_cap == 0 || G == 0) return hipSuccess;
+  if (ncols % 256 == 0 && m_cap >= 256 * (int64_t)G && G <= 8192) {
+    static bool done[2] = {false, false};
+    auto k = out_bf16 ? k_dgrad_dma<true> : k_dgrad_dma<false>;
+    const size_t lds = (size_t)DS * D_STAGE;
+    hipError_t e = set_lds(k, lds, done[out_bf16]);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((m_cap + 255) / 256 + G) * (ncols / 256);   // bound on live tiles
+    k<<<(unsigned)tiles, 256, lds, stream>>>(a, ae, b, be, offsets, G, L, ncols, bl, out);
+    return hipGetLastError();
+  }
+  return dgrad_t<128>(a, ae, b, be, offsets, G, m_cap, L, ncols, bl, out, out_bf16, stream);
 }
 
 template <int T>
@@ -729,18 +767,17 @@ hipError_t wgrad_t(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* xT, c
 hipError_t launch_dgrad(const uint8_t* dy, const uint8_t* dye, const uint8_t* w,
                         const uint8_t* we, const int64_t* offsets, int G, int64_t m_cap,
                         int64_t N, int64_t K, void* dx, bool dx_bf16, hipStream_t stream) {
-  if (m_cap == 0 || G == 0) return hipSuccess;
-  if (K % 256 == 0 && m_cap >= 256 * (int64_t)G && G <= 8192) {
-    static bool done[2] = {false, false};
-    auto k = dx_bf16 ? k_dgrad_dma<true> : k_dgrad_dma<false>;
-    const size_t lds = (size_t)DS * D_STAGE;
-    hipError_t e = set_lds(k, lds, done[dx_bf16]);
-    if (e != hipSuccess) return e;
-    const int64_t tiles = ((m_cap + 255) / 256 + G) * (K / 256);   // bound on live tiles
-    k<<<(unsigned)tiles, 256, lds, stream>>>(dy, dye, w, we, offsets, G, N, K, dx);
-    return hipGetLastError();
-  }
-  return dgrad_t<128>(dy, dye, w, we, offsets, G, m_cap, N, K, dx, dx_bf16, stream);
+  // W8 [K, G*N]: group g's rows are all K, its contraction starts at g*N
+  return launch_rowxrow(dy, dye, w, we, offsets, G, m_cap, N, K, BLayout{(int64_t)G * N, N, 0},
+                        dx, dx_bf16, stream);
+}
+
+hipError_t launch_fwd_mxfp8(const uint8_t* x, const uint8_t* xe, const uint8_t* w,
+                            const uint8_t* we, const int64_t* offsets, int G, int64_t m_cap,
+                            int64_t N, int64_t K, void* y, bool y_bf16, hipStream_t stream) {
+  // W8 [G*N, K]: group g's rows start at g*N, contraction from 0
+  return launch_rowxrow(x, xe, w, we, offsets, G, m_cap, K, N, BLayout{K, 0, N}, y, y_bf16,
+                        stream);
 }
 
 hipError_t launch_wgrad(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* xT,

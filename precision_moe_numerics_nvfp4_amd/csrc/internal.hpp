@@ -39,6 +39,12 @@ hipError_t launch_mxfp8_quantize_colwise(const void* x, bool bf16, int64_t rows,
                                          uint8_t* out_e4m3, uint8_t* out_e8m0,
                                          hipStream_t stream);
 
+// permute.hip: copy rows dst[r] = src[row_token[r]] for r < offsets[G]
+hipError_t launch_gather_rows(const int32_t* row_token, const int64_t* offsets, int G,
+                              int64_t m_cap, int64_t src_rows, const uint8_t* src_q,
+                              const uint8_t* src_s, int64_t qbytes, int64_t sbytes,
+                              uint8_t* dst_q, uint8_t* dst_s, hipStream_t stream);
+
 // gemm_fwd.hip
 hipError_t launch_fwd_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const float* a_outer, const uint8_t* b_codes,
@@ -50,6 +56,9 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scal
 hipError_t launch_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0, const uint8_t* w_e4m3,
                         const uint8_t* w_e8m0, const int64_t* offsets, int G, int64_t m_cap,
                         int64_t N, int64_t K, void* dx, bool dx_bf16, hipStream_t stream);
+hipError_t launch_fwd_mxfp8(const uint8_t* x_e4m3, const uint8_t* x_e8m0, const uint8_t* w_e4m3,
+                            const uint8_t* w_e8m0, const int64_t* offsets, int G, int64_t m_cap,
+                            int64_t N, int64_t K, void* y, bool y_bf16, hipStream_t stream);
 hipError_t launch_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0,
                         const uint8_t* xT_e4m3, const uint8_t* xT_e8m0,
                         const int64_t* padded_offsets, int G, int64_t P, int64_t N, int64_t K,

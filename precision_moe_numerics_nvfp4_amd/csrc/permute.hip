@@ -419,7 +419,50 @@ __global__ __launch_bounds__(256) void k_scatter_copy(
                   K, pc, ps, po);
 }
 
+// Row gather of already-grouped rows: dst row r (r < offsets[G]) is src row
+// row_token[r]; code rows of qbytes (a multiple of 16, 16-byte aligned) and
+// scale rows of sbytes. Indices outside the source are skipped.
+__global__ __launch_bounds__(256) void k_gather_rows(const int32_t* __restrict__ row_token,
+                                                     const int64_t* __restrict__ offsets, int G,
+                                                     int64_t src_rows,
+                                                     const uint8_t* __restrict__ sq,
+                                                     const uint8_t* __restrict__ ss,
+                                                     int64_t qbytes, int64_t sbytes,
+                                                     uint8_t* __restrict__ dq,
+                                                     uint8_t* __restrict__ ds) {
+  const int64_t M = offsets[G];
+  const int64_t n16 = qbytes / 16;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M * n16; i += stride) {
+    const int64_t r = i / n16, c = i - r * n16;
+    const int64_t t = row_token[r];
+    if (t < 0 || t >= src_rows) continue;
+    *reinterpret_cast<uint4*>(dq + r * qbytes + 16 * c) =
+        *reinterpret_cast<const uint4*>(sq + t * qbytes + 16 * c);
+  }
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M * sbytes; i += stride) {
+    const int64_t r = i / sbytes, c = i - r * sbytes;
+    const int64_t t = row_token[r];
+    if (t < 0 || t >= src_rows) continue;
+    ds[r * sbytes + c] = ss[t * sbytes + c];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_rows(const int32_t* row_token, const int64_t* offsets, int G,
+                              int64_t m_cap, int64_t src_rows, const uint8_t* src_q,
+                              const uint8_t* src_s, int64_t qbytes, int64_t sbytes,
+                              uint8_t* dst_q, uint8_t* dst_s, hipStream_t stream) {
+  if (m_cap == 0 || G == 0) return hipSuccess;
+  int64_t grid = (m_cap * (qbytes / 16) + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  k_gather_rows<<<(unsigned)grid, 256, 0, stream>>>(row_token, offsets, G, src_rows, src_q, src_s,
+                                                    qbytes, sbytes, dst_q, dst_s);
+  return hipGetLastError();
+}
 
 size_t permute_workspace_bytes(int64_t T, int k, int n_local) {
   const int64_t n = T * k;

@@ -90,6 +90,17 @@ def test_gemm_and_requant_argument_errors(L):
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16711936 + 32 - 16711936 % 32, 128, 128, FAKE,
              None) == EUNSUP
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 16385, 64, 128, 128, FAKE, None) == EUNSUP
+    f8 = L.moe_fwd_grouped_gemm_mxfp8
+    assert f8(FAKE, FAKE, FAKE, FAKE, None, 2, 64, 256, 256, FAKE, 0, None) == EINVAL   # no offsets
+    assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 256, 256, FAKE, 5, None) == EINVAL   # bad dtype
+    assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 200, 256, FAKE, 0, None) == EUNSUP   # N % 128
+    assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 256, 96, FAKE, 0, None) == EUNSUP    # K % 128
+    assert f8(FAKE_MIS, FAKE, FAKE, FAKE, FAKE, 2, 64, 256, 256, FAKE, 0, None) == EUNSUP
+    assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, 256, FAKE, 0, None) == 0         # nothing to do
+    gr = L.mxfp8_gather_rows
+    assert gr(None, FAKE, 2, 64, FAKE, FAKE, 10, 256, FAKE, FAKE, None) == EINVAL
+    assert gr(FAKE, FAKE, 2, 64, FAKE, FAKE, 10, 48, FAKE, FAKE, None) == EUNSUP        # K % 32
+    assert gr(FAKE, FAKE, 2, 64, FAKE, FAKE, -1, 256, FAKE, FAKE, None) == EINVAL
     m = L.mxfp8_quantize
     assert m(FAKE, 1, 64, 256, 9, None, None, 0, 0, FAKE, FAKE, None) == EINVAL
     assert m(FAKE, 1, 64, 48, 0, None, None, 0, 0, FAKE, FAKE, None) == EUNSUP

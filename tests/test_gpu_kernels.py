@@ -421,6 +421,67 @@ def test_dgrad(nv, counts, N, K):
     assert_gemm_close(got[:M], ref, groups, bound, what="dgrad", elementwise=False)
 
 
+# all-MXFP8 forward: 256x256 tiles (m_cap >= 256 G, N % 256 == 0) and the
+# 128-row fallback, ragged groups, an empty group
+@pytest.mark.parametrize("counts,N,K", [([300, 0, 517, 260], 512, 384), ([1100], 256, 1024),
+                                        ([37, 5, 100], 384, 256), ([64, 200], 128, 640)])
+def test_fwd_grouped_gemm_mxfp8(nv, counts, N, K):
+    import torch
+    off, pad = _groups_from_counts(counts)
+    M, G = int(off[-1]), len(counts)
+    x = gen.normal(900 + N, 0, (M, K))
+    gen.with_outliers(x, 900 + N, 6, frac=0.01)
+    w = gen.normal(901 + N, 1, (G * N, K), std=0.02)
+    xq, xe = _mx(x)
+    wq, we = _mx(w)
+    cap = M + 19
+    dxq = torch.zeros((cap, K), dtype=torch.uint8, device="cuda")
+    dxq[:M] = to_dev(xq)
+    dxe = torch.zeros((cap, K // 32), dtype=torch.uint8, device="cuda")
+    dxe[:M] = to_dev(xe)
+    y = torch.full((cap, N), float("nan"), dtype=torch.float32, device="cuda")
+    nv.moe_fwd_grouped_gemm_mxfp8(dxq, dxe, to_dev(wq), to_dev(we), to_dev(off), y=y)
+    _sync()
+    got = from_dev(y)
+    assert np.all(np.isnan(got[M:]))
+    ref = GM.fwd_grouped_mxfp8(xq, xe, wq, we, off, N, accum="fp64")
+    X, W = np.abs(MX.dequantize(xq, xe)), np.abs(MX.dequantize(wq, we)).reshape(G, N, K)
+    bound = np.zeros((M, N))
+    for g in range(G):
+        bound[off[g]:off[g + 1]] = mx_bound(X[off[g]:off[g + 1]], W[g])
+    groups = [(off[g], off[g + 1]) for g in range(G)]
+    assert_gemm_close(got[:M], ref, groups, bound, what="fwd mxfp8", elementwise=False)
+    # bf16 output: within one bf16 step of the exact value where the float32
+    # result is within its bound
+    yb = nv.moe_fwd_grouped_gemm_mxfp8(dxq, dxe, to_dev(wq), to_dev(we), to_dev(off),
+                                       out_dtype=torch.bfloat16)
+    _sync()
+    gb = F.bf16_bits_to_f32(from_dev(yb)[:M]).astype(np.float64)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-38))) - 7)
+    assert np.all(np.abs(gb - ref) <= ulp * 1.0000001 + bound)
+
+
+def test_mxfp8_gather_rows(nv):
+    import torch
+    topk, e0, nl = gen.route_uniform(905, 700, 16, 3), 4, 8
+    T, k = topk.shape
+    K = 288
+    x8, xe = _mx(gen.normal(906, 0, (T, K)))
+    o = nv.moe_permute(to_dev(topk), e0, nl,
+                       *(to_dev(a) for a in Q.quantize(gen.to_bf16_bits(gen.normal(907, 0, (T, 256))))))
+    _sync()
+    off, pad, rt, rs = PM.permute(topk, e0, nl)
+    M = int(off[-1])
+    cap = T * k
+    dq = torch.full((cap, K), 0xAB, dtype=torch.uint8, device="cuda")
+    de = torch.full((cap, K // 32), 0xAB, dtype=torch.uint8, device="cuda")
+    nv.mxfp8_gather_rows(o["row_token"], o["offsets"], to_dev(x8), to_dev(xe), out=(dq, de))
+    _sync()
+    assert np.array_equal(from_dev(dq)[:M], x8[rt])
+    assert np.array_equal(from_dev(de)[:M], xe[rt])
+    assert np.all(from_dev(dq)[M:] == 0xAB) and np.all(from_dev(de)[M:] == 0xAB)
+
+
 @pytest.mark.parametrize("counts,N,K", [([100, 0, 37, 250], 256, 384), ([64], 512, 256), ([129, 3], 128, 128),
                                          # unsorted sizes with ties (tiles are ranked by size)
                                          ([40, 300, 0, 40, 130, 300, 7], 256, 512)])

@@ -161,3 +161,31 @@ def test_dgrad_wgrad_bruteforce_layouts():
     assert np.array_equal(DYT[:, poff[1]:poff[1] + 33], MX.dequantize(*MX.quantize_rne(
         np.ascontiguousarray(np.pad(dy[7:40].T, ((0, 0), (0, 31))))))[:, :33])
     assert F.E4M3_MAX == 448.0
+
+
+def test_forward_mxfp8_bruteforce_and_fp32_bound():
+    """The all-MXFP8 forward: exact sums by brute force over k on sampled
+    outputs (every dequantized product is exact), and float32 accumulation
+    within the summation error bound of the exact sum."""
+    r = np.random.default_rng(28)
+    G, N, K = 3, 32, 96
+    offsets = np.array([0, 5, 5, 23])
+    M = int(offsets[-1])
+    x = (r.standard_normal((M, K)) * np.exp2(r.integers(-6, 6, (M, 1)))).astype(np.float32)
+    w = (r.standard_normal((G * N, K)) * 0.05).astype(np.float32)
+    x8, xe = MX.quantize_rne(x)
+    w8, we = MX.quantize_rne(w)
+    y64 = GM.fwd_grouped_mxfp8(x8, xe, w8.reshape(G, N, K), we.reshape(G, N, K // 32), offsets, N,
+                               accum="fp64")
+    y32 = GM.fwd_grouped_mxfp8(x8, xe, w8, we, offsets, N)
+    X, W = MX.dequantize(x8, xe), MX.dequantize(w8, we).reshape(G, N, K)
+    for g in range(G):
+        for rr in range(offsets[g], offsets[g + 1]):
+            for n in range(0, N, 5):
+                s = sum(Fraction(float(X[rr, k])) * Fraction(float(W[g, n, k])) for k in range(K))
+                assert abs(float(s) - y64[rr, n]) <= 1e-12 * max(1.0, abs(float(s)))
+                bound = K * 2.0 ** -24 * float(sum(abs(Fraction(float(X[rr, k])) * Fraction(float(W[g, n, k])))
+                                                   for k in range(K)))
+                assert abs(float(y32[rr, n]) - float(s)) <= bound + 1e-30
+    # rows of an empty group: none; rows past offsets[-1]: none
+    assert y32.shape == (M, N)
