@@ -192,6 +192,22 @@ NVFP4MOE_API int mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_
                    uint8_t* out_e4m3, uint8_t* out_e8m0, void* stream);
 
 /*
+ * Both MXFP8 orientations of dY from one read of it: the NVFP4MOE_ROWWISE and
+ * NVFP4MOE_COLWISE_GROUPED results of mxfp8_quantize, byte for byte.
+ * Pages: as mxfp8_quantize.
+ *
+ * row_e4m3 [rows, cols], row_e8m0 [rows, cols/32]: written for the rows that
+ * belong to a group (offsets[0] <= r < offsets[G]), other rows untouched;
+ * col_e4m3 [cols, P], col_e8m0 [cols, P/32]: as NVFP4MOE_COLWISE_GROUPED.
+ * Requires cols % 128 == 0, P % 32 == 0, x, row_e4m3 and col_e4m3 16-byte
+ * aligned.
+ */
+NVFP4MOE_API int mxfp8_quantize_dual(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                        const int64_t* offsets, const int64_t* padded_offsets, int G, int64_t P,
+                        uint8_t* row_e4m3, uint8_t* row_e8m0, uint8_t* col_e4m3,
+                        uint8_t* col_e8m0, void* stream);
+
+/*
  * MXFP8 dgrad grouped GEMM (contraction over N).
  * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), sections
  * "NVFP4 forward, MXFP8 backward" and "Stochastic rounding across transposes".

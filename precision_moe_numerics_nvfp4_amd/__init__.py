@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     moe_permute,
     mxfp8_gather_rows,
     mxfp8_quantize,
+    mxfp8_quantize_dual,
     mxfp8_requant_sr,
     nvfp4_quantize,
     permute_workspace_size,

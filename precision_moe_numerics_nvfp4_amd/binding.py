@@ -41,6 +41,8 @@ SIGNATURES = {
     "moe_fwd_grouped_gemm_mxfp8": ([_p, _p, _p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p,
                                     _c_int, _p], _c_int),
     "mxfp8_gather_rows": ([_p, _p, _c_int, _c_i64, _p, _p, _c_i64, _c_i64, _p, _p, _p], _c_int),
+    "mxfp8_quantize_dual": ([_p, _c_int, _c_i64, _c_i64, _p, _p, _c_int, _c_i64, _p, _p, _p, _p,
+                             _p], _c_int),
 }
 
 _LIB = None
@@ -354,3 +356,26 @@ def mxfp8_gather_rows(row_token, offsets, src_e4m3, src_e8m0, m_cap=None, out=No
                                  _stream(src_e4m3))
     _check("mxfp8_gather_rows", st)
     return out
+
+
+def mxfp8_quantize_dual(x, offsets, padded_offsets, P, row_out=None, col_out=None):
+    """dY [rows, cols] -> (row-wise MXFP8 [rows, cols] + [rows, cols/32] for the
+    grouped rows, grouped column-wise [cols, P] + [cols, P/32]) in one pass."""
+    torch = _torch()
+    _dev(x, "x", ndim=2)
+    _dev(offsets, "offsets", torch.int64, 1)
+    _dev(padded_offsets, "padded_offsets", torch.int64, 1)
+    rows, cols = x.shape
+    dev = x.device
+    if row_out is None:
+        row_out = (torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                   torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev))
+    if col_out is None:
+        col_out = (torch.empty((cols, P), dtype=torch.uint8, device=dev),
+                   torch.empty((cols, P // 32), dtype=torch.uint8, device=dev))
+    G = offsets.shape[0] - 1
+    st = lib().mxfp8_quantize_dual(_ptr(x), _in_dtype(x), rows, cols, _ptr(offsets),
+                                   _ptr(padded_offsets), G, int(P), _ptr(row_out[0]),
+                                   _ptr(row_out[1]), _ptr(col_out[0]), _ptr(col_out[1]), _stream(x))
+    _check("mxfp8_quantize_dual", st)
+    return row_out[0], row_out[1], col_out[0], col_out[1]

@@ -181,6 +181,23 @@ int moe_bwd_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0, const uint8_
                                  dw, as_stream(stream)));
 }
 
+int mxfp8_quantize_dual(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                        const int64_t* offsets, const int64_t* padded_offsets, int G, int64_t P,
+                        uint8_t* row_e4m3, uint8_t* row_e8m0, uint8_t* col_e4m3,
+                        uint8_t* col_e8m0, void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0 && G >= 0 && P >= 0, NVFP4MOE_EINVAL);
+  REQUIRE(x_dtype == NVFP4MOE_F32 || x_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (G == 0 || P == 0 || cols == 0) return NVFP4MOE_OK;
+  REQUIRE(offsets && padded_offsets && row_e4m3 && row_e8m0 && col_e4m3 && col_e8m0,
+          NVFP4MOE_EINVAL);
+  if (rows > 0) REQUIRE(x != nullptr, NVFP4MOE_EINVAL);
+  REQUIRE(cols % 128 == 0 && P % 32 == 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(x) && aligned16(col_e4m3) && aligned16(row_e4m3), NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_mxfp8_quantize_dual(x, x_dtype == NVFP4MOE_BF16, rows, cols, offsets,
+                                               padded_offsets, G, P, row_e4m3, row_e8m0,
+                                               col_e4m3, col_e8m0, as_stream(stream)));
+}
+
 int moe_fwd_grouped_gemm_mxfp8(const uint8_t* x_e4m3, const uint8_t* x_e8m0,
                                const uint8_t* w_e4m3, const uint8_t* w_e8m0,
                                const int64_t* offsets, int G, int64_t m_cap, int64_t N, int64_t K,

@@ -45,6 +45,12 @@ hipError_t launch_gather_rows(const int32_t* row_token, const int64_t* offsets, 
                               const uint8_t* src_s, int64_t qbytes, int64_t sbytes,
                               uint8_t* dst_q, uint8_t* dst_s, hipStream_t stream);
 
+// requant.hip: both dY orientations from one read (row-wise for rows < offsets[G])
+hipError_t launch_mxfp8_quantize_dual(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                      const int64_t* offsets, const int64_t* padded, int G,
+                                      int64_t P, uint8_t* row_out, uint8_t* row_e8, uint8_t* out,
+                                      uint8_t* out_e8, hipStream_t stream);
+
 // gemm_fwd.hip
 hipError_t launch_fwd_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const float* a_outer, const uint8_t* b_codes,

@@ -79,12 +79,16 @@ __device__ __forceinline__ int64_t xcd_band(int64_t w, int64_t live) {
   return x * q + (x < r ? x : r) + s;
 }
 
-template <Src S, bool SR>
+// ROWS (float sources only): the staged tile also yields the row-wise MXFP8
+// quantization of its rows (blocks of 32 along the columns), written to
+// row_out [rows, cols] and row_e8 [rows, cols/32] at the source row.
+template <Src S, bool SR, bool ROWS = false>
 __global__ __launch_bounds__(256) void k_transpose_mx(
     const void* __restrict__ src, const uint8_t* __restrict__ src_scales,
     const float* __restrict__ src_outer, int64_t rpg, int64_t cols,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ padded, int G, int64_t P,
-    uint64_t seed, uint32_t tag, uint8_t* __restrict__ out, uint8_t* __restrict__ out_e8) {
+    uint64_t seed, uint32_t tag, uint8_t* __restrict__ out, uint8_t* __restrict__ out_e8,
+    uint8_t* __restrict__ row_out = nullptr, uint8_t* __restrict__ row_e8 = nullptr) {
   __shared__ Tile<S> tile;
   __shared__ int64_t row_of[TP];  // source row of each tile token, -1 = padding
 
@@ -167,6 +171,44 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
   }
   __syncthreads();
 
+  if constexpr (ROWS && S != Src::NVFP4) {
+    // row-wise pass over the staged tile: lane l takes 8 columns (chunk l % 16)
+    // of token (l / 16) + 16 it; the four lanes of a quad hold one 32-column
+    // block. Same exponent rule and rounding as the row-wise kernel.
+    const int c = tid & 15;
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const int t = (tid >> 4) + 16 * it;
+      const int64_t r = row_of[t];
+      float v[8];
+      if constexpr (S == Src::BF16) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&tile.v[slot_of(t)][8 * c]);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = u2f(w[j] << 16);
+          v[2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+        }
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(&tile.v[slot_of(t)][8 * c]);
+        const float4 b = *reinterpret_cast<const float4*>(&tile.v[slot_of(t)][8 * c + 4]);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+      float mf = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mf = fmaxf(mf, fabsf(v[j]));
+      const uint32_t code = e8m0_code_bits(quad_max_bits(f2u(mf)));
+      const float scale = u2f(code << 23);
+      const uint32_t lo = e4m3x4_rne_scaled(v[0], v[1], v[2], v[3], scale);
+      const uint32_t hi = e4m3x4_rne_scaled(v[4], v[5], v[6], v[7], scale);
+      if (r >= 0) {
+        *reinterpret_cast<uint2*>(row_out + r * cols + k0 + 8 * c) = make_uint2(lo, hi);
+        if ((c & 3) == 0) row_e8[r * (cols / 32) + (k0 + 8 * c) / 32] = (uint8_t)code;
+      }
+    }
+  }
+
   // ---- micro-tile: 8 columns x 8 tokens per thread
   const int pc = tid & 15;   // token chunk: tokens 8*pc .. 8*pc+7 of the tile
   const int kc = tid >> 4;   // column chunk: columns 8*kc .. 8*kc+7
@@ -239,15 +281,16 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
   }
 }
 
-template <Src S, bool SR>
+template <Src S, bool SR, bool ROWS = false>
 hipError_t run(const void* src, const uint8_t* sc, const float* so, int64_t rpg, int64_t rows,
                int64_t cols, const int64_t* offsets, const int64_t* padded, int G, int64_t P,
-               uint64_t seed, uint32_t tag, uint8_t* out, uint8_t* out_e8, hipStream_t stream) {
+               uint64_t seed, uint32_t tag, uint8_t* out, uint8_t* out_e8, hipStream_t stream,
+               uint8_t* row_out = nullptr, uint8_t* row_e8 = nullptr) {
   (void)rows;
   if (P == 0 || cols == 0 || G == 0) return hipSuccess;
   const int64_t grid = (P + TP - 1) / TP * (cols / TK);
-  k_transpose_mx<S, SR><<<(unsigned)grid, 256, 0, stream>>>(src, sc, so, rpg, cols, offsets, padded,
-                                                            G, P, seed, tag, out, out_e8);
+  k_transpose_mx<S, SR, ROWS><<<(unsigned)grid, 256, 0, stream>>>(
+      src, sc, so, rpg, cols, offsets, padded, G, P, seed, tag, out, out_e8, row_out, row_e8);
   return hipGetLastError();
 }
 
@@ -270,6 +313,17 @@ hipError_t launch_mxfp8_quantize_colwise(const void* x, bool bf16, int64_t rows,
                                  out, out_e8, stream);
   return run<Src::F32, false>(x, nullptr, nullptr, 0, rows, cols, offsets, padded, G, P, 0, 0,
                               out, out_e8, stream);
+}
+
+hipError_t launch_mxfp8_quantize_dual(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                      const int64_t* offsets, const int64_t* padded, int G,
+                                      int64_t P, uint8_t* row_out, uint8_t* row_e8, uint8_t* out,
+                                      uint8_t* out_e8, hipStream_t stream) {
+  if (bf16)
+    return run<Src::BF16, false, true>(x, nullptr, nullptr, 0, rows, cols, offsets, padded, G, P,
+                                       0, 0, out, out_e8, stream, row_out, row_e8);
+  return run<Src::F32, false, true>(x, nullptr, nullptr, 0, rows, cols, offsets, padded, G, P, 0,
+                                    0, out, out_e8, stream, row_out, row_e8);
 }
 
 }  // namespace nvfp4moe

@@ -75,10 +75,10 @@ class ExpertLayerStep:
                                   rows_per_group=self.N, out=self.wT[0], out_e8=self.wT[1])
 
     def quantize_dy(self, dy):
+        """Both orientations in one pass (row-wise for the routed rows)."""
         p = self.perm
-        B.mxfp8_quantize(dy, "rowwise", out=self.dy8[0], out_e8=self.dy8[1])
-        B.mxfp8_quantize(dy, "colwise", p["offsets"], p["padded_offsets"], self.P,
-                         out=self.dyT[0], out_e8=self.dyT[1])
+        B.mxfp8_quantize_dual(dy, p["offsets"], p["padded_offsets"], self.P, row_out=self.dy8,
+                              col_out=self.dyT)
 
     def dgrad(self):
         return B.moe_bwd_dgrad(*self.dy8, *self.wT, self.perm["offsets"], self.N, self.K,

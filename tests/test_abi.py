@@ -97,6 +97,10 @@ def test_gemm_and_requant_argument_errors(L):
     assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 256, 96, FAKE, 0, None) == EUNSUP    # K % 128
     assert f8(FAKE_MIS, FAKE, FAKE, FAKE, FAKE, 2, 64, 256, 256, FAKE, 0, None) == EUNSUP
     assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, 256, FAKE, 0, None) == 0         # nothing to do
+    qd = L.mxfp8_quantize_dual
+    assert qd(FAKE, 1, 64, 256, None, FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert qd(FAKE, 1, 64, 96, FAKE, FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == EUNSUP
+    assert qd(FAKE, 1, 64, 256, FAKE, FAKE, 2, 100, FAKE, FAKE, FAKE, FAKE, None) == EUNSUP
     gr = L.mxfp8_gather_rows
     assert gr(None, FAKE, 2, 64, FAKE, FAKE, 10, 256, FAKE, FAKE, None) == EINVAL
     assert gr(FAKE, FAKE, 2, 64, FAKE, FAKE, 10, 48, FAKE, FAKE, None) == EUNSUP        # K % 32

@@ -275,6 +275,31 @@ def test_mxfp8_quantize_colwise(nv, bf16, counts, cols):
     assert np.array_equal(from_dev(e), re)
 
 
+@pytest.mark.parametrize("bf16,counts,cols", [(True, [37, 0, 100, 5], 256), (False, [64, 65], 512),
+                                              (True, [1000, 3], 128), (False, [40, 3, 70], 256)])
+def test_mxfp8_quantize_dual(nv, bf16, counts, cols):
+    import torch
+    off, pad = _groups_from_counts(counts)
+    M = int(off[-1])
+    x = gen.normal(650 + cols, 3, (M + 5, cols), std=1e-3)    # 5 rows past the groups
+    if len(counts) > 2:
+        x[off[2]:off[3]] *= np.float32(1e-36)
+    a = gen.to_bf16_bits(x) if bf16 else x
+    P = int(pad[-1]) + 32
+    row = (torch.full((M + 5, cols), 0xCD, dtype=torch.uint8, device="cuda"),
+           torch.full((M + 5, cols // 32), 0xCD, dtype=torch.uint8, device="cuda"))
+    rq, re_, cq, ce = nv.mxfp8_quantize_dual(to_dev(a), to_dev(off), to_dev(pad), P, row_out=row)
+    _sync()
+    wr, wre = MX.quantize_rowwise(a[:M])
+    wc, wce = MX.quantize_colwise_grouped(a[:M], off, pad, P)
+    assert np.array_equal(from_dev(rq)[:M], wr)
+    assert np.array_equal(from_dev(re_)[:M], wre)
+    assert np.all(from_dev(rq)[M:] == 0xCD) and np.all(from_dev(re_)[M:] == 0xCD)
+    pt = int(pad[-1])
+    assert np.array_equal(from_dev(cq)[:, :pt], wc[:, :pt])
+    assert np.array_equal(from_dev(ce)[:, :pt // 32], wce[:, :pt // 32])
+
+
 # ------------------------------------------------------------------ forward GEMM
 
 def _fwd_case(seed, T, K, N, E, k, exact=False):
