@@ -260,6 +260,23 @@ def mxfp8_forward_compare(torch, reps):
             "note": "weights quantized once outside the timed paths"}
 
 
+def tile16_compare(torch, reps):
+    import precision_moe_numerics_nvfp4_amd as nv
+    from workloads import gen
+    w = gen.small_moe()
+    N, E, K = w["N"], w["E"], w["K"]
+    wt = dev_tensor(w["w"], torch)
+    q1 = nv.nvfp4_quantize(wt, rows_per_group=N)
+    qt = nv.nvfp4_quantize_tile16(wt, rows_per_group=N)
+    t1 = _time(torch, lambda: nv.nvfp4_quantize(wt, N, *q1), reps)
+    tt = _time(torch, lambda: nv.nvfp4_quantize_tile16(wt, N, *qt), reps)
+    n = E * N * K
+    tbytes = n * (2 + 0.5) + n / 256        # bf16 in, codes out, one scale per 256 elements
+    return {"weights": f"{E}x{N}x{K} bf16",
+            "blocks_1x16": {"ms": round(t1, 4), "GB/s": round(n * B_QUANT_BF16 / t1 / 1e6, 1)},
+            "tiles_16x16": {"ms": round(tt, 4), "GB/s": round(tbytes / tt / 1e6, 1)}}
+
+
 def extras(torch, reps=10):
     import precision_moe_numerics_nvfp4_amd as nv
     from workloads import gen
@@ -327,6 +344,10 @@ def extras(torch, reps=10):
     # on the small MoE layer: MXFP8 quantize of X and W (row-wise, RNE), the row
     # gather in expert order, the grouped GEMM; next to the NVFP4 forward's
     out["mxfp8_forward_small_moe"] = mxfp8_forward_compare(torch, reps)
+    torch.cuda.empty_cache()
+    # the rejected 16x16-tile scaling (ablation): weight quantization speed next
+    # to the 16-element blocks, same weights, one outer scale per expert
+    out["tile16_weight_quantize"] = tile16_compare(torch, reps)
     torch.cuda.empty_cache()
     # streaming: 1 GiB bf16 [262144 x 2048] per-token quantize, then requant of its transpose
     rows, cols = 262144, 2048

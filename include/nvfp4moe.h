@@ -99,6 +99,26 @@ NVFP4MOE_API int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_
                    int outer_mode, int64_t rows_per_group,
                    uint8_t* codes, uint8_t* scales, float* outer, void* stream);
 
+/*
+ * NVFP4 with one E4M3 scale per 16x16 tile: the transpose-invariant
+ * alternative the pages report trying and rejecting as too sensitive to
+ * outliers; kept for the ablation against 16-element blocks.
+ * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), section
+ * "Stochastic rounding across transposes".
+ *
+ * x [rows, cols] (bf16 | f32), rows and cols multiples of 16; one outer scale
+ * per group of rows_per_group rows (a multiple of 16 dividing rows; rows for a
+ * single outer scale). A = max|x| over the group, s = A / 2688, tile scale
+ * S = E4M3_RNE(max|x_tile| / (6 s)), codes E2M1_RNE(x * (1 / (S s))) (signed
+ * zeros for a zero tile).
+ * codes [rows, cols/2] (element 2j low nibble), scales [rows/16, cols/16],
+ * outer [rows/rows_per_group] (float32, also the group-maximum scratch).
+ * Requires x 16-byte and codes 8-byte aligned, rows/16 <= 65535.
+ */
+NVFP4MOE_API int nvfp4_quantize_tile16(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                          int64_t rows_per_group, uint8_t* codes, uint8_t* scales, float* outer,
+                          void* stream);
+
 /* Bytes of device workspace moe_permute needs for T tokens, top-k, n_local experts. */
 NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int k, int n_local);
 

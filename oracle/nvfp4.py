@@ -129,3 +129,75 @@ def dequantize(codes, scales, outer, rows_per_group=None, apply_outer=True):
     if rows_per_group is not None:
         s = np.repeat(s, rows_per_group)
     return (inner * s[:, None]).astype(np.float32)
+
+
+# ---------------------------------------------------------------- 16x16 tiles
+#
+# The alternative the pages report trying and rejecting ("Inkling 2 Small uses
+# four-bit training ...", ai-primer, section "Stochastic rounding across
+# transposes"): one scale shared by each 16x16 tile, so that a tensor and its
+# transpose are represented by the same values; rejected as too sensitive to
+# outliers (one large value pushes the rest of its tile to zero). Reading:
+# the same two-level recipe as above with the 16-element block replaced by
+# the 16x16 tile and the outer scale taken per group of rows (the expert for
+# weights; one group for a whole tensor):
+#   A = max|x| over the group, s = A / 2688, d = 6 s,
+#   S_t = E4M3_RNE_saturating(max|x_t| / d) over tile t,
+#   codes E2M1_RNE_saturating(x * (1 / (S_t * s))), signed zeros when S_t = 0.
+# Layouts: codes as above; scales uint8 [rows/16, cols/16]; outer [groups].
+
+TILE = 16
+
+
+def quantize_tile16(x, rows_per_group=None):
+    """16x16-tile NVFP4 of x [rows, cols] (rows and cols multiples of 16).
+
+    rows_per_group None: one outer scale for the whole tensor; otherwise one
+    per group of rows_per_group rows (a multiple of 16).
+    Returns (codes [rows, cols/2], scales [rows/16, cols/16], outer [groups]).
+    """
+    x = _as_f32(x)
+    rows, cols = x.shape
+    if rows % TILE or cols % TILE:
+        raise ValueError("rows and cols must be multiples of 16")
+    rpg = rows if rows_per_group is None else rows_per_group
+    if rpg % TILE or (rows and rows % rpg):
+        raise ValueError("rows_per_group must be a multiple of 16 dividing rows")
+    ax = np.abs(x)
+    g = rows // rpg if rows else 0
+    amax = ax.reshape(g, rpg * cols).max(axis=1) if g else np.zeros(0, np.float32)
+    per_row_amax = np.repeat(amax, rpg)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        s_out = (amax / OUTER_DIVISOR).astype(np.float32)
+        s = (per_row_amax / OUTER_DIVISOR).astype(np.float32)
+        d = (np.float32(6.0) * s).astype(np.float32)
+        tr, tc = rows // TILE, cols // TILE
+        at = ax.reshape(tr, TILE, tc, TILE).max(axis=(1, 3))              # [tr, tc]
+        dt = d.reshape(tr, TILE)[:, 0]                                     # one d per tile row
+        t = (at / dt[:, None]).astype(np.float32)
+        t = np.where(per_row_amax.reshape(tr, TILE)[:, :1] == 0, np.float32(0), t)
+        scale_codes = F.e4m3_rne(t)
+        S = F.e4m3_decode(scale_codes).astype(np.float32)                  # [tr, tc]
+        st = s.reshape(tr, TILE)[:, 0]
+        r = (np.float32(1.0) / (S * st[:, None]).astype(np.float32)).astype(np.float32)
+        rr = np.repeat(np.repeat(r, TILE, axis=0), TILE, axis=1)           # [rows, cols]
+        y = (x * rr).astype(np.float32)
+        codes = F.e2m1_rne(y)
+    zero = np.repeat(np.repeat(scale_codes == 0, TILE, axis=0), TILE, axis=1)
+    signed_zero = (np.signbit(x).astype(np.uint8) << 3)
+    codes = np.where(zero, signed_zero, codes).astype(np.uint8)
+    return pack_codes(codes), scale_codes.astype(np.uint8), s_out
+
+
+def dequantize_tile16(codes, scales, outer, rows_per_group=None, apply_outer=True):
+    """16x16-tile NVFP4 -> float32: v = (e2m1 * S_t) * s, one rounding."""
+    c = unpack_codes(codes)
+    rows, cols = c.shape
+    S = F.e4m3_decode(np.asarray(scales)).astype(np.float64)
+    Sx = np.repeat(np.repeat(S, TILE, axis=0), TILE, axis=1)
+    inner = (F.e2m1_decode(c) * Sx).astype(np.float32)                     # exact
+    if not apply_outer:
+        return inner
+    rpg = rows if rows_per_group is None else rows_per_group
+    s = np.repeat(np.asarray(outer, dtype=np.float32), rpg)
+    return (inner * s[:, None]).astype(np.float32)

@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     mxfp8_quantize_dual,
     mxfp8_requant_sr,
     nvfp4_quantize,
+    nvfp4_quantize_tile16,
     permute_workspace_size,
     status_string,
 )

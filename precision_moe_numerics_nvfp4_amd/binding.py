@@ -41,6 +41,7 @@ SIGNATURES = {
     "moe_fwd_grouped_gemm_mxfp8": ([_p, _p, _p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p,
                                     _c_int, _p], _c_int),
     "mxfp8_gather_rows": ([_p, _p, _c_int, _c_i64, _p, _p, _c_i64, _c_i64, _p, _p, _p], _c_int),
+    "nvfp4_quantize_tile16": ([_p, _c_int, _c_i64, _c_i64, _c_i64, _p, _p, _p, _p], _c_int),
     "mxfp8_quantize_dual": ([_p, _c_int, _c_i64, _c_i64, _p, _p, _c_int, _c_i64, _p, _p, _p, _p,
                              _p], _c_int),
 }
@@ -379,3 +380,23 @@ def mxfp8_quantize_dual(x, offsets, padded_offsets, P, row_out=None, col_out=Non
                                    _ptr(row_out[1]), _ptr(col_out[0]), _ptr(col_out[1]), _stream(x))
     _check("mxfp8_quantize_dual", st)
     return row_out[0], row_out[1], col_out[0], col_out[1]
+
+
+def nvfp4_quantize_tile16(x, rows_per_group=None, codes=None, scales=None, outer=None):
+    """16x16-tile NVFP4 of x [rows, cols] (bf16|f32): (codes [rows, cols/2],
+    scales [rows/16, cols/16], outer [rows/rows_per_group])."""
+    torch = _torch()
+    _dev(x, "x", ndim=2)
+    rows, cols = x.shape
+    rpg = rows if rows_per_group is None else int(rows_per_group)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows // 16, cols // 16), dtype=torch.uint8, device=dev)
+    if outer is None:
+        outer = torch.empty((max(rows // max(rpg, 1), 1),), dtype=torch.float32, device=dev)
+    st = lib().nvfp4_quantize_tile16(_ptr(x), _in_dtype(x), rows, cols, rpg, _ptr(codes),
+                                     _ptr(scales), _ptr(outer), _stream(x))
+    _check("nvfp4_quantize_tile16", st)
+    return codes, scales, outer

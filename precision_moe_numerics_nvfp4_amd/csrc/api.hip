@@ -181,6 +181,23 @@ int moe_bwd_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0, const uint8_
                                  dw, as_stream(stream)));
 }
 
+int nvfp4_quantize_tile16(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                          int64_t rows_per_group, uint8_t* codes, uint8_t* scales, float* outer,
+                          void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0 && rows_per_group > 0, NVFP4MOE_EINVAL);
+  REQUIRE(x_dtype == NVFP4MOE_F32 || x_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (rows == 0 || cols == 0) return NVFP4MOE_OK;
+  REQUIRE(x && codes && scales && outer, NVFP4MOE_EINVAL);
+  REQUIRE(rows % 16 == 0 && cols % 16 == 0 && rows_per_group % 16 == 0 &&
+              rows % rows_per_group == 0,
+          NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(rows / 16 <= 65535, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(x) && ((reinterpret_cast<uintptr_t>(codes) & 7u) == 0), NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_nvfp4_quantize_tile16(x, x_dtype == NVFP4MOE_BF16, rows, cols,
+                                                 rows_per_group, codes, scales, outer,
+                                                 as_stream(stream)));
+}
+
 int mxfp8_quantize_dual(const void* x, int x_dtype, int64_t rows, int64_t cols,
                         const int64_t* offsets, const int64_t* padded_offsets, int G, int64_t P,
                         uint8_t* row_e4m3, uint8_t* row_e8m0, uint8_t* col_e4m3,

@@ -13,6 +13,9 @@ namespace nvfp4moe {
 hipError_t launch_nvfp4_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
                                  bool per_group, int64_t rows_per_group, uint8_t* codes,
                                  uint8_t* scales, float* outer, hipStream_t stream);
+hipError_t launch_nvfp4_quantize_tile16(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                        int64_t rpg, uint8_t* codes, uint8_t* scales,
+                                        float* outer, hipStream_t stream);
 hipError_t launch_mxfp8_quantize_rowwise(const void* x, bool bf16, int64_t rows, int64_t cols,
                                          uint8_t* out_e4m3, uint8_t* out_e8m0,
                                          hipStream_t stream);

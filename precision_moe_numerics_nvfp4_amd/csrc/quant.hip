@@ -110,6 +110,58 @@ __global__ __launch_bounds__(256) void k_nvfp4_quantize(
   }
 }
 
+// 16x16-tile NVFP4 (one E4M3 scale per tile, outer scale per group of rows):
+// a workgroup covers 16 rows x 256 columns; thread (r = tid % 16, c = tid /
+// 16) owns row r of tile column c (16 elements), the 16 lanes of a tile reduce
+// its maximum with four shuffles, and each lane packs its 16 codes. The group
+// maximum comes from the same pass as the per-expert quantizer.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_nvfp4_quantize_tile16(
+    const void* __restrict__ x, int64_t cols, const uint32_t* __restrict__ gamax, int64_t rpg,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int r = threadIdx.x & 15, c = threadIdx.x >> 4;
+  const int64_t ty = blockIdx.y;                          // tile row
+  const int64_t tc = (int64_t)blockIdx.x * 16 + c;        // tile column
+  const int64_t ntc = cols / 16;
+  const bool live = tc < ntc;                             // the same for a tile's 16 lanes
+  const int64_t row = ty * 16 + r;
+  Row16<BF16> v;
+  float m = 0.0f;
+  if (live) {
+    load16<BF16>(x, row * cols + tc * 16, v);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v.get(j)));
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (!live) return;
+  const float A = u2f(gamax[row / rpg]);
+  const float s = __fdiv_rn(A, 2688.0f);
+  const float d = __fmul_rn(6.0f, s);
+  uint32_t sc = 0;
+  if (A > 0.0f) sc = e4m3_rne_sat_pos(__fdiv_rn(m, d));
+  uint32_t lo = 0, hi = 0;
+  if (sc) {
+    const float rc = __fdiv_rn(1.0f, __fmul_rn(e4m3_pos_to_f32(sc), s));
+    float a[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[j] = __fmul_rn(v.get(j), rc);
+      b[j] = __fmul_rn(v.get(j + 8), rc);
+    }
+    lo = e2m1x8_rne(a);
+    hi = e2m1x8_rne(b);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo |= ((f2u(v.get(j)) >> 28) & 8u) << (4 * j);
+      hi |= ((f2u(v.get(j + 8)) >> 28) & 8u) << (4 * j);
+    }
+  }
+  *reinterpret_cast<uint2*>(codes + row * (cols / 2) + tc * 8) = make_uint2(lo, hi);
+  if (r == 0) scales[ty * ntc + tc] = (uint8_t)sc;
+}
+
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -277,6 +329,34 @@ hipError_t launch_nvfp4_quantize(const void* x, bool bf16, int64_t rows, int64_t
                                  float* outer, hipStream_t stream) {
   return bf16 ? quantize_impl<true>(x, rows, cols, per_group, rpg, codes, scales, outer, stream)
               : quantize_impl<false>(x, rows, cols, per_group, rpg, codes, scales, outer, stream);
+}
+
+template <bool BF16>
+static hipError_t quantize_tile16_impl(const void* x, int64_t rows, int64_t cols, int64_t rpg,
+                                       uint8_t* codes, uint8_t* scales, float* outer,
+                                       hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const int64_t G = rows / rpg;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(outer);
+  k_fill_u32<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(bits, G, 0u);
+  const int64_t per = rpg * cols;
+  const int64_t pieces = per / (BF16 ? 8 : 4);
+  int64_t gx = ((int64_t)device_cu_count() + G - 1) / G;
+  const int64_t most = (pieces + 1023) / 1024;
+  if (gx > most) gx = most;
+  gx = gx < 1 ? 1 : (gx > 65535 ? 65535 : gx);
+  k_group_amax<BF16><<<dim3((unsigned)gx, (unsigned)G), 1024, 0, stream>>>(x, per, bits);
+  const dim3 grid((unsigned)((cols / 16 + 15) / 16), (unsigned)(rows / 16));
+  k_nvfp4_quantize_tile16<BF16><<<grid, 256, 0, stream>>>(x, cols, bits, rpg, codes, scales);
+  k_outer_from_amax<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(outer, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize_tile16(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                        int64_t rpg, uint8_t* codes, uint8_t* scales,
+                                        float* outer, hipStream_t stream) {
+  return bf16 ? quantize_tile16_impl<true>(x, rows, cols, rpg, codes, scales, outer, stream)
+              : quantize_tile16_impl<false>(x, rows, cols, rpg, codes, scales, outer, stream);
 }
 
 hipError_t launch_mxfp8_quantize_rowwise(const void* x, bool bf16, int64_t rows, int64_t cols,

@@ -97,6 +97,12 @@ def test_gemm_and_requant_argument_errors(L):
     assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 256, 96, FAKE, 0, None) == EUNSUP    # K % 128
     assert f8(FAKE_MIS, FAKE, FAKE, FAKE, FAKE, 2, 64, 256, 256, FAKE, 0, None) == EUNSUP
     assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, 256, FAKE, 0, None) == 0         # nothing to do
+    t16 = L.nvfp4_quantize_tile16
+    assert t16(FAKE, 1, 64, 256, 0, FAKE, FAKE, FAKE, None) == EINVAL           # rows_per_group 0
+    assert t16(FAKE, 1, 40, 256, 40, FAKE, FAKE, FAKE, None) == EUNSUP          # rows % 16
+    assert t16(FAKE, 1, 64, 256, 24, FAKE, FAKE, FAKE, None) == EUNSUP          # group % 16
+    assert t16(FAKE, 1, 64, 200, 64, FAKE, FAKE, FAKE, None) == EUNSUP          # cols % 16
+    assert t16(None, 1, 64, 256, 64, FAKE, FAKE, FAKE, None) == EINVAL
     qd = L.mxfp8_quantize_dual
     assert qd(FAKE, 1, 64, 256, None, FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
     assert qd(FAKE, 1, 64, 96, FAKE, FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == EUNSUP

@@ -137,6 +137,23 @@ def test_nvfp4_quantize_per_expert(nv, bf16, E, N, K):
     assert np.array_equal(_bits(from_dev(o)), _bits(ro))
 
 
+@pytest.mark.parametrize("bf16,rows,cols,rpg", [(True, 512, 256, None), (False, 64, 96, 32),
+                                                 (True, 4096, 1024, 512), (True, 48, 4112, 16)])
+def test_nvfp4_quantize_tile16(nv, bf16, rows, cols, rpg):
+    x = gen.normal(450 + rows, 0, (rows, cols))
+    gen.with_outliers(x, 450 + rows, 6, frac=0.001)
+    x[:16, :16] = 0.0                                        # a zero tile
+    if rows >= 64:
+        x[32:48] *= np.float32(1e-30)                        # tiny values (zero tiles for rpg 16..32)
+    a = gen.to_bf16_bits(x) if bf16 else x
+    c, sc, o = nv.nvfp4_quantize_tile16(to_dev(a), rows_per_group=rpg)
+    _sync()
+    rc, rs, ro = Q.quantize_tile16(a, rows_per_group=rpg)
+    assert np.array_equal(from_dev(c), rc)
+    assert np.array_equal(from_dev(sc), rs)
+    assert np.array_equal(_bits(from_dev(o)), _bits(ro))
+
+
 # ------------------------------------------------------------------ permute
 
 # up to 16384 routed pairs take the one-launch form, more the three-launch one;
