@@ -5,9 +5,10 @@ quantization or matmul arithmetic. Both the HIP path (tests, bench) and the
 CPU oracle consume what it returns.
 
 Every tensor has its own numpy Generator seeded with SeedSequence([cfg, tid]):
-tid 0 = X, 1 = W (or W1), 2 = W2, 3 = dY, 4 = H, 5 = routing, 6/7 = outlier
-masks of X/W. bfloat16 tensors are returned as uint16 bit patterns made from
-float32 draws by round-to-nearest-even, so both sides see identical values.
+tid 0 = X, 1 = W (or W1), 2 = W2, 3 = dY (or dOut), 4 = H, 5 = routing,
+6/7 = outlier masks of X/W, 8 = routing-weight scores. bfloat16 tensors are
+returned as uint16 bit patterns made from float32 draws by
+round-to-nearest-even, so both sides see identical values.
 
 Workloads (shapes from the expert layer of Inkling 2 Small: 8 of 384 experts
 per token, 48 experts per GPU at 8-way expert parallelism):

@@ -6,7 +6,7 @@ __all__ = [
     "rng", "to_bf16_bits", "normal", "with_outliers", "route_uniform",
     "route_zipf", "zipf_placement", "philox_seed", "single_expert",
     "small_moe", "expert_share", "backward_dy", "decode", "streaming",
-    "moe_case",
+    "moe_case", "gates", "ffn_case",
 ]
 
 N_EXPERTS = 384
@@ -159,3 +159,32 @@ def moe_case(seed, T, K, N, E, k, routing="uniform", n_experts=None, e0=0,
         x, w, dy = to_bf16_bits(x), to_bf16_bits(w), to_bf16_bits(dy)
     return dict(cfg=seed, x=x, w=w, dy=dy, topk=topk, e0=e0, n_local=E, E=E,
                 T=T, K=K, N=N, k=k)
+
+
+def gates(cfg, T, k, tid=8):
+    """Routing weights [T, k] float32: positive, each row summing to one (a
+    softmax over the selected experts' scores; the scores are N(0, 1))."""
+    s = rng(cfg, tid).standard_normal(size=(T, k))
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def ffn_case(seed, T, K, F, E, k, routing="uniform", n_experts=None, e0=0,
+             x_std=1.0, w_std=0.02, dout_std=1e-3, fp32=False):
+    """The routed expert FFN (up-projection K -> F, down-projection F -> K)
+    at the same recipe as the workloads above: x [T, K], w1 [E, F, K],
+    w2 [E, K, F], gate [T, k] float32, dout [T, K]."""
+    n_experts = E if n_experts is None else n_experts
+    x = normal(seed, 0, (T, K), std=x_std)
+    w1 = normal(seed, 1, (E, F, K), std=w_std)
+    w2 = normal(seed, 2, (E, K, F), std=w_std)
+    dout = normal(seed, 3, (T, K), std=dout_std)
+    if routing == "uniform":
+        topk = route_uniform(seed, T, n_experts, k)
+    else:
+        topk = route_zipf(seed, T, k=k, n_experts=n_experts)
+    g = gates(seed, T, k)
+    if not fp32:
+        x, w1, w2, dout = to_bf16_bits(x), to_bf16_bits(w1), to_bf16_bits(w2), to_bf16_bits(dout)
+    return dict(cfg=seed, x=x, w1=w1, w2=w2, dout=dout, topk=topk, gate=g, e0=e0, n_local=E,
+                E=E, T=T, K=K, F=F, k=k)
