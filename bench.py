@@ -260,6 +260,30 @@ def mxfp8_forward_compare(torch, reps):
             "note": "weights quantized once outside the timed paths"}
 
 
+def ffn_step_bench(torch, reps, x, w1, w2, topk, gate, dout, E, F, e0):
+    """The routed expert FFN (up-projection, per-token re-quantization of the
+    intermediate, down-projection, combine) forward and backward through both
+    projections: per-step, forward and backward times and the rate of its six
+    grouped GEMMs."""
+    from precision_moe_numerics_nvfp4_amd.layer import ExpertFFNStep
+    T, K = x.shape
+    k = topk.shape[1]
+    L = ExpertFFNStep(T, K, F, E, k, e0=e0)
+    L.quantize_weights(w1, w2)
+    L.forward(x, topk, gate)
+    torch.cuda.synchronize()
+    M = int(L.perm["offsets"][-1].item())
+    t_step = _time(torch, lambda: L.step(x, w1, w2, topk, gate, dout), reps)
+    t_fwd = _time(torch, lambda: L.forward(x, topk, gate), reps)
+    t_bwd = _time(torch, lambda: L.backward(dout, gate), reps)
+    fl = 6 * 2.0 * M * F * K
+    del L
+    return {"routed_rows": M, "ms_per_step": round(t_step, 4), "ms_forward": round(t_fwd, 4),
+            "ms_backward": round(t_bwd, 4), "gemm_TFLOP": round(fl / 1e12, 3),
+            "TFLOP/s": round(fl / t_step / 1e9, 1),
+            "note": "step = weight quantize + forward + backward; six grouped GEMMs"}
+
+
 def tile16_compare(torch, reps):
     import precision_moe_numerics_nvfp4_amd as nv
     from workloads import gen
@@ -316,7 +340,22 @@ def extras(torch, reps=10):
                                   "GB/s": round(T * K * B_QUANT_BF16 / tq / 1e6, 1)},
         "permute_gather": {"ms": round(tp, 4)},
     }
-    del x, w1, w2, h, xq, w1q, hq, perm, y1, y2
+    del h, xq, w1q, w2q, hq, perm, y1, y2
+    torch.cuda.empty_cache()
+    # the whole routed FFN at this shape, forward and backward
+    gate = dev_tensor(gen.gates(3, T, 8), torch)
+    dout = dev_tensor(gen.to_bf16_bits(gen.normal(3, 3, (T, K), std=1e-3)), torch)
+    out["expert_share_ffn_step"] = ffn_step_bench(torch, reps, x, w1, w2, topk, gate, dout, E, F,
+                                                  144)
+    del x, w1, w2, topk, gate, dout
+    torch.cuda.empty_cache()
+    # the same on the small MoE layer's shapes (1024 -> 2048 -> 1024, 8 experts, top-2)
+    c = gen.ffn_case(2, T=4096, K=1024, F=2048, E=8, k=2)
+    out["small_moe_ffn_step"] = ffn_step_bench(
+        torch, reps, dev_tensor(c["x"], torch), dev_tensor(c["w1"].reshape(8 * 2048, 1024), torch),
+        dev_tensor(c["w2"].reshape(8 * 1024, 2048), torch), dev_tensor(c["topk"], torch),
+        dev_tensor(c["gate"], torch), dev_tensor(c["dout"], torch), 8, 2048, 0)
+    del c
     torch.cuda.empty_cache()
     # decode: 512 tokens top-8 uniform over 384, 48 local, weights pre-quantized
     w5 = gen.decode()

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define NVFP4MOE_ABI_VERSION 1
+#define NVFP4MOE_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define NVFP4MOE_API __attribute__((visibility("default")))
@@ -135,6 +135,8 @@ NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int k, int n_loca
  *   padded_offsets[n_local+1] int64, exclusive scan of rows rounded up to 32;
  *   row_token[T*k], row_slot[T*k] int32: row r < offsets[n_local] holds pair
  *     (token, slot); rows of one expert are ordered by t*k+slot ascending;
+ *   pair_row[T*k] int32 (may be NULL): the inverse map, pair_row[t*k+slot] =
+ *     the row holding that pair, or -1 when its expert is not local;
  *   xperm_codes [T*k, K/2], xperm_scales [T*k, K/16], xperm_outer [T*k]: the
  *     NVFP4 row of row_token[r] copied to row r.
  * Entries at or beyond offsets[n_local] are left untouched.
@@ -145,7 +147,7 @@ NVFP4MOE_API int moe_permute(const int32_t* topk_ids, int64_t T, int k, int e0, 
                 const uint8_t* xq_codes, const uint8_t* xq_scales, const float* xq_outer,
                 int64_t K,
                 int64_t* offsets, int64_t* padded_offsets,
-                int32_t* row_token, int32_t* row_slot,
+                int32_t* row_token, int32_t* row_slot, int32_t* pair_row,
                 uint8_t* xperm_codes, uint8_t* xperm_scales, float* xperm_outer,
                 void* workspace, size_t workspace_bytes, void* stream);
 
@@ -298,6 +300,64 @@ NVFP4MOE_API int moe_bwd_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_e8m0,
                   const uint8_t* xT_e4m3, const uint8_t* xT_e8m0,
                   const int64_t* padded_offsets, int G, int64_t P, int64_t N, int64_t K,
                   float* dw, void* stream);
+
+/*
+ * Per-row NVFP4 quantization of the routed rows of a capacity-sized buffer:
+ * the expert FFN's intermediate activation, re-quantized per token before the
+ * down-projection. Pages: "Inkling 2 Small uses four-bit training ..."
+ * (ai-primer), sections "NVFP4 forward, MXFP8 backward" (expert matmuls in
+ * NVFP4) and "Block scales and per-token activations" (one outer scale per
+ * token).
+ *
+ * x [m_cap, cols] float32 or bfloat16; n_live (device, e.g. &offsets[G] of
+ * moe_permute): rows r < min(*n_live, m_cap) are quantized exactly as
+ * nvfp4_quantize does with NVFP4MOE_OUTER_PER_ROW; later rows untouched.
+ * Requires cols % 32 == 0, cols <= 8192, x, codes, scales 16-byte aligned.
+ */
+NVFP4MOE_API int nvfp4_quantize_live(const void* x, int x_dtype, int64_t m_cap, int64_t cols,
+                        const int64_t* n_live, uint8_t* codes, uint8_t* scales, float* outer,
+                        void* stream);
+
+/*
+ * Expert outputs back to token order: weighted sum over each token's routed
+ * pairs (the combine step; with gate == NULL, the un-permute sum of the
+ * backward pass). Pages: "Inkling 2 Small uses four-bit training ..."
+ * (ai-primer), section "Quantized NVLink and BBBK" (expert outputs are
+ * combined back to their tokens; the Hadamard + S2F6 transfer format is a
+ * communication step between GPUs, not part of this call).
+ *
+ * y [m_cap, N] float32 or bfloat16, rows in moe_permute's order; pair_row
+ * [T, k] (device) as written by moe_permute; gate [T, k] float32 or NULL
+ * (all ones).
+ * out[t, n] = sum over j = 0..k-1 with pair_row[t, j] in [0, m_cap) of
+ * gate[t, j] * y[pair_row[t, j], n], float32 fused multiply-adds in slot
+ * order from 0; out [T, N] float32 or bfloat16 (round to nearest even).
+ * Requires m_cap >= 1 when T > 0, N % 8 == 0, k <= 64, T * N / 8 < 2^31, y
+ * and out 16-byte aligned.
+ */
+NVFP4MOE_API int moe_combine(const void* y, int y_dtype, int64_t m_cap, int64_t T, int k,
+                int64_t N, const int32_t* pair_row, const float* gate, void* out,
+                int out_dtype, void* stream);
+
+/*
+ * Backward of moe_combine for the routed rows. Pages: as moe_combine.
+ *
+ * dout [T, N] float32 or bfloat16; row_token, row_slot, offsets[G+1] (device)
+ * as written by moe_permute; gate [T, k] float32 or NULL (ones); y [m_cap, N]
+ * (the forward's expert outputs) or NULL.
+ * For rows r < min(offsets[G], m_cap), with (t, j) = (row_token[r],
+ * row_slot[r]):
+ *   dy[r, n]   = gate[t, j] * dout[t, n] (float32 product; dy float32 or
+ *                bfloat16, round to nearest even);
+ *   dgate[t*k + j] = sum_n dout[t, n] * y[r, n] (float32; only when y is
+ *                given; entries of non-local pairs untouched).
+ * Requires N % 8 == 0 and dout, y, dy 16-byte aligned.
+ */
+NVFP4MOE_API int moe_combine_bwd(const void* dout, int dout_dtype, int64_t T, int k, int64_t N,
+                    const int32_t* row_token, const int32_t* row_slot,
+                    const int64_t* offsets, int G, int64_t m_cap, const float* gate,
+                    const void* y, int y_dtype, void* dy, int dy_dtype, float* dgate,
+                    void* stream);
 
 #ifdef __cplusplus
 }

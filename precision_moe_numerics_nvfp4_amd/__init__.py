@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     lib,
     moe_bwd_dgrad,
     moe_bwd_wgrad,
+    moe_combine,
+    moe_combine_bwd,
     moe_fwd_grouped_gemm,
     moe_fwd_grouped_gemm_mxfp8,
     moe_permute,
@@ -25,6 +27,7 @@ from .binding import (  # noqa: F401
     mxfp8_quantize_dual,
     mxfp8_requant_sr,
     nvfp4_quantize,
+    nvfp4_quantize_live,
     nvfp4_quantize_tile16,
     permute_workspace_size,
     status_string,

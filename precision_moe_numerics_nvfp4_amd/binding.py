@@ -28,7 +28,7 @@ SIGNATURES = {
     "nvfp4_quantize": ([_p, _c_int, _c_i64, _c_i64, _c_int, _c_i64, _p, _p, _p, _p], _c_int),
     "nvfp4moe_permute_workspace_size": ([_c_i64, _c_int, _c_int], _c_size),
     "moe_permute": ([_p, _c_i64, _c_int, _c_int, _c_int, _p, _p, _p, _c_i64, _p, _p, _p, _p,
-                     _p, _p, _p, _p, _c_size, _p], _c_int),
+                     _p, _p, _p, _p, _p, _c_size, _p], _c_int),
     "moe_fwd_grouped_gemm": ([_p, _p, _p, _p, _p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p,
                               _c_int, _p], _c_int),
     "mxfp8_requant_sr": ([_p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p, _p, _c_int, _c_i64,
@@ -44,6 +44,10 @@ SIGNATURES = {
     "nvfp4_quantize_tile16": ([_p, _c_int, _c_i64, _c_i64, _c_i64, _p, _p, _p, _p], _c_int),
     "mxfp8_quantize_dual": ([_p, _c_int, _c_i64, _c_i64, _p, _p, _c_int, _c_i64, _p, _p, _p, _p,
                              _p], _c_int),
+    "nvfp4_quantize_live": ([_p, _c_int, _c_i64, _c_i64, _p, _p, _p, _p, _p], _c_int),
+    "moe_combine": ([_p, _c_int, _c_i64, _c_i64, _c_int, _c_i64, _p, _p, _p, _c_int, _p], _c_int),
+    "moe_combine_bwd": ([_p, _c_int, _c_i64, _c_int, _c_i64, _p, _p, _p, _c_int, _c_i64, _p, _p,
+                         _c_int, _p, _c_int, _p, _p], _c_int),
 }
 
 _LIB = None
@@ -162,8 +166,10 @@ def moe_permute(topk_ids, e0, n_local, xq_codes, xq_scales, xq_outer, workspace=
     """Group routed (token, slot) pairs by local expert and gather NVFP4 rows.
 
     Returns a dict with offsets, padded_offsets (int64 [n_local+1]), row_token,
-    row_slot (int32 [T*k]) and codes/scales/outer of the permuted rows
-    (capacity T*k rows; rows >= offsets[-1] are not written)."""
+    row_slot (int32 [T*k]), pair_row (int32 [T, k], the row of each pair or
+    -1) and codes/scales/outer of the permuted rows (capacity T*k rows; rows
+    >= offsets[-1] are not written). An ``out`` dict without "pair_row" asks
+    for no inverse map."""
     torch = _torch()
     _dev(topk_ids, "topk_ids", torch.int32, 2)
     T, k = topk_ids.shape
@@ -174,6 +180,8 @@ def moe_permute(topk_ids, e0, n_local, xq_codes, xq_scales, xq_outer, workspace=
     dev = topk_ids.device
     cap = T * k
     o = dict(out or {})
+    if out is None:
+        o["pair_row"] = torch.empty((T, k), dtype=torch.int32, device=dev)
     o.setdefault("offsets", torch.empty((n_local + 1,), dtype=torch.int64, device=dev))
     o.setdefault("padded_offsets", torch.empty((n_local + 1,), dtype=torch.int64, device=dev))
     o.setdefault("row_token", torch.empty((cap,), dtype=torch.int32, device=dev))
@@ -187,7 +195,7 @@ def moe_permute(topk_ids, e0, n_local, xq_codes, xq_scales, xq_outer, workspace=
     st = lib().moe_permute(_ptr(topk_ids), T, k, int(e0), int(n_local), _ptr(xq_codes),
                            _ptr(xq_scales), _ptr(xq_outer), K, _ptr(o["offsets"]),
                            _ptr(o["padded_offsets"]), _ptr(o["row_token"]), _ptr(o["row_slot"]),
-                           _ptr(o["codes"]), _ptr(o["scales"]), _ptr(o["outer"]),
+                           _ptr(o.get("pair_row")), _ptr(o["codes"]), _ptr(o["scales"]), _ptr(o["outer"]),
                            _ptr(workspace), workspace.numel(), _stream(topk_ids))
     _check("moe_permute", st)
     return o
@@ -400,3 +408,76 @@ def nvfp4_quantize_tile16(x, rows_per_group=None, codes=None, scales=None, outer
                                      _ptr(scales), _ptr(outer), _stream(x))
     _check("nvfp4_quantize_tile16", st)
     return codes, scales, outer
+
+
+def nvfp4_quantize_live(x, offsets, codes=None, scales=None, outer=None):
+    """Per-row NVFP4 of the routed rows r < offsets[-1] of x [m_cap, cols]
+    (bf16|f32): (codes [m_cap, cols/2], scales [m_cap, cols/16], outer
+    [m_cap]); later rows untouched."""
+    torch = _torch()
+    _dev(x, "x", ndim=2)
+    _dev(offsets, "offsets", torch.int64, 1)
+    rows, cols = x.shape
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    if outer is None:
+        outer = torch.empty((rows,), dtype=torch.float32, device=dev)
+    st = lib().nvfp4_quantize_live(_ptr(x), _in_dtype(x), rows, cols, _ptr(offsets[-1:]),
+                                   _ptr(codes), _ptr(scales), _ptr(outer), _stream(x))
+    _check("nvfp4_quantize_live", st)
+    return codes, scales, outer
+
+
+def moe_combine(y, pair_row, gate=None, out_dtype=None, out=None):
+    """out [T, N] = sum_j gate[t, j] * y[pair_row[t, j]] (gate None: ones).
+    y [m_cap, N] bf16|f32; pair_row int32 [T, k]; gate f32 [T, k]."""
+    torch = _torch()
+    _dev(y, "y", ndim=2)
+    _dev(pair_row, "pair_row", torch.int32, 2)
+    if gate is not None:
+        _dev(gate, "gate", torch.float32, 2)
+        if tuple(gate.shape) != tuple(pair_row.shape):
+            raise ValueError("gate and pair_row must have the same shape")
+    T, k = pair_row.shape
+    N = y.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=out_dtype or y.dtype, device=y.device)
+    _dev(out, "out", ndim=2)
+    st = lib().moe_combine(_ptr(y), _in_dtype(y), y.shape[0], T, k, N, _ptr(pair_row),
+                           _ptr(gate), _ptr(out), _out_dtype(out.dtype), _stream(y))
+    _check("moe_combine", st)
+    return out
+
+
+def moe_combine_bwd(dout, row_token, row_slot, offsets, k, gate=None, y=None, dy=None,
+                    dgate=None, dy_dtype=None, m_cap=None):
+    """Backward of moe_combine for the routed rows: (dy [m_cap, N], dgate
+    [T, k] or None). dout [T, N]; y [m_cap, N] (the forward's expert outputs)
+    or None; rows >= offsets[-1] of dy and non-local dgate entries untouched."""
+    torch = _torch()
+    _dev(dout, "dout", ndim=2)
+    _dev(row_token, "row_token", torch.int32, 1)
+    _dev(row_slot, "row_slot", torch.int32, 1)
+    _dev(offsets, "offsets", torch.int64, 1)
+    T, N = dout.shape
+    if m_cap is None:
+        m_cap = row_token.shape[0] if dy is None else dy.shape[0]
+    if dy is None:
+        dy = torch.empty((m_cap, N), dtype=dy_dtype or dout.dtype, device=dout.device)
+    _dev(dy, "dy", ndim=2)
+    if gate is not None:
+        _dev(gate, "gate", torch.float32, 2)
+    if y is not None:
+        _dev(y, "y", ndim=2)
+        if dgate is None:
+            dgate = torch.zeros((T, k), dtype=torch.float32, device=dout.device)
+    G = offsets.shape[0] - 1
+    st = lib().moe_combine_bwd(_ptr(dout), _in_dtype(dout), T, int(k), N, _ptr(row_token),
+                               _ptr(row_slot), _ptr(offsets), G, int(m_cap), _ptr(gate), _ptr(y),
+                               _in_dtype(y) if y is not None else NVFP4MOE_F32, _ptr(dy),
+                               _out_dtype(dy.dtype), _ptr(dgate), _stream(dout))
+    _check("moe_combine_bwd", st)
+    return dy, dgate

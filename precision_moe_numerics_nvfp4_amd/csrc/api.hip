@@ -69,8 +69,9 @@ size_t nvfp4moe_permute_workspace_size(int64_t T, int k, int n_local) {
 int moe_permute(const int32_t* topk_ids, int64_t T, int k, int e0, int n_local,
                 const uint8_t* xq_codes, const uint8_t* xq_scales, const float* xq_outer,
                 int64_t K, int64_t* offsets, int64_t* padded_offsets, int32_t* row_token,
-                int32_t* row_slot, uint8_t* xperm_codes, uint8_t* xperm_scales,
-                float* xperm_outer, void* workspace, size_t workspace_bytes, void* stream) {
+                int32_t* row_slot, int32_t* pair_row, uint8_t* xperm_codes,
+                uint8_t* xperm_scales, float* xperm_outer, void* workspace,
+                size_t workspace_bytes, void* stream) {
   REQUIRE(T >= 0 && K >= 0 && k > 0 && n_local > 0, NVFP4MOE_EINVAL);
   REQUIRE(offsets && padded_offsets && workspace, NVFP4MOE_EINVAL);
   if (T > 0)
@@ -84,7 +85,7 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int k, int e0, int n_local,
   REQUIRE(aligned16(xq_codes) && aligned16(xperm_codes) && aligned16(workspace),
           NVFP4MOE_EUNSUPPORTED);
   return hip_status(launch_permute(topk_ids, T, k, e0, n_local, xq_codes, xq_scales, xq_outer,
-                                   K, offsets, padded_offsets, row_token, row_slot, xperm_codes,
+                                   K, offsets, padded_offsets, row_token, row_slot, pair_row, xperm_codes,
                                    xperm_scales, xperm_outer, workspace, as_stream(stream)));
 }
 
@@ -240,6 +241,53 @@ int mxfp8_gather_rows(const int32_t* row_token, const int64_t* offsets, int G, i
   REQUIRE(aligned16(src_e4m3) && aligned16(dst_e4m3), NVFP4MOE_EUNSUPPORTED);
   return hip_status(launch_gather_rows(row_token, offsets, G, m_cap, src_rows, src_e4m3, src_e8m0,
                                        K, K / 32, dst_e4m3, dst_e8m0, as_stream(stream)));
+}
+
+int nvfp4_quantize_live(const void* x, int x_dtype, int64_t m_cap, int64_t cols,
+                        const int64_t* n_live, uint8_t* codes, uint8_t* scales, float* outer,
+                        void* stream) {
+  REQUIRE(m_cap >= 0 && cols >= 0, NVFP4MOE_EINVAL);
+  REQUIRE(x_dtype == NVFP4MOE_F32 || x_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (m_cap == 0) return NVFP4MOE_OK;
+  REQUIRE(x && n_live && codes && scales && outer, NVFP4MOE_EINVAL);
+  REQUIRE(cols > 0 && cols % 32 == 0 && cols <= 8192, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(x) && aligned16(codes) && aligned16(scales), NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_nvfp4_quantize_live(x, x_dtype == NVFP4MOE_BF16, m_cap, cols, n_live,
+                                               codes, scales, outer, as_stream(stream)));
+}
+
+int moe_combine(const void* y, int y_dtype, int64_t m_cap, int64_t T, int k, int64_t N,
+                const int32_t* pair_row, const float* gate, void* out, int out_dtype,
+                void* stream) {
+  REQUIRE(m_cap >= 0 && T >= 0 && N >= 0 && k > 0, NVFP4MOE_EINVAL);
+  REQUIRE(y_dtype == NVFP4MOE_F32 || y_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  REQUIRE(out_dtype == NVFP4MOE_F32 || out_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (T == 0 || N == 0) return NVFP4MOE_OK;
+  REQUIRE(m_cap > 0 && y && pair_row && out, NVFP4MOE_EINVAL);
+  REQUIRE(N % 8 == 0 && k <= 64, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(T * (N / 8) < ((int64_t)1 << 31), NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(y) && aligned16(out), NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_combine(y, y_dtype == NVFP4MOE_BF16, m_cap, T, k, N, pair_row, gate,
+                                   out, out_dtype == NVFP4MOE_BF16, as_stream(stream)));
+}
+
+int moe_combine_bwd(const void* dout, int dout_dtype, int64_t T, int k, int64_t N,
+                    const int32_t* row_token, const int32_t* row_slot, const int64_t* offsets,
+                    int G, int64_t m_cap, const float* gate, const void* y, int y_dtype,
+                    void* dy, int dy_dtype, float* dgate, void* stream) {
+  REQUIRE(T >= 0 && N >= 0 && k > 0 && G >= 0 && m_cap >= 0, NVFP4MOE_EINVAL);
+  REQUIRE(dout_dtype == NVFP4MOE_F32 || dout_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  REQUIRE(dy_dtype == NVFP4MOE_F32 || dy_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (y) REQUIRE(y_dtype == NVFP4MOE_F32 || y_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (G == 0 || m_cap == 0 || N == 0) return NVFP4MOE_OK;
+  REQUIRE(dout && row_token && row_slot && offsets && dy, NVFP4MOE_EINVAL);
+  if (y) REQUIRE(dgate != nullptr, NVFP4MOE_EINVAL);
+  REQUIRE(N % 8 == 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(dout) && aligned16(dy) && aligned16(y), NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_combine_bwd(dout, dout_dtype == NVFP4MOE_BF16, N, k, row_token,
+                                       row_slot, offsets, G, m_cap, gate, y,
+                                       y_dtype == NVFP4MOE_BF16, dy, dy_dtype == NVFP4MOE_BF16,
+                                       dgate, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -20,13 +20,28 @@ hipError_t launch_mxfp8_quantize_rowwise(const void* x, bool bf16, int64_t rows,
                                          uint8_t* out_e4m3, uint8_t* out_e8m0,
                                          hipStream_t stream);
 
+hipError_t launch_nvfp4_quantize_live(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                      const int64_t* n_live, uint8_t* codes, uint8_t* scales,
+                                      float* outer, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(const void* y, bool y_bf16, int64_t m_cap, int64_t T, int k,
+                          int64_t N, const int32_t* pair_row, const float* gate, void* out,
+                          bool out_bf16, hipStream_t stream);
+hipError_t launch_combine_bwd(const void* dout, bool dout_bf16, int64_t N, int k,
+                              const int32_t* row_token, const int32_t* row_slot,
+                              const int64_t* offsets, int G, int64_t m_cap, const float* gate,
+                              const void* y, bool y_bf16, void* dy, bool dy_bf16, float* dgate,
+                              hipStream_t stream);
+
 // permute.hip
 size_t permute_workspace_bytes(int64_t T, int k, int n_local);
 hipError_t launch_permute(const int32_t* topk_ids, int64_t T, int k, int e0, int n_local,
                           const uint8_t* xq_codes, const uint8_t* xq_scales,
                           const float* xq_outer, int64_t K, int64_t* offsets,
                           int64_t* padded_offsets, int32_t* row_token, int32_t* row_slot,
-                          uint8_t* xperm_codes, uint8_t* xperm_scales, float* xperm_outer,
+                          int32_t* pair_row, uint8_t* xperm_codes, uint8_t* xperm_scales,
+                          float* xperm_outer,
                           void* workspace, hipStream_t stream);
 
 // requant.hip: grouped-transpose MXFP8 quantizers

@@ -144,8 +144,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs,
     const float* __restrict__ qo, int64_t K, int64_t* __restrict__ offsets,
     int64_t* __restrict__ padded, int32_t* __restrict__ row_token,
-    int32_t* __restrict__ row_slot, uint8_t* __restrict__ pc, uint8_t* __restrict__ ps,
-    float* __restrict__ po) {
+    int32_t* __restrict__ row_slot, int32_t* __restrict__ pair_row, uint8_t* __restrict__ pc,
+    uint8_t* __restrict__ ps, float* __restrict__ po) {
   __shared__ int32_t tot[1024];   // pairs per local expert, all of them
   __shared__ int32_t pre[1024];   // pairs per local expert before this workgroup's
   __shared__ int32_t list_dst[kSmallChunk];
@@ -240,8 +240,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
       peers &= bit ? bal : ~bal;
     }
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int pos = -1;
     if (valid) {
-      const int pos = pre[le] + __popcll(peers & below);
+      pos = pre[le] + __popcll(peers & below);
       const int32_t t = (int32_t)(f / k);
       row_token[pos] = t;
       row_slot[pos] = (int32_t)(f % k);
@@ -249,6 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
       list_dst[slot] = pos;
       list_src[slot] = t;
     }
+    if (pair_row && f < n) pair_row[f] = pos;
     if (lane == 0) nv_sh = __popcll(vmask);
   }
   __syncthreads();
@@ -373,8 +375,9 @@ __global__ __launch_bounds__(256) void k_scatter_copy(
     const int32_t* __restrict__ ids, int64_t n, int k, int e0, int n_local, int nbits,
     int64_t n_chunks, const int32_t* __restrict__ ws, const uint8_t* __restrict__ qc,
     const uint8_t* __restrict__ qs, const float* __restrict__ qo, int64_t K,
-    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot, uint8_t* __restrict__ pc,
-    uint8_t* __restrict__ ps, float* __restrict__ po) {
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ pair_row, uint8_t* __restrict__ pc, uint8_t* __restrict__ ps,
+    float* __restrict__ po) {
   __shared__ int32_t base[1024];
   __shared__ int32_t wcnt[4][1024];     // pairs per expert in each wavefront
   __shared__ int32_t list_dst[kChunk];  // compacted (output row, token) of routed pairs
@@ -402,8 +405,9 @@ __global__ __launch_bounds__(256) void k_scatter_copy(
   if (valid && (peers & below) == 0) wcnt[w][le] = __popcll(peers);   // lowest lane of its expert
   if (lane == 0) wvalid[w] = __popcll(vmask);
   __syncthreads();
+  int pos = -1;
   if (valid) {
-    int pos = base[le] + __popcll(peers & below);
+    pos = base[le] + __popcll(peers & below);
     for (int i = 0; i < w; ++i) pos += wcnt[i][le];
     const int32_t t = (int32_t)(f / k);
     row_token[pos] = t;
@@ -413,6 +417,7 @@ __global__ __launch_bounds__(256) void k_scatter_copy(
     list_dst[slot] = pos;
     list_src[slot] = t;
   }
+  if (pair_row && f < n) pair_row[f] = pos;
   __syncthreads();
 
   copy_rows<SC16>(wvalid[0] + wvalid[1] + wvalid[2] + wvalid[3], list_dst, list_src, qc, qs, qo,
@@ -473,8 +478,8 @@ size_t permute_workspace_bytes(int64_t T, int k, int n_local) {
 hipError_t launch_permute(const int32_t* ids, int64_t T, int k, int e0, int n_local,
                           const uint8_t* qc, const uint8_t* qs, const float* qo, int64_t K,
                           int64_t* offsets, int64_t* padded, int32_t* row_token,
-                          int32_t* row_slot, uint8_t* pc, uint8_t* ps, float* po,
-                          void* workspace, hipStream_t stream) {
+                          int32_t* row_slot, int32_t* pair_row, uint8_t* pc, uint8_t* ps,
+                          float* po, void* workspace, hipStream_t stream) {
   const int64_t n = T * k;
   int nbits = 0;
   while ((1 << nbits) < n_local) ++nbits;
@@ -485,11 +490,11 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int k, int e0, int n_lo
     if (sc16)
       k_permute_small<true><<<grid, 256, 0, stream>>>(ids, n, k, e0, n_local, nbits, qc, qs, qo,
                                                       K, offsets, padded, row_token, row_slot,
-                                                      pc, ps, po);
+                                                      pair_row, pc, ps, po);
     else
       k_permute_small<false><<<grid, 256, 0, stream>>>(ids, n, k, e0, n_local, nbits, qc, qs, qo,
                                                        K, offsets, padded, row_token, row_slot,
-                                                       pc, ps, po);
+                                                       pair_row, pc, ps, po);
     return hipGetLastError();
   }
   const int64_t n_chunks = (n + kChunk - 1) / kChunk;
@@ -501,12 +506,12 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int k, int e0, int n_lo
   if (n_chunks > 0) {
     if (sc16)
       k_scatter_copy<true><<<(unsigned)n_chunks, 256, 0, stream>>>(
-          ids, n, k, e0, n_local, nbits, n_chunks, ws, qc, qs, qo, K, row_token, row_slot, pc,
-          ps, po);
+          ids, n, k, e0, n_local, nbits, n_chunks, ws, qc, qs, qo, K, row_token, row_slot,
+          pair_row, pc, ps, po);
     else
       k_scatter_copy<false><<<(unsigned)n_chunks, 256, 0, stream>>>(
-          ids, n, k, e0, n_local, nbits, n_chunks, ws, qc, qs, qo, K, row_token, row_slot, pc,
-          ps, po);
+          ids, n, k, e0, n_local, nbits, n_chunks, ws, qc, qs, qo, K, row_token, row_slot,
+          pair_row, pc, ps, po);
   }
   return hipGetLastError();
 }

@@ -50,17 +50,14 @@ __device__ __forceinline__ void load16(const void* base, int64_t elem, Row16<BF1
   }
 }
 
-// One wavefront per row, 4 rows per workgroup; lane l owns blocks l, l+64, ...
+// One wavefront per row; lane l owns blocks l, l+64, ...
 // gamax != nullptr: per-group mode, A is read from the group-max pass.
 template <bool BF16, int BPL>
-__global__ __launch_bounds__(256) void k_nvfp4_quantize(
-    const void* __restrict__ x, int64_t rows, int nb, const uint32_t* __restrict__ gamax,
+__device__ __forceinline__ void quantize_row(
+    const void* __restrict__ x, int64_t row, int nb, const uint32_t* __restrict__ gamax,
     int64_t rpg, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ outer) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;  // uniform per wavefront
-
   Row16<BF16> v[BPL];
   float bmax[BPL];
   float amax = 0.0f;
@@ -108,6 +105,30 @@ __global__ __launch_bounds__(256) void k_nvfp4_quantize(
     *reinterpret_cast<uint2*>(codes + blk * 8) = make_uint2(lo, hi);
     scales[blk] = (uint8_t)sc;
   }
+}
+
+// 4 rows per workgroup, one per wavefront.
+template <bool BF16, int BPL>
+__global__ __launch_bounds__(256) void k_nvfp4_quantize(
+    const void* __restrict__ x, int64_t rows, int nb, const uint32_t* __restrict__ gamax,
+    int64_t rpg, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ outer) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // uniform per wavefront
+  quantize_row<BF16, BPL>(x, row, nb, gamax, rpg, codes, scales, outer);
+}
+
+// Per-row outer scales for the first *n_live rows of a capacity-sized
+// buffer (the count is device data, so the grid walks the rows).
+template <bool BF16, int BPL>
+__global__ __launch_bounds__(256) void k_nvfp4_quantize_live(
+    const void* __restrict__ x, int64_t rows, const int64_t* __restrict__ n_live, int nb,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer) {
+  const int64_t live = *n_live;
+  const int64_t n = live < rows ? live : rows;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < n;
+       row += (int64_t)gridDim.x * 4)
+    quantize_row<BF16, BPL>(x, row, nb, nullptr, 1, codes, scales, outer);
 }
 
 // 16x16-tile NVFP4 (one E4M3 scale per tile, outer scale per group of rows):
@@ -329,6 +350,33 @@ hipError_t launch_nvfp4_quantize(const void* x, bool bf16, int64_t rows, int64_t
                                  float* outer, hipStream_t stream) {
   return bf16 ? quantize_impl<true>(x, rows, cols, per_group, rpg, codes, scales, outer, stream)
               : quantize_impl<false>(x, rows, cols, per_group, rpg, codes, scales, outer, stream);
+}
+
+template <bool BF16>
+static hipError_t quantize_live_impl(const void* x, int64_t rows, int64_t cols,
+                                     const int64_t* n_live, uint8_t* codes, uint8_t* scales,
+                                     float* outer, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int nb = (int)(cols / 16);
+  int64_t grid = (rows + 3) / 4;
+  const int64_t most = (int64_t)device_cu_count() * 16;   // 16 workgroups per CU at most
+  if (grid > most) grid = most;
+  if (nb <= 64)
+    k_nvfp4_quantize_live<BF16, 1><<<(unsigned)grid, 256, 0, stream>>>(x, rows, n_live, nb, codes, scales, outer);
+  else if (nb <= 128)
+    k_nvfp4_quantize_live<BF16, 2><<<(unsigned)grid, 256, 0, stream>>>(x, rows, n_live, nb, codes, scales, outer);
+  else if (nb <= 256)
+    k_nvfp4_quantize_live<BF16, 4><<<(unsigned)grid, 256, 0, stream>>>(x, rows, n_live, nb, codes, scales, outer);
+  else
+    k_nvfp4_quantize_live<BF16, 8><<<(unsigned)grid, 256, 0, stream>>>(x, rows, n_live, nb, codes, scales, outer);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize_live(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                      const int64_t* n_live, uint8_t* codes, uint8_t* scales,
+                                      float* outer, hipStream_t stream) {
+  return bf16 ? quantize_live_impl<true>(x, rows, cols, n_live, codes, scales, outer, stream)
+              : quantize_live_impl<false>(x, rows, cols, n_live, codes, scales, outer, stream);
 }
 
 template <bool BF16>

@@ -99,3 +99,100 @@ class ExpertLayerStep:
         self.quantize_dy(dy)
         self.dgrad()
         self.wgrad()
+
+
+class ExpertFFNStep:
+    """The routed expert FFN around the layer: up-projection W1 [E, F, K],
+    per-token NVFP4 re-quantization of the intermediate H, down-projection
+    W2 [E, K, F], weighted combine back to token order; and the backward
+    through both projections, the MXFP8 path of each. The nonlinearity
+    between the projections is the caller's and is not applied here.
+
+    Philox streams: tag 0 = X_perm, 1 = W1, 3 = H, 4 = W2. Stored precisions:
+    H, Y2, dY2, dH, dX_perm, the output and dX are bfloat16; dW1, dW2 and the
+    routing-weight gradient are float32."""
+
+    def __init__(self, T, K, F, E, k, e0=0, seed=0x5EED0002, device="cuda"):
+        self.T, self.K, self.F, self.E, self.k, self.e0 = T, K, F, E, k, e0
+        self.seed = seed
+        dev = torch.device(device)
+        u8, f32, i64, bf = torch.uint8, torch.float32, torch.int64, torch.bfloat16
+        cap = T * k
+        self.m_cap = cap
+        self.P = ((cap + 31 * E + 31) // 32) * 32
+        P = self.P
+        e = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=dev)
+        nvfp4 = lambda r, c, n_outer: (e(r, c // 2), e(r, c // 16), e(n_outer, dt=f32))
+        mx = lambda r, c: (e(r, c), e(r, c // 32))
+        # forward
+        self.xq = nvfp4(T, K, T)
+        self.w1q = nvfp4(E * F, K, E)
+        self.w2q = nvfp4(E * K, F, E)
+        self.perm = dict(offsets=e(E + 1, dt=i64), padded_offsets=e(E + 1, dt=i64),
+                         row_token=e(cap, dt=torch.int32), row_slot=e(cap, dt=torch.int32),
+                         pair_row=e(T, k, dt=torch.int32),
+                         codes=e(cap, K // 2), scales=e(cap, K // 16), outer=e(cap, dt=f32))
+        self.ws = e(B.permute_workspace_size(T, k, E))
+        self.h = e(cap, F, dt=bf)
+        self.hq = nvfp4(cap, F, cap)
+        self.y2 = e(cap, K, dt=bf)
+        self.out = e(T, K, dt=bf)
+        # backward
+        self.w_off1 = torch.arange(E + 1, dtype=i64, device=dev) * F
+        self.w_off2 = torch.arange(E + 1, dtype=i64, device=dev) * K
+        self.dy2 = e(cap, K, dt=bf)
+        self.dgate = torch.zeros((T, k), dtype=f32, device=dev)
+        self.dy2_8, self.dy2T = mx(cap, K), mx(K, P)
+        self.hT, self.w2T = mx(F, P), mx(F, E * K)
+        self.dh = e(cap, F, dt=bf)
+        self.dh8, self.dhT = mx(cap, F), mx(F, P)
+        self.xT, self.w1T = mx(K, P), mx(K, E * F)
+        self.dxp = e(cap, K, dt=bf)
+        self.dw1 = e(E, F, K, dt=f32)
+        self.dw2 = e(E, K, F, dt=f32)
+        self.dx = e(T, K, dt=bf)
+
+    def quantize_weights(self, w1, w2):
+        """w1 [E*F, K], w2 [E*K, F] (bf16|f32), one outer scale per expert."""
+        B.nvfp4_quantize(w1, self.F, *self.w1q)
+        B.nvfp4_quantize(w2, self.K, *self.w2q)
+
+    def forward(self, x, topk_ids, gate):
+        p = self.perm
+        B.nvfp4_quantize(x, None, *self.xq)
+        B.moe_permute(topk_ids, self.e0, self.E, *self.xq, workspace=self.ws, out=p)
+        B.moe_fwd_grouped_gemm(p["codes"], p["scales"], p["outer"], *self.w1q, p["offsets"],
+                               y=self.h)
+        B.nvfp4_quantize_live(self.h, p["offsets"], *self.hq)
+        B.moe_fwd_grouped_gemm(*self.hq, *self.w2q, p["offsets"], y=self.y2)
+        B.moe_combine(self.y2, p["pair_row"], gate, out=self.out)
+        return self.out
+
+    def backward(self, dout, gate):
+        p = self.perm
+        off, poff, P, s = p["offsets"], p["padded_offsets"], self.P, self.seed
+        B.moe_combine_bwd(dout, p["row_token"], p["row_slot"], off, self.k, gate=gate, y=self.y2,
+                          dy=self.dy2, dgate=self.dgate)
+        # down-projection
+        B.mxfp8_quantize_dual(self.dy2, off, poff, P, row_out=self.dy2_8, col_out=self.dy2T)
+        B.mxfp8_requant_sr(*self.hq, off, poff, P, s, 3, out=self.hT[0], out_e8=self.hT[1])
+        B.mxfp8_requant_sr(*self.w2q, self.w_off2, self.w_off2, self.E * self.K, s, 4,
+                           rows_per_group=self.K, out=self.w2T[0], out_e8=self.w2T[1])
+        B.moe_bwd_dgrad(*self.dy2_8, *self.w2T, off, self.K, self.F, dx=self.dh)
+        B.moe_bwd_wgrad(*self.dy2T, *self.hT, poff, self.K, self.F, dw=self.dw2)
+        # up-projection
+        B.mxfp8_quantize_dual(self.dh, off, poff, P, row_out=self.dh8, col_out=self.dhT)
+        B.mxfp8_requant_sr(p["codes"], p["scales"], p["outer"], off, poff, P, s, 0,
+                           out=self.xT[0], out_e8=self.xT[1])
+        B.mxfp8_requant_sr(*self.w1q, self.w_off1, self.w_off1, self.E * self.F, s, 1,
+                           rows_per_group=self.F, out=self.w1T[0], out_e8=self.w1T[1])
+        B.moe_bwd_dgrad(*self.dh8, *self.w1T, off, self.F, self.K, dx=self.dxp)
+        B.moe_bwd_wgrad(*self.dhT, *self.xT, poff, self.F, self.K, dw=self.dw1)
+        B.moe_combine(self.dxp, p["pair_row"], None, out=self.dx)
+        return self.dx
+
+    def step(self, x, w1, w2, topk_ids, gate, dout):
+        """Forward and backward once, weights quantized in the step."""
+        self.quantize_weights(w1, w2)
+        self.forward(x, topk_ids, gate)
+        self.backward(dout, gate)

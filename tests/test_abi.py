@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     from precision_moe_numerics_nvfp4_amd import binding
-    assert L.nvfp4moe_abi_version() == 1
+    assert L.nvfp4moe_abi_version() == 2
     for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported size or alignment"),
                     (3, "workspace too small"), (4, "HIP launch or runtime error"), (99, "unknown status")]:
         assert binding.status_string(s) == text
@@ -119,13 +119,39 @@ def test_gemm_and_requant_argument_errors(L):
 def test_permute_argument_errors(L):
     p = L.moe_permute
     args = lambda T, k, nl, K, ws, wsb: (FAKE, T, k, 0, nl, FAKE, FAKE, FAKE, K, FAKE, FAKE, FAKE,
-                                         FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+                                         FAKE, None, FAKE, FAKE, FAKE, ws, wsb, None)
     need = L.nvfp4moe_permute_workspace_size(100, 2, 8)
     assert p(*args(100, 2, 8, 256, FAKE, need - 1)) == EWS
     assert p(*args(100, 2, 8, 48, FAKE, need)) == EUNSUP
     assert p(*args(100, 2, 2000, 256, FAKE, 1 << 30)) == EUNSUP
     assert p(*args(100, 0, 8, 256, FAKE, need)) == EINVAL
     assert p(*args(100, 2, 8, 256, None, need)) == EINVAL
+
+
+def test_ffn_entry_argument_errors(L):
+    ql = L.nvfp4_quantize_live
+    assert ql(FAKE, 1, 64, 256, None, FAKE, FAKE, FAKE, None) == EINVAL            # n_live
+    assert ql(FAKE, 1, 64, 48, FAKE, FAKE, FAKE, FAKE, None) == EUNSUP             # cols % 32
+    assert ql(FAKE, 1, 64, 16384, FAKE, FAKE, FAKE, FAKE, None) == EUNSUP          # cols > 8192
+    assert ql(FAKE, 7, 64, 256, FAKE, FAKE, FAKE, FAKE, None) == EINVAL            # dtype
+    assert ql(None, 1, 0, 256, None, None, None, None, None) == 0                  # empty
+    c = L.moe_combine
+    assert c(FAKE, 1, 64, 32, 2, 256, None, None, FAKE, 1, None) == EINVAL         # pair_row
+    assert c(FAKE, 1, 0, 32, 2, 256, FAKE, None, FAKE, 1, None) == EINVAL          # m_cap 0
+    assert c(FAKE, 1, 64, 32, 2, 252, FAKE, None, FAKE, 1, None) == EUNSUP         # N % 8
+    assert c(FAKE, 1, 64, 32, 65, 256, FAKE, None, FAKE, 1, None) == EUNSUP        # k > 64
+    assert c(FAKE, 1, 64, 32, 0, 256, FAKE, None, FAKE, 1, None) == EINVAL         # k 0
+    assert c(FAKE, 1, 64, 32, 2, 256, FAKE, None, FAKE, 5, None) == EINVAL         # out dtype
+    assert c(None, 1, 0, 0, 2, 256, None, None, None, 1, None) == 0                # no tokens
+    b = L.moe_combine_bwd
+    assert b(FAKE, 1, 32, 2, 256, FAKE, FAKE, None, 2, 64, None, None, 0, FAKE, 1, None,
+             None) == EINVAL                                                        # offsets
+    assert b(FAKE, 1, 32, 2, 256, FAKE, FAKE, FAKE, 2, 64, None, FAKE, 1, FAKE, 1, None,
+             None) == EINVAL                                                        # y without dgate
+    assert b(FAKE, 1, 32, 2, 250, FAKE, FAKE, FAKE, 2, 64, None, None, 0, FAKE, 1, None,
+             None) == EUNSUP                                                        # N % 8
+    assert b(FAKE, 1, 32, 2, 256, FAKE, FAKE, FAKE, 0, 64, None, None, 0, FAKE, 1, None,
+             None) == 0                                                             # no groups
 
 
 def test_binding_rejects_host_tensors():

@@ -26,6 +26,7 @@ import numpy as np
 import pytest
 
 from helpers import assert_gemm_close, ensure_built, from_dev, to_dev
+from oracle import ffn as FF
 from oracle import formats as F
 from oracle import gemm as GM
 from oracle import mxfp8 as MX
@@ -197,6 +198,8 @@ def test_moe_permute(nv, case, K):
     assert np.array_equal(from_dev(o["padded_offsets"]), pad)
     assert np.array_equal(from_dev(o["row_token"])[:M], rt)
     assert np.array_equal(from_dev(o["row_slot"])[:M], rs)
+    if T:
+        assert np.array_equal(from_dev(o["pair_row"]), FF.pair_rows(topk, e0, nl))
     if M:
         gc, gs, go = PM.gather_rows(rt, xc, xs, xo)
         assert np.array_equal(from_dev(o["codes"])[:M], gc)
