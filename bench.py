@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", choices=["ffn-share", "ffn-small"], default=None,
+                    help="time one routed-FFN workload alone and print its record "
+                         "(for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="0 skips the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run three 256 MiB device copies (the known-size reference for "
@@ -284,6 +287,26 @@ def ffn_step_bench(torch, reps, x, w1, w2, topk, gate, dout, E, F, e0):
             "note": "step = weight quantize + forward + backward; six grouped GEMMs"}
 
 
+def ffn_workload(torch, name, reps):
+    """ffn_step_bench on the expert share ("ffn-share": 48 of 384 experts,
+    32768 tokens top-8 Zipf, 4096 -> 1536 -> 4096) or on the small MoE layer's
+    shapes ("ffn-small": 4096 tokens top-2 over 8, 1024 -> 2048 -> 1024)."""
+    from workloads import gen
+    if name == "ffn-share":
+        w3 = gen.expert_share()
+        T, K, F, E = w3["T"], w3["K"], w3["N"], w3["E"]
+        args = (dev_tensor(w3["x"], torch), dev_tensor(w3["w1"], torch),
+                dev_tensor(w3["w2"], torch), dev_tensor(w3["topk"], torch),
+                dev_tensor(gen.gates(3, T, 8), torch),
+                dev_tensor(gen.to_bf16_bits(gen.normal(3, 3, (T, K), std=1e-3)), torch))
+        return ffn_step_bench(torch, reps, *args, E, F, 144)
+    c = gen.ffn_case(2, T=4096, K=1024, F=2048, E=8, k=2)
+    return ffn_step_bench(
+        torch, reps, dev_tensor(c["x"], torch), dev_tensor(c["w1"].reshape(8 * 2048, 1024), torch),
+        dev_tensor(c["w2"].reshape(8 * 1024, 2048), torch), dev_tensor(c["topk"], torch),
+        dev_tensor(c["gate"], torch), dev_tensor(c["dout"], torch), 8, 2048, 0)
+
+
 def tile16_compare(torch, reps):
     import precision_moe_numerics_nvfp4_amd as nv
     from workloads import gen
@@ -479,6 +502,9 @@ def main():
     if not os.path.exists(binding.LIB_PATH):
         from precision_moe_numerics_nvfp4_amd import build as _b
         _b.build()
+    if args.only:
+        print(json.dumps({args.only: ffn_workload(torch, args.only, max(args.steps, 1))}))
+        return
     print("bench: small MoE layer step", file=sys.stderr, flush=True)
     r = main_step_bench(args, torch)
     line = {

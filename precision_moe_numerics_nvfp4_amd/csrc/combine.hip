@@ -6,8 +6,9 @@
 // combine_bwd:  dy[r, :] = gate[t, j] * dout[t, :] for the routed rows, and
 //               dgate[t, j] = sum_n dout[t, n] * y[r, n].
 // Both are streaming kernels: 16-byte accesses along rows, every load of a
-// round issued before its first use (indices clamped, weights zeroed), so
-// nothing waits on a branch.
+// round issued before its first use. A pair that is not local still issues
+// its load, from the first 16 bytes of y for every lane (one cached line per
+// wavefront, weight zero), so no branch holds the other loads back.
 #include "codecs.hpp"
 #include "internal.hpp"
 
@@ -47,44 +48,53 @@ __device__ __forceinline__ void store8(void* base, int64_t elem, const float (&v
   }
 }
 
-// One thread per 8 consecutive columns of one token; the grid walks
-// (token, column chunk) with the chunk fastest. S routed pairs per round of
-// loads (2, 4 or 8: the smallest not below k, 8 for larger k).
-template <bool YB, bool OB, int S>
+// One wavefront per token (the grid walks the tokens), lanes along the
+// columns: four 512-column pieces per round. The token's pairs are the same
+// for the whole wavefront, so they are taken two at a time, a couple with no
+// local pair is skipped by a branch of the whole wavefront, and a non-local
+// pair next to a local one loads the first 16 bytes of y (one cached line,
+// weight zero) so the couple's loads are in flight together.
+template <bool YB, bool OB>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, int64_t m_cap,
-                                                 uint32_t T, int k, uint32_t nc,
+                                                 int64_t T, int k, int64_t N,
                                                  const int32_t* __restrict__ pair_row,
                                                  const float* __restrict__ gate,
                                                  void* __restrict__ out) {
-  const uint32_t total = T * nc;
-  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-    const uint32_t t = i / nc, c = i - t * nc;
-    const int64_t N = (int64_t)nc * 8;
-    float acc[8];
+  const int lane = threadIdx.x & 63;
+  // the token index is the same for the whole wavefront: scalar loads of its pairs
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int64_t t = (int64_t)blockIdx.x * 4 + w; t < T; t += (int64_t)gridDim.x * 4) {
+    for (int64_t base = 0; base < N; base += 2048) {
+      const int64_t c0 = base + 8 * lane;
+      float acc[4][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    for (int j0 = 0; j0 < k; j0 += S) {
-      int32_t r[S];
-      float g[S];
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int u = 0; u < S; ++u) {
-        const int j = j0 + u < k ? j0 + u : k - 1;
-        r[u] = pair_row[(int64_t)t * k + j];
-        g[u] = gate ? gate[(int64_t)t * k + j] : 1.0f;
+        for (int e = 0; e < 8; ++e) acc[q][e] = 0.0f;
+      for (int j = 0; j < k; j += 2) {
+        const int32_t r0 = pair_row[t * k + j];
+        const int32_t r1 = j + 1 < k ? pair_row[t * k + j + 1] : -1;
+        const bool u0 = r0 >= 0 && r0 < m_cap, u1 = r1 >= 0 && r1 < m_cap;
+        if (!u0 && !u1) continue;                // the same for the whole wavefront
+        const float g0 = u0 ? (gate ? gate[t * k + j] : 1.0f) : 0.0f;
+        const float g1 = u1 ? (gate ? gate[t * k + j + 1] : 1.0f) : 0.0f;
+        float v0[4][8], v1[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + 512 * q < N ? c0 + 512 * q : N - 8;
+          load8<YB>(y, u0 ? (int64_t)r0 * N + c : 0, v0[q]);
+          load8<YB>(y, u1 ? (int64_t)r1 * N + c : 0, v1[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[q][e] = __fmaf_rn(g1, v1[q][e], __fmaf_rn(g0, v0[q][e], acc[q][e]));
       }
-      float v[S][8];
 #pragma unroll
-      for (int u = 0; u < S; ++u) {
-        const bool use = (j0 + u < k) && r[u] >= 0 && r[u] < m_cap;
-        g[u] = use ? g[u] : 0.0f;
-        load8<YB>(y, (use ? (int64_t)r[u] : 0) * N + 8 * (int64_t)c, v[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < S; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = __fmaf_rn(g[u], v[u][e], acc[e]);
+      for (int q = 0; q < 4; ++q)
+        if (c0 + 512 * q < N) store8<OB>(out, t * N + c0 + 512 * q, acc[q]);
     }
-    store8<OB>(out, (int64_t)t * N + 8 * (int64_t)c, acc);
   }
 }
 
@@ -95,7 +105,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // One wavefront per routed row, rows walked by the grid up to offsets[G].
-template <bool DB, bool YB, bool OB>
+// HASY: y is given and dgate is computed.
+template <bool DB, bool YB, bool OB, bool HASY>
 __global__ __launch_bounds__(256) void k_combine_bwd(
     const void* __restrict__ dout, int64_t N, int k, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ row_slot, const int64_t* __restrict__ offsets, int G,
@@ -110,21 +121,31 @@ __global__ __launch_bounds__(256) void k_combine_bwd(
     const int64_t pair = t * k + row_slot[r];
     const float g = gate ? gate[pair] : 1.0f;
     float part = 0.0f;
-    for (int64_t c = 8 * lane; c < N; c += 512) {
-      float d[8];
-      load8<DB>(dout, t * N + c, d);
-      float o[8];
+    // four 512-column pieces per round, all loads of a round in flight together
+    for (int64_t c0 = 8 * lane; c0 < N; c0 += 4 * 512) {
+      float d[4][8], v[4][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = __fmul_rn(g, d[e]);
-      store8<OB>(dy, r * N + c, o);
-      if (y) {
-        float v[8];
-        load8<YB>(y, r * N + c, v);
+      for (int q = 0; q < 4; ++q) {            // past the row's end: reload its last chunk
+        const int64_t c = c0 + 512 * q < N ? c0 + 512 * q : N - 8;
+        load8<DB>(dout, t * N + c, d[q]);
+        if constexpr (HASY) load8<YB>(y, r * N + c, v[q]);
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part = __fmaf_rn(d[e], v[e], part);
+      for (int q = 0; q < 4; ++q) {
+        const int64_t c = c0 + 512 * q;
+        if (c < N) {
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = __fmul_rn(g, d[q][e]);
+          store8<OB>(dy, r * N + c, o);
+          if constexpr (HASY) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = __fmaf_rn(d[q][e], v[q][e], part);
+          }
+        }
       }
     }
-    if (y) {
+    if constexpr (HASY) {
       part = wave_sum(part);
       if (lane == 0) dgate[pair] = part;
     }
@@ -137,27 +158,17 @@ hipError_t launch_combine(const void* y, bool y_bf16, int64_t m_cap, int64_t T, 
                           int64_t N, const int32_t* pair_row, const float* gate, void* out,
                           bool out_bf16, hipStream_t stream) {
   if (T == 0 || N == 0) return hipSuccess;
-  const uint32_t nc = (uint32_t)(N / 8);
-  const int64_t work = T * (int64_t)nc;
-  int64_t grid = (work + 255) / 256;
-  const int64_t most = (int64_t)device_cu_count() * 16;
+  int64_t grid = (T + 3) / 4;                   // one wavefront per token
+  const int64_t most = (int64_t)device_cu_count() * 64;
   if (grid > most) grid = most;
-#define NVFP4MOE_COMBINE_S(YB, OB, S)                                                     \
-  k_combine<YB, OB, S><<<(unsigned)grid, 256, 0, stream>>>(y, m_cap, (uint32_t)T, k, nc,   \
-                                                           pair_row, gate, out)
-#define NVFP4MOE_COMBINE(YB, OB)                                                          \
-  do {                                                                                    \
-    if (k <= 2) NVFP4MOE_COMBINE_S(YB, OB, 2);                                            \
-    else if (k <= 4) NVFP4MOE_COMBINE_S(YB, OB, 4);                                       \
-    else NVFP4MOE_COMBINE_S(YB, OB, 8);                                                   \
-  } while (0)
+#define NVFP4MOE_COMBINE(YB, OB) \
+  k_combine<YB, OB><<<(unsigned)grid, 256, 0, stream>>>(y, m_cap, T, k, N, pair_row, gate, out)
   if (y_bf16) {
     if (out_bf16) NVFP4MOE_COMBINE(true, true); else NVFP4MOE_COMBINE(true, false);
   } else {
     if (out_bf16) NVFP4MOE_COMBINE(false, true); else NVFP4MOE_COMBINE(false, false);
   }
 #undef NVFP4MOE_COMBINE
-#undef NVFP4MOE_COMBINE_S
   return hipGetLastError();
 }
 
@@ -168,11 +179,16 @@ hipError_t launch_combine_bwd(const void* dout, bool dout_bf16, int64_t N, int k
                               hipStream_t stream) {
   if (m_cap == 0 || N == 0) return hipSuccess;
   int64_t grid = (m_cap + 3) / 4;
-  const int64_t most = (int64_t)device_cu_count() * 16;
+  const int64_t most = (int64_t)device_cu_count() * 32;
   if (grid > most) grid = most;
-#define NVFP4MOE_CBWD(DB, YB, OB)                                                            \
-  k_combine_bwd<DB, YB, OB><<<(unsigned)grid, 256, 0, stream>>>(                             \
+#define NVFP4MOE_CBWD3(DB, YB, OB, HY)                                                       \
+  k_combine_bwd<DB, YB, OB, HY><<<(unsigned)grid, 256, 0, stream>>>(                         \
       dout, N, k, row_token, row_slot, offsets, G, m_cap, gate, y, dy, dgate)
+#define NVFP4MOE_CBWD(DB, YB, OB)                                                            \
+  do {                                                                                       \
+    if (y) NVFP4MOE_CBWD3(DB, YB, OB, true);                                                 \
+    else NVFP4MOE_CBWD3(DB, true, OB, false);                                                \
+  } while (0)
   if (dout_bf16) {
     if (y_bf16) {
       if (dy_bf16) NVFP4MOE_CBWD(true, true, true); else NVFP4MOE_CBWD(true, true, false);
@@ -187,6 +203,7 @@ hipError_t launch_combine_bwd(const void* dout, bool dout_bf16, int64_t N, int k
     }
   }
 #undef NVFP4MOE_CBWD
+#undef NVFP4MOE_CBWD3
   return hipGetLastError();
 }
 
