@@ -33,6 +33,6 @@ examples or independent library routines. Philox4x32-10 is pinned against the
 rocRAND source header's host implementation and known-answer vectors.
 """
 
-from . import formats, philox, nvfp4, mxfp8, permute, gemm, ffn  # noqa: F401
+from . import formats, philox, nvfp4, mxfp8, permute, gemm, ffn, nvfp4_bwd  # noqa: F401
 
-__all__ = ["formats", "philox", "nvfp4", "mxfp8", "permute", "gemm", "ffn"]
+__all__ = ["formats", "philox", "nvfp4", "mxfp8", "permute", "gemm", "ffn", "nvfp4_bwd"]
