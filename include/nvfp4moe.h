@@ -72,6 +72,9 @@ enum nvfp4moe_outer_mode { NVFP4MOE_OUTER_PER_ROW = 0, NVFP4MOE_OUTER_PER_GROUP 
 
 enum nvfp4moe_orientation { NVFP4MOE_ROWWISE = 0, NVFP4MOE_COLWISE_GROUPED = 1 };
 
+/* Output layout of the NVFP4 backward's transposes (nvfp4_requant_sr). */
+enum nvfp4moe_layout { NVFP4MOE_LAYOUT_TRANSPOSED = 0, NVFP4MOE_LAYOUT_PER_GROUP = 1 };
+
 /* Version of this ABI (NVFP4MOE_ABI_VERSION). */
 NVFP4MOE_API int nvfp4moe_abi_version(void);
 
@@ -358,6 +361,91 @@ NVFP4MOE_API int moe_combine_bwd(const void* dout, int dout_dtype, int64_t T, in
                     const int64_t* offsets, int G, int64_t m_cap, const float* gate,
                     const void* y, int y_dtype, void* dy, int dy_dtype, float* dgate,
                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * NVFP4 backward: the alternative to the MXFP8 backward, with every gradient
+ * matmul operand in NVFP4. Pages: "Inkling 2 Small uses four-bit training ..."
+ * (ai-primer), section "NVFP4 forward, MXFP8 backward" (NVFP4 in both passes
+ * was tried first and given up) and section "Stochastic rounding across
+ * transposes" (the re-quantization recipe kept here); "Thinking Machines
+ * details ... 4 bit" (advanceintelligence.ai), section "What to expect next"
+ * (a 4-bit backward is being explored).
+ * Common rules: E4M3 block scales are rounded up, S = smallest E4M3 value >=
+ * max|block| / (6 s), so scaled elements stay within [-6, 6]; E2M1 codes are
+ * rounded stochastically with the 16-bit Philox draw of the element's linear
+ * output index (as in mxfp8_requant_sr), a magnitude above 6 (float32
+ * rounding only) becoming 6; blocks whose scale is 0 hold signed zeros; outer
+ * scales s = A / 2688 with A the largest magnitude they cover.
+ * dgrad is moe_fwd_grouped_gemm with a = NVFP4 dY (one outer per row) and
+ * b = the per-expert transposed weights [G, K, N] (one outer per expert).
+ * ------------------------------------------------------------------------- */
+
+/*
+ * padded_offsets[g] = sum over g' < g of round_up(offsets[g'+1] - offsets[g'],
+ * align), g = 0..G (device arrays). Requires G <= 1024.
+ */
+NVFP4MOE_API int moe_padded_offsets(const int64_t* offsets, int G, int align,
+                       int64_t* padded_offsets, void* stream);
+
+/*
+ * Row-wise NVFP4 with stochastic rounding: x [rows, cols] float32 or bfloat16,
+ * one outer scale per row (outer[rows]), blocks of 16 along the row; codes
+ * [rows, cols/2], scales [rows, cols/16]; the draw of element (r, c) is at
+ * index r * cols + c. Requires cols % 32 == 0, cols <= 8192, x, codes, scales
+ * 16-byte aligned.
+ */
+NVFP4MOE_API int nvfp4_quantize_sr(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                      uint64_t seed, uint32_t tag, uint8_t* codes, uint8_t* scales,
+                      float* outer, void* stream);
+
+/*
+ * Saved NVFP4 [rows, cols] (outer per row, or per rows_per_group rows) ->
+ * dequantize (float32) -> grouped transpose -> NVFP4 with stochastic
+ * rounding along the former rows, one outer scale per group: out_outer[G].
+ * Input rows [offsets[g], offsets[g+1]) become output columns
+ * [padded_offsets[g], ... + length) of group g, zero up to
+ * padded_offsets[g+1]; padded offsets must be multiples of 128 (see
+ * moe_padded_offsets) and P >= padded_offsets[G].
+ * layout NVFP4MOE_LAYOUT_TRANSPOSED: codes [cols, P/2], scales [cols, P/16],
+ *   element (k, p) at linear index k * P + p; columns >= padded_offsets[G]
+ *   untouched.
+ * layout NVFP4MOE_LAYOUT_PER_GROUP (weights: all groups of one length L):
+ *   group g's block [cols, L] at element g * cols * L, element (k, p) at
+ *   g * cols * L + k * L + (p - padded_offsets[g]): the transposed weights
+ *   [G, K, N] of the dgrad.
+ * out_outer holds scratch during the call. Requires cols % 128 == 0,
+ * P % 128 == 0, codes, out_codes 16-byte aligned, scales 8-byte aligned.
+ */
+NVFP4MOE_API int nvfp4_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                     int outer_mode, int64_t rows_per_group, int64_t rows, int64_t cols,
+                     const int64_t* offsets, const int64_t* padded_offsets, int G, int64_t P,
+                     int layout, uint64_t seed, uint32_t tag, uint8_t* out_codes,
+                     uint8_t* out_scales, float* out_outer, void* stream);
+
+/*
+ * dY [rows, cols] float32 or bfloat16 -> grouped transpose [cols, P] -> NVFP4
+ * with stochastic rounding, one outer scale per group (the wgrad operand).
+ * Same grouping, layout and requirements as nvfp4_requant_sr with
+ * NVFP4MOE_LAYOUT_TRANSPOSED.
+ */
+NVFP4MOE_API int nvfp4_quantize_sr_colwise(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                              const int64_t* offsets, const int64_t* padded_offsets, int G,
+                              int64_t P, uint64_t seed, uint32_t tag, uint8_t* out_codes,
+                              uint8_t* out_scales, float* out_outer, void* stream);
+
+/*
+ * NVFP4 wgrad grouped GEMM: dyT NVFP4 [N, P] (outer dyT_outer[G]), xT NVFP4
+ * [K, P] (outer xT_outer[G]), padded_offsets[G+1] multiples of 128 (device).
+ * dw[g, n, k] = dyT_outer[g] * xT_outer[g] * sum over p in group g's columns
+ * of (e2m1 * S)_dyT[n, p] * (e2m1 * S)_xT[k, p], exact products (f16 MFMA),
+ * float32 accumulation; dw [G, N, K] float32; empty groups get zeros.
+ * Requires N % 256 == 0, K % 256 == 0, P % 128 == 0, 128 * P < 2^32.
+ */
+NVFP4MOE_API int moe_bwd_wgrad_nvfp4(const uint8_t* dyT_codes, const uint8_t* dyT_scales,
+                        const float* dyT_outer, const uint8_t* xT_codes,
+                        const uint8_t* xT_scales, const float* xT_outer,
+                        const int64_t* padded_offsets, int G, int64_t P, int64_t N, int64_t K,
+                        float* dw, void* stream);
 
 #ifdef __cplusplus
 }

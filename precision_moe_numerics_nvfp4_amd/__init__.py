@@ -20,7 +20,9 @@ from .binding import (  # noqa: F401
     moe_combine,
     moe_combine_bwd,
     moe_fwd_grouped_gemm,
+    moe_bwd_wgrad_nvfp4,
     moe_fwd_grouped_gemm_mxfp8,
+    moe_padded_offsets,
     moe_permute,
     mxfp8_gather_rows,
     mxfp8_quantize,
@@ -28,7 +30,10 @@ from .binding import (  # noqa: F401
     mxfp8_requant_sr,
     nvfp4_quantize,
     nvfp4_quantize_live,
+    nvfp4_quantize_sr,
+    nvfp4_quantize_sr_colwise,
     nvfp4_quantize_tile16,
+    nvfp4_requant_sr,
     permute_workspace_size,
     status_string,
 )

@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe
 NVFP4MOE_F32 = 0
 NVFP4MOE_BF16 = 1
 _OUTER_PER_ROW, _OUTER_PER_GROUP = 0, 1
+_LAYOUT_TRANSPOSED, _LAYOUT_PER_GROUP = 0, 1
 _ROWWISE, _COLWISE_GROUPED = 0, 1
 
 _c_i64 = ctypes.c_int64
@@ -48,6 +49,14 @@ SIGNATURES = {
     "moe_combine": ([_p, _c_int, _c_i64, _c_i64, _c_int, _c_i64, _p, _p, _p, _c_int, _p], _c_int),
     "moe_combine_bwd": ([_p, _c_int, _c_i64, _c_int, _c_i64, _p, _p, _p, _c_int, _c_i64, _p, _p,
                          _c_int, _p, _c_int, _p, _p], _c_int),
+    "moe_padded_offsets": ([_p, _c_int, _c_int, _p, _p], _c_int),
+    "nvfp4_quantize_sr": ([_p, _c_int, _c_i64, _c_i64, _c_u64, _c_u32, _p, _p, _p, _p], _c_int),
+    "nvfp4_requant_sr": ([_p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p, _p, _c_int, _c_i64,
+                          _c_int, _c_u64, _c_u32, _p, _p, _p, _p], _c_int),
+    "nvfp4_quantize_sr_colwise": ([_p, _c_int, _c_i64, _c_i64, _p, _p, _c_int, _c_i64, _c_u64,
+                                   _c_u32, _p, _p, _p, _p], _c_int),
+    "moe_bwd_wgrad_nvfp4": ([_p, _p, _p, _p, _p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p, _p],
+                            _c_int),
 }
 
 _LIB = None
@@ -481,3 +490,115 @@ def moe_combine_bwd(dout, row_token, row_slot, offsets, k, gate=None, y=None, dy
                                _out_dtype(dy.dtype), _ptr(dgate), _stream(dout))
     _check("moe_combine_bwd", st)
     return dy, dgate
+
+
+# ------------------------------------------------------------ NVFP4 backward
+
+def moe_padded_offsets(offsets, align=128, out=None):
+    """Exclusive scan of the group lengths rounded up to ``align`` (int64 [G+1])."""
+    torch = _torch()
+    _dev(offsets, "offsets", torch.int64, 1)
+    G = offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(offsets)
+    st = lib().moe_padded_offsets(_ptr(offsets), G, int(align), _ptr(out), _stream(offsets))
+    _check("moe_padded_offsets", st)
+    return out
+
+
+def nvfp4_quantize_sr(x, seed, tag, codes=None, scales=None, outer=None):
+    """Row-wise NVFP4 of x [rows, cols] with stochastic rounding and rounded-up
+    block scales: (codes [rows, cols/2], scales [rows, cols/16], outer [rows])."""
+    torch = _torch()
+    _dev(x, "x", ndim=2)
+    rows, cols = x.shape
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    if outer is None:
+        outer = torch.empty((rows,), dtype=torch.float32, device=dev)
+    st = lib().nvfp4_quantize_sr(_ptr(x), _in_dtype(x), rows, cols, int(seed), int(tag),
+                                 _ptr(codes), _ptr(scales), _ptr(outer), _stream(x))
+    _check("nvfp4_quantize_sr", st)
+    return codes, scales, outer
+
+
+def nvfp4_requant_sr(codes, scales, outer, offsets, padded_offsets, P, seed, tag,
+                     rows_per_group=None, per_group_layout=False, out=None):
+    """Saved NVFP4 [rows, cols] -> grouped transpose -> NVFP4 with stochastic
+    rounding, one outer scale per group. Transposed layout: (codes [cols, P/2],
+    scales [cols, P/16], outer [G]); per-group layout (groups of one length L,
+    P = G * L): (codes [G * cols, L/2], scales [G * cols, L/16], outer [G])."""
+    torch = _torch()
+    _dev(codes, "codes", torch.uint8, 2)
+    _dev(scales, "scales", torch.uint8, 2)
+    _dev(outer, "outer", torch.float32, 1)
+    _dev(offsets, "offsets", torch.int64, 1)
+    _dev(padded_offsets, "padded_offsets", torch.int64, 1)
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    G = offsets.shape[0] - 1
+    dev = codes.device
+    if out is None:
+        if per_group_layout:
+            L = P // max(G, 1)
+            out = (torch.empty((G * cols, L // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((G * cols, L // 16), dtype=torch.uint8, device=dev),
+                   torch.empty((G,), dtype=torch.float32, device=dev))
+        else:
+            out = (torch.empty((cols, P // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((cols, P // 16), dtype=torch.uint8, device=dev),
+                   torch.empty((G,), dtype=torch.float32, device=dev))
+    mode = _OUTER_PER_ROW if rows_per_group is None else _OUTER_PER_GROUP
+    st = lib().nvfp4_requant_sr(_ptr(codes), _ptr(scales), _ptr(outer), mode,
+                                0 if rows_per_group is None else int(rows_per_group), rows, cols,
+                                _ptr(offsets), _ptr(padded_offsets), G, int(P),
+                                _LAYOUT_PER_GROUP if per_group_layout else _LAYOUT_TRANSPOSED,
+                                int(seed), int(tag), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                                _stream(codes))
+    _check("nvfp4_requant_sr", st)
+    return out
+
+
+def nvfp4_quantize_sr_colwise(x, offsets, padded_offsets, P, seed, tag, out=None):
+    """dY [rows, cols] -> grouped transpose [cols, P] -> NVFP4 with stochastic
+    rounding, one outer scale per group: (codes [cols, P/2], scales
+    [cols, P/16], outer [G])."""
+    torch = _torch()
+    _dev(x, "x", ndim=2)
+    _dev(offsets, "offsets", torch.int64, 1)
+    _dev(padded_offsets, "padded_offsets", torch.int64, 1)
+    rows, cols = x.shape
+    G = offsets.shape[0] - 1
+    dev = x.device
+    if out is None:
+        out = (torch.empty((cols, P // 2), dtype=torch.uint8, device=dev),
+               torch.empty((cols, P // 16), dtype=torch.uint8, device=dev),
+               torch.empty((G,), dtype=torch.float32, device=dev))
+    st = lib().nvfp4_quantize_sr_colwise(_ptr(x), _in_dtype(x), rows, cols, _ptr(offsets),
+                                         _ptr(padded_offsets), G, int(P), int(seed), int(tag),
+                                         _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _stream(x))
+    _check("nvfp4_quantize_sr_colwise", st)
+    return out
+
+
+def moe_bwd_wgrad_nvfp4(dyT, xT, padded_offsets, N, K, dw=None):
+    """dW [G, N, K] float32 from NVFP4 dYT [N, P] and XT [K, P], each given as
+    (codes, scales, outer [G])."""
+    torch = _torch()
+    for t, n in ((dyT[0], "dyT codes"), (dyT[1], "dyT scales"), (xT[0], "xT codes"),
+                 (xT[1], "xT scales")):
+        _dev(t, n, torch.uint8, 2)
+    _dev(dyT[2], "dyT outer", torch.float32, 1)
+    _dev(xT[2], "xT outer", torch.float32, 1)
+    _dev(padded_offsets, "padded_offsets", torch.int64, 1)
+    G = padded_offsets.shape[0] - 1
+    P = dyT[0].shape[1] * 2
+    if dw is None:
+        dw = torch.empty((G, N, K), dtype=torch.float32, device=dyT[0].device)
+    st = lib().moe_bwd_wgrad_nvfp4(_ptr(dyT[0]), _ptr(dyT[1]), _ptr(dyT[2]), _ptr(xT[0]),
+                                   _ptr(xT[1]), _ptr(xT[2]), _ptr(padded_offsets), G, P, int(N),
+                                   int(K), _ptr(dw), _stream(dyT[0]))
+    _check("moe_bwd_wgrad_nvfp4", st)
+    return dw

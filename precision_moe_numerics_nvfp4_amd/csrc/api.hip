@@ -290,4 +290,94 @@ int moe_combine_bwd(const void* dout, int dout_dtype, int64_t T, int k, int64_t 
                                        dgate, as_stream(stream)));
 }
 
+int moe_padded_offsets(const int64_t* offsets, int G, int align, int64_t* padded_offsets,
+                       void* stream) {
+  REQUIRE(G >= 0 && align > 0, NVFP4MOE_EINVAL);
+  REQUIRE(offsets && padded_offsets, NVFP4MOE_EINVAL);
+  REQUIRE(G <= 1024, NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_padded_offsets(offsets, G, align, padded_offsets, as_stream(stream)));
+}
+
+int nvfp4_quantize_sr(const void* x, int x_dtype, int64_t rows, int64_t cols, uint64_t seed,
+                      uint32_t tag, uint8_t* codes, uint8_t* scales, float* outer,
+                      void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0, NVFP4MOE_EINVAL);
+  REQUIRE(x_dtype == NVFP4MOE_F32 || x_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (rows == 0) return NVFP4MOE_OK;
+  REQUIRE(x && codes && scales && outer, NVFP4MOE_EINVAL);
+  REQUIRE(cols > 0 && cols % 32 == 0 && cols <= 8192, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(x) && aligned16(codes) && aligned16(scales), NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_nvfp4_quantize_sr(x, x_dtype == NVFP4MOE_BF16, rows, cols, seed, tag,
+                                             codes, scales, outer, as_stream(stream)));
+}
+
+int nvfp4_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                     int outer_mode, int64_t rows_per_group, int64_t rows, int64_t cols,
+                     const int64_t* offsets, const int64_t* padded_offsets, int G, int64_t P,
+                     int layout, uint64_t seed, uint32_t tag, uint8_t* out_codes,
+                     uint8_t* out_scales, float* out_outer, void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0 && G >= 0 && P >= 0, NVFP4MOE_EINVAL);
+  REQUIRE(outer_mode == NVFP4MOE_OUTER_PER_ROW || outer_mode == NVFP4MOE_OUTER_PER_GROUP,
+          NVFP4MOE_EINVAL);
+  REQUIRE(layout == NVFP4MOE_LAYOUT_TRANSPOSED || layout == NVFP4MOE_LAYOUT_PER_GROUP,
+          NVFP4MOE_EINVAL);
+  const bool per_group = outer_mode == NVFP4MOE_OUTER_PER_GROUP;
+  if (per_group) REQUIRE(rows_per_group > 0, NVFP4MOE_EINVAL);
+  if (G == 0) return NVFP4MOE_OK;
+  REQUIRE(offsets && padded_offsets && out_outer, NVFP4MOE_EINVAL);
+  if (P == 0 || cols == 0) return hip_status(launch_nvfp4_requant_sr(
+      codes, scales, outer, per_group ? rows_per_group : 0, 0, 0, offsets, padded_offsets, G, P,
+      false, seed, tag, out_codes, out_scales, out_outer, as_stream(stream)));
+  REQUIRE(out_codes && out_scales, NVFP4MOE_EINVAL);
+  if (rows > 0) REQUIRE(codes && scales && outer, NVFP4MOE_EINVAL);
+  REQUIRE(cols % 128 == 0 && P % 128 == 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(codes) && aligned16(out_codes), NVFP4MOE_EUNSUPPORTED);
+  REQUIRE((reinterpret_cast<uintptr_t>(scales) & 7u) == 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(((reinterpret_cast<uintptr_t>(out_scales) | reinterpret_cast<uintptr_t>(outer)) & 3u) == 0,
+          NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_nvfp4_requant_sr(
+      codes, scales, outer, per_group ? rows_per_group : 0, rows, cols, offsets, padded_offsets,
+      G, P, layout == NVFP4MOE_LAYOUT_PER_GROUP, seed, tag, out_codes, out_scales, out_outer,
+      as_stream(stream)));
+}
+
+int nvfp4_quantize_sr_colwise(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                              const int64_t* offsets, const int64_t* padded_offsets, int G,
+                              int64_t P, uint64_t seed, uint32_t tag, uint8_t* out_codes,
+                              uint8_t* out_scales, float* out_outer, void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0 && G >= 0 && P >= 0, NVFP4MOE_EINVAL);
+  REQUIRE(x_dtype == NVFP4MOE_F32 || x_dtype == NVFP4MOE_BF16, NVFP4MOE_EINVAL);
+  if (G == 0) return NVFP4MOE_OK;
+  REQUIRE(offsets && padded_offsets && out_outer, NVFP4MOE_EINVAL);
+  if (P > 0 && cols > 0) {
+    REQUIRE(out_codes && out_scales, NVFP4MOE_EINVAL);
+    if (rows > 0) REQUIRE(x != nullptr, NVFP4MOE_EINVAL);
+    REQUIRE(cols % 128 == 0 && P % 128 == 0, NVFP4MOE_EUNSUPPORTED);
+    REQUIRE(aligned16(x) && aligned16(out_codes), NVFP4MOE_EUNSUPPORTED);
+  }
+  return hip_status(launch_nvfp4_quantize_sr_colwise(
+      x, x_dtype == NVFP4MOE_BF16, rows, (P > 0 ? cols : 0), offsets, padded_offsets, G, P, seed,
+      tag, out_codes, out_scales, out_outer, as_stream(stream)));
+}
+
+int moe_bwd_wgrad_nvfp4(const uint8_t* dyT_codes, const uint8_t* dyT_scales,
+                        const float* dyT_outer, const uint8_t* xT_codes, const uint8_t* xT_scales,
+                        const float* xT_outer, const int64_t* padded_offsets, int G, int64_t P,
+                        int64_t N, int64_t K, float* dw, void* stream) {
+  REQUIRE(G >= 0 && P >= 0 && N >= 0 && K >= 0, NVFP4MOE_EINVAL);
+  if (G == 0 || N == 0 || K == 0) return NVFP4MOE_OK;
+  REQUIRE(dyT_codes && dyT_scales && dyT_outer && xT_codes && xT_scales && xT_outer &&
+              padded_offsets && dw,
+          NVFP4MOE_EINVAL);
+  REQUIRE(N % 256 == 0 && K % 256 == 0 && P % 128 == 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(256 * (P / 2) < ((int64_t)1 << 32) - 1, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(aligned16(dyT_codes) && aligned16(xT_codes) && aligned16(dw), NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(((reinterpret_cast<uintptr_t>(dyT_scales) | reinterpret_cast<uintptr_t>(xT_scales)) &
+           7u) == 0,
+          NVFP4MOE_EUNSUPPORTED);
+  return hip_status(launch_wgrad_nvfp4(dyT_codes, dyT_scales, dyT_outer, xT_codes, xT_scales,
+                                       xT_outer, padded_offsets, G, P, N, K, dw,
+                                       as_stream(stream)));
+}
+
 }  // extern "C"

@@ -52,6 +52,39 @@ __device__ __forceinline__ uint32_t e2m1x8_rne(const float* v) {
   return w;
 }
 
+// Stochastic rounding of y onto the E2M1 grid {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+// with a 16-bit draw u: with lo the grid value at or below |y| and D its
+// fractional distance to the next one, round up iff u + floor(D * 2^16) >=
+// 2^16. |y| >= 6 gives 6 (saturation, reached only through float32 rounding
+// when block scales are rounded up). The sign bit of y is kept. Position
+// arithmetic is exact: 2|y|, |y| - 2 and (|y| - 4) / 2 are exact in float32.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
+  const float a = fabsf(y);
+  uint32_t mag;
+  if (a >= 6.0f) {
+    mag = 7u;
+  } else {
+    float t;
+    uint32_t base;
+    if (a < 2.0f) { t = a * 2.0f; base = 0u; }                 // codes 0..3, step 0.5
+    else if (a < 4.0f) { t = a - 2.0f; base = 4u; }            // codes 4..5, step 1
+    else { t = (a - 4.0f) * 0.5f; base = 6u; }                 // code 6, step 2
+    const float fl = floorf(t);
+    const uint32_t d16 = (uint32_t)((t - fl) * 65536.0f);      // floor: exact product
+    mag = base + (uint32_t)fl + ((u + d16) >> 16);
+  }
+  return mag | ((f2u(y) >> 28) & 8u);
+}
+
+// Eight values -> eight stochastically rounded E2M1 codes packed in a word
+// (element j in bits 4j..4j+3), draws u[j].
+__device__ __forceinline__ uint32_t e2m1x8_sr(const float* v, const uint32_t* u) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= e2m1_sr(v[j], u[j]) << (4 * j);
+  return w;
+}
+
 // Two E2M1 codes (one byte: element 2i low nibble) -> float32 values
 // (v_cvt_scalef32_pk_f32_fp4 with a unit scale decodes exactly).
 __device__ __forceinline__ void e2m1x2_to_f32(uint32_t word, int byte, float& lo, float& hi) {
@@ -85,6 +118,13 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_pos(float t) {
   uint32_t b = f2u(t);
   b += 0x7FFFFu + ((b >> 20) & 1u);                     // round mantissa to 3 bits
   return (b >> 20) - (120u << 3);                       // rebias exponent 127 -> 7
+}
+
+// Smallest E4M3FN value >= t for t >= 0 (448 for larger t) -> code.
+__device__ __forceinline__ uint32_t e4m3_ceil_pos(float t) {
+  uint32_t c = e4m3_rne_sat_pos(t);
+  if (c < 0x7Eu && e4m3_pos_to_f32(c) < t) ++c;
+  return c;
 }
 
 // Four values with |y| <= 448 -> E4M3FN bytes (first value in the low byte),

@@ -339,11 +339,17 @@ __device__ __forceinline__ void* first_lane_ptr(const void* p) {
   return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
 }
 
-template <int NS, bool OUT_BF16>
+// WG: the NVFP4 weight gradient with the same main loop. A = dY^T NVFP4
+// [N, P] and B = X^T NVFP4 [K, P] (row stride P / 2 bytes), group g's
+// contraction is columns [offsets[g], offsets[g+1]) (multiples of 128: no
+// stage straddles two groups), outer scales ao[g], bo[g] per group, output
+// y = dW [G, N, K] float32; all tiles are full (N, K multiples of 256).
+template <int NS, bool OUT_BF16, bool WG = false>
 __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ao,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bo,
-    const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y) {
+    const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y,
+    int64_t P = 0) {
   constexpr int TM = 4, TN = 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
 
@@ -356,7 +362,20 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   const int ntn = (int)(N / LT);
   int g, nt;
   int64_t row0, row_end;
-  {
+  if constexpr (WG) {
+    // tiles expert by expert; inside an expert, blocks of 4 output-column
+    // tiles with the output-row tile fastest
+    const int nrt = (int)(N / LT), nct = (int)(K / LT);
+    const int per = nrt * nct, total = G * per;
+    if ((int)blockIdx.x >= total) return;
+    const int tt = (int)xcd_tile(blockIdx.x, total);
+    g = tt / per;
+    int mi, ni;
+    block_order(tt - g * per, nrt, nct, mi, ni);
+    nt = ni;
+    row0 = (int64_t)mi * LT;
+    row_end = row0 + LT;
+  } else {
     int* pre = reinterpret_cast<int*>(lsm);            // [3G+1], before any stage load
     tile_prefix(3 * G, [&](int e) {
       const int part = e / G, gg = e - part * G;
@@ -396,20 +415,23 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // uniform per wavefront
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, r32 = lane & 31;
-  const int64_t KB = K / 2, KSB = K / 16;
+  // row strides (bytes) of codes and scales; WG: contraction starts at the
+  // group's first column
+  const int64_t KB = WG ? P / 2 : K / 2, KSB = WG ? P / 16 : K / 16;
+  const int64_t cb0 = WG ? offsets[g] / 2 : 0, sb0 = WG ? offsets[g] / 16 : 0;
   const int arows = __builtin_amdgcn_readfirstlane(
       (int)(row_end - row0 < LT ? row_end - row0 : LT));          // valid A rows
 
   // buffer resources (tile-relative, uniform)
   const __amdgpu_buffer_rsrc_t rac = __builtin_amdgcn_make_buffer_rsrc(
-      first_lane_ptr(ac + row0 * KB), (short)0, (int)(uint32_t)(arows * KB), kBufWord3);
+      first_lane_ptr(ac + row0 * KB + cb0), (short)0, (int)(uint32_t)(arows * KB), kBufWord3);
   const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
-      first_lane_ptr(as + row0 * KSB), (short)0, (int)(uint32_t)(arows * KSB), kBufWord3);
-  const int64_t brow0 = (int64_t)g * N + n0;
+      first_lane_ptr(as + row0 * KSB + sb0), (short)0, (int)(uint32_t)(arows * KSB), kBufWord3);
+  const int64_t brow0 = WG ? n0 : (int64_t)g * N + n0;
   const __amdgpu_buffer_rsrc_t rbc = __builtin_amdgcn_make_buffer_rsrc(
-      first_lane_ptr(bc + brow0 * KB), (short)0, (int)(uint32_t)(LT * KB), kBufWord3);
+      first_lane_ptr(bc + brow0 * KB + cb0), (short)0, (int)(uint32_t)(LT * KB), kBufWord3);
   const __amdgpu_buffer_rsrc_t rbs = __builtin_amdgcn_make_buffer_rsrc(
-      first_lane_ptr(bs + brow0 * KSB), (short)0, (int)(uint32_t)(LT * KSB), kBufWord3);
+      first_lane_ptr(bs + brow0 * KSB + sb0), (short)0, (int)(uint32_t)(LT * KSB), kBufWord3);
 
   // DMA offsets of this lane. Codes: instruction i of wavefront w fills rows
   // (4i + w) * 16 + lane / 4 at position lane % 4; scales: instruction j
@@ -479,7 +501,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int64_t nk = K / LBK;
+  const int64_t nk = WG ? (offsets[g + 1] - offsets[g]) / LBK : K / LBK;
 
   // per-lane LDS byte offsets of the fragment reads (stage-relative)
   int fa[TM][2], fb[TN][2], sa_off[TM], sb_off[TN];
@@ -630,7 +652,9 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     region(f1, f0, 0, none, Z{}, Z{});   // step 0 of stage kt+1 (unused after the last stage)
   }
   };
-  {
+  if constexpr (WG) {
+    mainloop(std::integral_constant<int, 4>{});        // weight-gradient tiles are full
+  } else {
     const int act = (arows - wm * 128 + 31) >> 5;      // valid 32-row blocks of this wavefront
     if (act >= 4) mainloop(std::integral_constant<int, 4>{});
     else if (act == 3) mainloop(std::integral_constant<int, 3>{});
@@ -650,11 +674,13 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   uint8_t* ep = lsm + wave * (32 * RS);
   const float sw = bo[g];
   const int64_t col0 = n0 + wn * 128;
+  const int64_t ldo = WG ? K : N;                        // output row stride (elements)
+  const int64_t obase = WG ? (int64_t)g * N * K : 0;    // WG: expert g's dW
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int rl = i * 32 + r32;                         // row within the wavefront's block
     const int64_t row = row0 + wm * 128 + rl;
-    const float sx = row < row_end ? ao[row] : 0.0f;
+    const float sx = WG ? ao[g] : (row < row_end ? ao[row] : 0.0f);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -679,7 +705,8 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
       const u32x4 val = *reinterpret_cast<const u32x4*>(ep + r * RS + c * 16);
       const int64_t orow = row0 + wm * 128 + i * 32 + r;
       if (orow < row_end)
-        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(y) + (orow * N + col0) * ES + c * 16) = val;
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(y) + (obase + orow * ldo + col0) * ES +
+                                  c * 16) = val;
     }
   }
 }
@@ -699,7 +726,7 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
-  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y);
+  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, 0);
   return hipGetLastError();
 }
 
@@ -1022,6 +1049,27 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
     return launch_cfg<32, 128, 1, 4>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
                                      stream);
   return launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, stream);
+}
+
+// NVFP4 weight gradient (see WG above).
+hipError_t launch_wgrad_nvfp4(const uint8_t* ac, const uint8_t* as, const float* ao,
+                              const uint8_t* bc, const uint8_t* bs, const float* bo,
+                              const int64_t* padded, int G, int64_t P, int64_t N, int64_t K,
+                              float* dw, hipStream_t stream) {
+  constexpr int NS = 3;
+  const size_t lds = (size_t)NS * kStageBytes;
+  const int64_t tiles = (int64_t)G * (N / LT) * (K / LT);
+  if (tiles == 0) return hipSuccess;
+  auto k = k_fwd_lds4<NS, false, true>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, padded, G, N, K, dw, P);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4moe

@@ -69,7 +69,28 @@ hipError_t launch_mxfp8_quantize_dual(const void* x, bool bf16, int64_t rows, in
                                       int64_t P, uint8_t* row_out, uint8_t* row_e8, uint8_t* out,
                                       uint8_t* out_e8, hipStream_t stream);
 
+hipError_t launch_nvfp4_requant_sr(const uint8_t* codes, const uint8_t* scales,
+                                   const float* outer, int64_t rpg, int64_t rows, int64_t cols,
+                                   const int64_t* offsets, const int64_t* padded, int G, int64_t P,
+                                   bool blocked, uint64_t seed, uint32_t tag, uint8_t* out,
+                                   uint8_t* out_sc, float* out_outer, hipStream_t stream);
+hipError_t launch_nvfp4_quantize_sr_colwise(const void* x, bool bf16, int64_t rows,
+                                            int64_t cols, const int64_t* offsets,
+                                            const int64_t* padded, int G, int64_t P,
+                                            uint64_t seed, uint32_t tag, uint8_t* out,
+                                            uint8_t* out_sc, float* out_outer,
+                                            hipStream_t stream);
+hipError_t launch_nvfp4_quantize_sr(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                    uint64_t seed, uint32_t tag, uint8_t* codes, uint8_t* scales,
+                                    float* outer, hipStream_t stream);
+hipError_t launch_padded_offsets(const int64_t* offsets, int G, int64_t align, int64_t* padded,
+                                 hipStream_t stream);
+
 // gemm_fwd.hip
+hipError_t launch_wgrad_nvfp4(const uint8_t* ac, const uint8_t* as, const float* ao,
+                              const uint8_t* bc, const uint8_t* bs, const float* bo,
+                              const int64_t* padded, int G, int64_t P, int64_t N, int64_t K,
+                              float* dw, hipStream_t stream);
 hipError_t launch_fwd_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const float* a_outer, const uint8_t* b_codes,
                                    const uint8_t* b_scales, const float* b_outer,

@@ -475,6 +475,24 @@ size_t permute_workspace_bytes(int64_t T, int k, int n_local) {
   return (size_t)((n_chunks > 0 ? n_chunks : 1) * (int64_t)n_local * 4 + 256);
 }
 
+// padded[g] = sum over g' < g of round_up(offsets[g'+1] - offsets[g'], align),
+// one workgroup, G <= 1024.
+__global__ __launch_bounds__(1024) void k_pad_offsets(const int64_t* __restrict__ offsets, int G,
+                                                      int64_t align, int64_t* __restrict__ padded) {
+  const int g = threadIdx.x;
+  const int64_t len = g < G ? offsets[g + 1] - offsets[g] : 0;
+  int64_t total;
+  const int64_t ex = block_scan_1024((len + align - 1) / align * align, total);
+  if (g < G) padded[g] = ex;
+  if (g == 0) padded[G] = total;
+}
+
+hipError_t launch_padded_offsets(const int64_t* offsets, int G, int64_t align, int64_t* padded,
+                                 hipStream_t stream) {
+  k_pad_offsets<<<1, 1024, 0, stream>>>(offsets, G, align, padded);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const int32_t* ids, int64_t T, int k, int e0, int n_local,
                           const uint8_t* qc, const uint8_t* qs, const float* qo, int64_t K,
                           int64_t* offsets, int64_t* padded, int32_t* row_token,

@@ -52,11 +52,13 @@ __device__ __forceinline__ void load16(const void* base, int64_t elem, Row16<BF1
 
 // One wavefront per row; lane l owns blocks l, l+64, ...
 // gamax != nullptr: per-group mode, A is read from the group-max pass.
-template <bool BF16, int BPL>
+// SR: block scales rounded up to the next E4M3 value and codes rounded
+// stochastically, the draw of element (row, c) at index row * cols + c.
+template <bool BF16, int BPL, bool SR = false>
 __device__ __forceinline__ void quantize_row(
     const void* __restrict__ x, int64_t row, int nb, const uint32_t* __restrict__ gamax,
     int64_t rpg, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ outer) {
+    float* __restrict__ outer, uint64_t seed = 0, uint32_t tag = 0) {
   const int lane = threadIdx.x & 63;
   Row16<BF16> v[BPL];
   float bmax[BPL];
@@ -82,8 +84,12 @@ __device__ __forceinline__ void quantize_row(
     const int b = lane + 64 * i;
     if (b >= nb) continue;
     uint32_t sc = 0;
-    if (A > 0.0f) sc = e4m3_rne_sat_pos(__fdiv_rn(bmax[i], d));
+    if (A > 0.0f) {
+      if constexpr (SR) sc = e4m3_ceil_pos(__fdiv_rn(bmax[i], d));
+      else sc = e4m3_rne_sat_pos(__fdiv_rn(bmax[i], d));
+    }
     uint32_t lo = 0, hi = 0;
+    const uint64_t q = (uint64_t)(row * nb + b) * 2;   // Philox counter: (row * cols + 16 b) / 8
     if (sc) {
       const float r = __fdiv_rn(1.0f, __fmul_rn(e4m3_pos_to_f32(sc), s));
       float a[8], b[8];
@@ -92,8 +98,20 @@ __device__ __forceinline__ void quantize_row(
         a[j] = __fmul_rn(v[i].get(j), r);
         b[j] = __fmul_rn(v[i].get(j + 8), r);
       }
-      lo = e2m1x8_rne(a);
-      hi = e2m1x8_rne(b);
+      if constexpr (SR) {
+        const Draws8 d0 = draws8(q, seed, tag), d1 = draws8(q + 1, seed, tag);
+        uint32_t u0[8], u1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          u0[j] = d0.get(j);
+          u1[j] = d1.get(j);
+        }
+        lo = e2m1x8_sr(a, u0);
+        hi = e2m1x8_sr(b, u1);
+      } else {
+        lo = e2m1x8_rne(a);
+        hi = e2m1x8_rne(b);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -116,6 +134,17 @@ __global__ __launch_bounds__(256) void k_nvfp4_quantize(
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // uniform per wavefront
   quantize_row<BF16, BPL>(x, row, nb, gamax, rpg, codes, scales, outer);
+}
+
+// Row-wise NVFP4 with stochastic rounding (per-row outer scales), 4 rows per
+// workgroup.
+template <bool BF16, int BPL>
+__global__ __launch_bounds__(256) void k_nvfp4_quantize_sr(
+    const void* __restrict__ x, int64_t rows, int nb, uint64_t seed, uint32_t tag,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // uniform per wavefront
+  quantize_row<BF16, BPL, true>(x, row, nb, nullptr, 1, codes, scales, outer, seed, tag);
 }
 
 // Per-row outer scales for the first *n_live rows of a capacity-sized
@@ -377,6 +406,31 @@ hipError_t launch_nvfp4_quantize_live(const void* x, bool bf16, int64_t rows, in
                                       float* outer, hipStream_t stream) {
   return bf16 ? quantize_live_impl<true>(x, rows, cols, n_live, codes, scales, outer, stream)
               : quantize_live_impl<false>(x, rows, cols, n_live, codes, scales, outer, stream);
+}
+
+template <bool BF16>
+static hipError_t quantize_sr_impl(const void* x, int64_t rows, int64_t cols, uint64_t seed,
+                                   uint32_t tag, uint8_t* codes, uint8_t* scales, float* outer,
+                                   hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int nb = (int)(cols / 16);
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  if (nb <= 64)
+    k_nvfp4_quantize_sr<BF16, 1><<<grid, 256, 0, stream>>>(x, rows, nb, seed, tag, codes, scales, outer);
+  else if (nb <= 128)
+    k_nvfp4_quantize_sr<BF16, 2><<<grid, 256, 0, stream>>>(x, rows, nb, seed, tag, codes, scales, outer);
+  else if (nb <= 256)
+    k_nvfp4_quantize_sr<BF16, 4><<<grid, 256, 0, stream>>>(x, rows, nb, seed, tag, codes, scales, outer);
+  else
+    k_nvfp4_quantize_sr<BF16, 8><<<grid, 256, 0, stream>>>(x, rows, nb, seed, tag, codes, scales, outer);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize_sr(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                    uint64_t seed, uint32_t tag, uint8_t* codes, uint8_t* scales,
+                                    float* outer, hipStream_t stream) {
+  return bf16 ? quantize_sr_impl<true>(x, rows, cols, seed, tag, codes, scales, outer, stream)
+              : quantize_sr_impl<false>(x, rows, cols, seed, tag, codes, scales, outer, stream);
 }
 
 template <bool BF16>

@@ -1,12 +1,18 @@
-// Grouped transpose + MXFP8 quantization along the token dimension.
+// Grouped transpose + MXFP8 (or NVFP4) quantization along the token dimension.
 //
-// Two users:
+// Users:
 //  * mxfp8_requant_sr: the saved NVFP4 activations / weights are dequantized
 //    to float32, transposed, and re-quantized to MXFP8 with stochastic
 //    rounding ("Inkling 2 Small uses four-bit training ...", section
 //    "Stochastic rounding across transposes");
 //  * mxfp8_quantize (COLWISE_GROUPED): dY is transposed and quantized with
-//    round-to-nearest-even, giving the wgrad operand.
+//    round-to-nearest-even, giving the wgrad operand;
+//  * the NVFP4 backward (nvfp4_requant_sr, nvfp4_quantize_sr colwise): the
+//    same transposes with NVFP4 output: blocks of 16 tokens (two neighbouring
+//    lanes), E4M3 block scales rounded up, E2M1 codes rounded stochastically,
+//    one outer scale per group from a maximum pass over the group's rows
+//    (k_group_amax_rows) run before; optionally written per group
+//    ([G, cols, group length], the transposed weights of each expert).
 //
 // Output [cols, P]: input rows [offsets[g], offsets[g+1]) of group g land in
 // columns padded_offsets[g] + (r - offsets[g]); the rest of each group's
@@ -73,6 +79,80 @@ struct Tile<Src::F32> {
   float v[TP][PITCH];
 };
 
+// Maximum magnitude of each group's rows, as float bits (non-negative floats
+// order like their bits): one wavefront per row, rows walked by the grid up to
+// offsets[G]; NVFP4 rows give max |e2m1 * S| times their outer scale, the
+// value the transpose dequantizes them to. bits must be zero beforehand.
+template <Src S>
+__global__ __launch_bounds__(256) void k_group_amax_rows(
+    const void* __restrict__ src, const uint8_t* __restrict__ src_scales,
+    const float* __restrict__ src_outer, int64_t rpg, int64_t cols,
+    const int64_t* __restrict__ offsets, int G, uint32_t* __restrict__ bits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = offsets[G];
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows;
+       r += (int64_t)gridDim.x * 4) {
+    float m = 0.0f;
+    if constexpr (S == Src::NVFP4) {
+      // 16 code bytes (two blocks) per lane and step
+      const uint8_t* rc = static_cast<const uint8_t*>(src) + r * (cols / 2);
+      const uint8_t* rs = src_scales + r * (cols / 16);
+      for (int64_t c = 16 * lane; c < cols / 2; c += 16 * 64) {
+        const uint4 w = *reinterpret_cast<const uint4*>(rc + c);
+        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(rs + c / 8);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          uint32_t mx = 0;                    // largest magnitude code (order = value order)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int n = 0; n < 8; ++n) mx = max(mx, (wd[2 * blk + h] >> (4 * n)) & 7u);
+          float e0, e1;
+          e2m1x2_to_f32(mx, 0, e0, e1);
+          m = fmaxf(m, __fmul_rn(e0, e4m3_pos_to_f32((sc2 >> (8 * blk)) & 0x7Fu)));
+        }
+      }
+      m = __fmul_rn(m, src_outer[rpg ? r / rpg : r]);      // rounding is monotone
+    } else {
+      constexpr int EB = (S == Src::BF16) ? 2 : 4;
+      const uint8_t* rx = static_cast<const uint8_t*>(src) + r * cols * EB;
+      for (int64_t c = 16 * lane; c < cols * EB; c += 16 * 64) {
+        const uint4 w = *reinterpret_cast<const uint4*>(rx + c);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (S == Src::BF16) {
+            m = fmaxf(m, fabsf(u2f(wd[j] << 16)));
+            m = fmaxf(m, fabsf(u2f(wd[j] & 0xFFFF0000u)));
+          } else {
+            m = fmaxf(m, fabsf(u2f(wd[j])));
+          }
+        }
+      }
+    }
+    m = wave_max(m);
+    if (lane == 0) {
+      int lo = 0, hi = G;                   // last g with offsets[g] <= r
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offsets[mid] <= r) lo = mid; else hi = mid;
+      }
+      atomicMax(bits + lo, f2u(m));
+    }
+  }
+}
+
+__global__ void k_zero_u32(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__global__ void k_bits_to_outer(float* __restrict__ outer, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) outer[i] = __fdiv_rn(outer[i], 2688.0f);     // maximum bits -> A / (6 * 448)
+}
+
 __device__ __forceinline__ int64_t xcd_band(int64_t w, int64_t live) {
   const int64_t x = w & 7, s = w >> 3;
   const int64_t q = live >> 3, r = live & 7;
@@ -82,15 +162,20 @@ __device__ __forceinline__ int64_t xcd_band(int64_t w, int64_t live) {
 // ROWS (float sources only): the staged tile also yields the row-wise MXFP8
 // quantization of its rows (blocks of 32 along the columns), written to
 // row_out [rows, cols] and row_e8 [rows, cols/32] at the source row.
-template <Src S, bool SR, bool ROWS = false>
+// NVO: NVFP4 output instead (codes to out, E4M3 scales to out_e8, group maxima
+// as float bits in gbits); BLK: each group's part written as its own
+// [cols, group length] block.
+template <Src S, bool SR, bool ROWS = false, bool NVO = false, bool BLK = false>
 __global__ __launch_bounds__(256) void k_transpose_mx(
     const void* __restrict__ src, const uint8_t* __restrict__ src_scales,
     const float* __restrict__ src_outer, int64_t rpg, int64_t cols,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ padded, int G, int64_t P,
     uint64_t seed, uint32_t tag, uint8_t* __restrict__ out, uint8_t* __restrict__ out_e8,
-    uint8_t* __restrict__ row_out = nullptr, uint8_t* __restrict__ row_e8 = nullptr) {
+    uint8_t* __restrict__ row_out = nullptr, uint8_t* __restrict__ row_e8 = nullptr,
+    const uint32_t* __restrict__ gbits = nullptr) {
   __shared__ Tile<S> tile;
   __shared__ int64_t row_of[TP];  // source row of each tile token, -1 = padding
+  __shared__ int grp_of[TP];      // group of each tile token
 
   const int tid = threadIdx.x;
   const int64_t n_ct = cols / TK;
@@ -112,6 +197,9 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
       }
       const int64_t i = p - padded[lo];
       if (i < offsets[lo + 1] - offsets[lo]) r = offsets[lo] + i;
+      grp_of[tid] = lo;
+    } else {
+      grp_of[tid] = 0;
     }
     row_of[tid] = r;
   }
@@ -247,6 +335,53 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
 
   const int64_t p = p0 + 8 * pc;                 // first output column of this thread
   const bool live_p = p < plim;                  // whole 8-chunk shares liveness
+  if constexpr (NVO) {
+    // 16-token blocks: this lane and its neighbour (pc ^ 1) hold one block
+    const int g = grp_of[8 * pc];
+    const float sg = __fdiv_rn(u2f(gbits[g]), 2688.0f);
+    const float dg = __fmul_rn(6.0f, sg);
+    const int64_t kt = k0 + 8 * kc;              // first output row of this thread
+    int64_t lin, step;                           // linear index of (kt, p), per output row
+    if constexpr (BLK) {
+      const int64_t pg = padded[g], glen = padded[g + 1] - pg;
+      lin = (int64_t)g * cols * glen + kt * glen + (p - pg);
+      step = glen;
+    } else {
+      lin = kt * P + p;
+      step = P;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float mf = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[j][i]));
+      uint32_t mb = f2u(mf);
+      mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, true));
+      const uint32_t sc = sg > 0.0f ? e4m3_ceil_pos(__fdiv_rn(u2f(mb), dg)) : 0u;
+      uint32_t w = 0;
+      if (sc) {
+        const float r = __fdiv_rn(1.0f, __fmul_rn(e4m3_pos_to_f32(sc), sg));
+        const Draws8 u = draws8((uint64_t)(lin >> 3), seed, tag);
+        float y[8];
+        uint32_t uu[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          y[i] = __fmul_rn(v[j][i], r);
+          uu[i] = u.get(i);
+        }
+        w = e2m1x8_sr(y, uu);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= ((f2u(v[j][i]) >> 28) & 8u) << (4 * i);
+      }
+      if (live_p) {
+        *reinterpret_cast<uint32_t*>(out + (lin >> 1)) = w;
+        if ((pc & 1) == 0) out_e8[lin >> 4] = (uint8_t)sc;
+      }
+      lin += step;
+    }
+    return;
+  }
   const int64_t PB = P / 32;
   const int64_t kt = k0 + 8 * kc;                // first output row of this thread
   uint8_t* o8 = out + kt * P + p;
@@ -281,16 +416,43 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
   }
 }
 
-template <Src S, bool SR, bool ROWS = false>
+template <Src S, bool SR, bool ROWS = false, bool NV = false, bool BLK = false>
 hipError_t run(const void* src, const uint8_t* sc, const float* so, int64_t rpg, int64_t rows,
                int64_t cols, const int64_t* offsets, const int64_t* padded, int G, int64_t P,
                uint64_t seed, uint32_t tag, uint8_t* out, uint8_t* out_e8, hipStream_t stream,
-               uint8_t* row_out = nullptr, uint8_t* row_e8 = nullptr) {
+               uint8_t* row_out = nullptr, uint8_t* row_e8 = nullptr,
+               const uint32_t* gbits = nullptr) {
   (void)rows;
   if (P == 0 || cols == 0 || G == 0) return hipSuccess;
   const int64_t grid = (P + TP - 1) / TP * (cols / TK);
-  k_transpose_mx<S, SR, ROWS><<<(unsigned)grid, 256, 0, stream>>>(
-      src, sc, so, rpg, cols, offsets, padded, G, P, seed, tag, out, out_e8, row_out, row_e8);
+  k_transpose_mx<S, SR, ROWS, NV, BLK><<<(unsigned)grid, 256, 0, stream>>>(
+      src, sc, so, rpg, cols, offsets, padded, G, P, seed, tag, out, out_e8, row_out, row_e8,
+      gbits);
+  return hipGetLastError();
+}
+
+// NVFP4 output: zero the group maxima (kept in out_outer), take them, run the
+// transpose, turn the maxima into outer scales.
+template <Src S, bool BLK>
+hipError_t run_nv(const void* src, const uint8_t* sc, const float* so, int64_t rpg, int64_t cols,
+                  const int64_t* offsets, const int64_t* padded, int G, int64_t P, uint64_t seed,
+                  uint32_t tag, uint8_t* out, uint8_t* out_sc, float* out_outer,
+                  int64_t m_cap, hipStream_t stream) {
+  if (G == 0) return hipSuccess;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(out_outer);
+  k_zero_u32<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(bits, G);
+  if (cols > 0 && m_cap > 0) {
+    int64_t grid = (m_cap + 3) / 4;
+    const int64_t most = (int64_t)device_cu_count() * 16;
+    if (grid > most) grid = most;
+    k_group_amax_rows<S><<<(unsigned)grid, 256, 0, stream>>>(src, sc, so, rpg, cols, offsets, G,
+                                                             bits);
+  }
+  hipError_t e = run<S, true, false, true, BLK>(src, sc, so, rpg, 0, cols, offsets, padded, G, P,
+                                                seed, tag, out, out_sc, stream, nullptr, nullptr,
+                                                bits);
+  if (e != hipSuccess) return e;
+  k_bits_to_outer<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(out_outer, G);
   return hipGetLastError();
 }
 
@@ -302,6 +464,31 @@ hipError_t launch_requant_sr(const uint8_t* codes, const uint8_t* scales, const 
                              uint32_t tag, uint8_t* out, uint8_t* out_e8, hipStream_t stream) {
   return run<Src::NVFP4, true>(codes, scales, outer, rpg, rows, cols, offsets, padded, G, P, seed,
                                tag, out, out_e8, stream);
+}
+
+hipError_t launch_nvfp4_requant_sr(const uint8_t* codes, const uint8_t* scales,
+                                   const float* outer, int64_t rpg, int64_t rows, int64_t cols,
+                                   const int64_t* offsets, const int64_t* padded, int G, int64_t P,
+                                   bool blocked, uint64_t seed, uint32_t tag, uint8_t* out,
+                                   uint8_t* out_sc, float* out_outer, hipStream_t stream) {
+  if (blocked)
+    return run_nv<Src::NVFP4, true>(codes, scales, outer, rpg, cols, offsets, padded, G, P, seed,
+                                    tag, out, out_sc, out_outer, rows, stream);
+  return run_nv<Src::NVFP4, false>(codes, scales, outer, rpg, cols, offsets, padded, G, P, seed,
+                                   tag, out, out_sc, out_outer, rows, stream);
+}
+
+hipError_t launch_nvfp4_quantize_sr_colwise(const void* x, bool bf16, int64_t rows,
+                                            int64_t cols, const int64_t* offsets,
+                                            const int64_t* padded, int G, int64_t P,
+                                            uint64_t seed, uint32_t tag, uint8_t* out,
+                                            uint8_t* out_sc, float* out_outer,
+                                            hipStream_t stream) {
+  if (bf16)
+    return run_nv<Src::BF16, false>(x, nullptr, nullptr, 0, cols, offsets, padded, G, P, seed,
+                                    tag, out, out_sc, out_outer, rows, stream);
+  return run_nv<Src::F32, false>(x, nullptr, nullptr, 0, cols, offsets, padded, G, P, seed, tag,
+                                 out, out_sc, out_outer, rows, stream);
 }
 
 hipError_t launch_mxfp8_quantize_colwise(const void* x, bool bf16, int64_t rows, int64_t cols,

@@ -154,6 +154,35 @@ def test_ffn_entry_argument_errors(L):
              None) == 0                                                             # no groups
 
 
+def test_nvfp4_backward_entry_argument_errors(L):
+    po = L.moe_padded_offsets
+    assert po(FAKE, 4, 0, FAKE, None) == EINVAL                                    # align 0
+    assert po(FAKE, 2000, 128, FAKE, None) == EUNSUP                               # G > 1024
+    assert po(None, 4, 128, FAKE, None) == EINVAL
+    q = L.nvfp4_quantize_sr
+    assert q(FAKE, 1, 64, 48, 1, 7, FAKE, FAKE, FAKE, None) == EUNSUP              # cols % 32
+    assert q(FAKE, 3, 64, 256, 1, 7, FAKE, FAKE, FAKE, None) == EINVAL             # dtype
+    assert q(None, 1, 64, 256, 1, 7, FAKE, FAKE, FAKE, None) == EINVAL
+    r = L.nvfp4_requant_sr
+    args = lambda mode, rpg, cols, P, layout: (FAKE, FAKE, FAKE, mode, rpg, 64, cols, FAKE, FAKE, 2,
+                                               P, layout, 1, 5, FAKE, FAKE, FAKE, None)
+    assert r(*args(2, 0, 256, 256, 0)) == EINVAL                                   # outer mode
+    assert r(*args(1, 0, 256, 256, 0)) == EINVAL                                   # rows_per_group
+    assert r(*args(0, 0, 256, 256, 5)) == EINVAL                                   # layout
+    assert r(*args(0, 0, 192, 256, 0)) == EUNSUP                                   # cols % 128
+    assert r(*args(0, 0, 256, 96, 0)) == EUNSUP                                    # P % 128
+    c = L.nvfp4_quantize_sr_colwise
+    assert c(FAKE, 1, 64, 256, None, FAKE, 2, 256, 1, 8, FAKE, FAKE, FAKE, None) == EINVAL
+    assert c(FAKE, 1, 64, 200, FAKE, FAKE, 2, 256, 1, 8, FAKE, FAKE, FAKE, None) == EUNSUP
+    w = L.moe_bwd_wgrad_nvfp4
+    wa = lambda P, N, K: (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, P, N, K, FAKE, None)
+    assert w(*wa(256, 384, 256)) == EUNSUP                                         # N % 256
+    assert w(*wa(256, 256, 128)) == EUNSUP                                         # K % 256
+    assert w(*wa(200, 256, 256)) == EUNSUP                                         # P % 128
+    assert w(*wa(1 << 26, 256, 256)) == EUNSUP                                     # 32-bit range
+    assert w(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 256, FAKE, None) == EINVAL
+
+
 def test_binding_rejects_host_tensors():
     import torch
     from precision_moe_numerics_nvfp4_amd import binding
