@@ -46,9 +46,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["ffn-share", "ffn-small"], default=None,
-                    help="time one routed-FFN workload alone and print its record "
-                         "(for profiling runs)")
+    ap.add_argument("--only", choices=["ffn-share", "ffn-small", "nvfp4-bwd"], default=None,
+                    help="time one routed-FFN workload or the NVFP4-backward comparison alone and print "
+                         "its record (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="0 skips the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run three 256 MiB device copies (the known-size reference for "
@@ -307,6 +307,88 @@ def ffn_workload(torch, name, reps):
         dev_tensor(c["gate"], torch), dev_tensor(c["dout"], torch), 8, 2048, 0)
 
 
+def _dequant_nvfp4(torch, codes, scales, outer):
+    """NVFP4 rows -> float32 (codes [R, C/2], scales [R, C/16], outer [R]) with
+    plain torch ops, for the error measurement only."""
+    e2m1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                         -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0],
+                        dtype=torch.float32, device=codes.device)
+    c = codes.to(torch.int64)
+    v = torch.stack([e2m1[c & 15], e2m1[c >> 4]], dim=2).reshape(codes.shape[0], -1)
+    sc = scales.to(torch.int64)
+    e, m = (sc >> 3) & 15, (sc & 7).to(torch.float32)
+    S = torch.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * torch.pow(2.0, (e - 7).to(torch.float32)))
+    return v * S.repeat_interleave(16, dim=1) * outer[:, None]
+
+
+def nvfp4_backward_compare(torch, reps, n_seeds=8):
+    """The NVFP4 backward next to the MXFP8 backward on the small MoE layer:
+    time of each path (requant of the saved activations and weights, dY in
+    both orientations, dgrad, wgrad) and, against the exact gradients of the
+    forward's dequantized operands (float32 matmuls), the relative error of
+    one step and the relative bias (error of the mean over n_seeds seeds)."""
+    from precision_moe_numerics_nvfp4_amd.layer import ExpertLayerStep, NVFP4BackwardStep
+    from workloads import gen
+    w = gen.small_moe()
+    T, K, N, E, k = w["T"], w["K"], w["N"], w["E"], w["k"]
+    dy = dev_tensor(gen.backward_dy(T * k, N), torch)
+    L = ExpertLayerStep(T, K, N, E, k, out_dtype=torch.float32)
+    x, wt, topk = dev_tensor(w["x"], torch), dev_tensor(w["w"], torch), dev_tensor(w["topk"], torch)
+    L.quantize_x(x)
+    L.quantize_w(wt)
+    L.permute(topk)
+    L.forward_gemm()
+    NB = NVFP4BackwardStep(L)
+    t_mx = _time(torch, lambda: (L.requant_x(), L.requant_w(), L.quantize_dy(dy), L.dgrad(),
+                                 L.wgrad()), reps)
+    t_nv = _time(torch, lambda: NB.backward(dy), reps)
+    stages = {"requant_x_w": lambda: NB.requant(), "quantize_dy_both": lambda: NB.quantize_dy(dy),
+              "dgrad": NB.dgrad, "wgrad": NB.wgrad}
+    t_st = {n: round(_time(torch, f, reps), 4) for n, f in stages.items()}
+    # exact gradients of the dequantized forward operands
+    torch.cuda.synchronize()
+    off = L.perm["offsets"].tolist()
+    p = L.perm
+    X = _dequant_nvfp4(torch, p["codes"], p["scales"], p["outer"])                  # [cap, K]
+    W = _dequant_nvfp4(torch, L.wq[0], L.wq[1], L.wq[2].repeat_interleave(N))       # [E*N, K]
+    dyf = dy.float()
+    dx_ex = torch.zeros((T * k, K), dtype=torch.float32, device="cuda")
+    dw_ex = torch.zeros((E, N, K), dtype=torch.float32, device="cuda")
+    for g in range(E):
+        a, b = off[g], off[g + 1]
+        dx_ex[a:b] = dyf[a:b] @ W[g * N:(g + 1) * N]
+        dw_ex[g] = dyf[a:b].t() @ X[a:b]
+    M = off[-1]
+    rel = lambda a, ref: float((a - ref).norm() / ref.norm())
+    out = {}
+    for name, run, dxb, dwb in (("mxfp8", lambda: (L.requant_x(), L.requant_w(), L.quantize_dy(dy),
+                                                   L.dgrad(), L.wgrad()), L.dx, L.dw),
+                                ("nvfp4", lambda: NB.backward(dy), NB.dx, NB.dw)):
+        sdx = torch.zeros_like(dx_ex)
+        sdw = torch.zeros_like(dw_ex)
+        first = None
+        seed0 = L.seed
+        for i in range(n_seeds):
+            L.seed = seed0 + i
+            run()
+            sdx += dxb.float()
+            sdw += dwb
+            if first is None:
+                torch.cuda.synchronize()
+                first = (rel(dxb[:M].float(), dx_ex[:M]), rel(dwb, dw_ex))
+        L.seed = seed0
+        out[name] = {"rel_err_dx": round(first[0], 5), "rel_err_dw": round(first[1], 5),
+                     "rel_bias_dx": round(rel(sdx[:M] / n_seeds, dx_ex[:M]), 5),
+                     "rel_bias_dw": round(rel(sdw / n_seeds, dw_ex), 5)}
+    out["mxfp8"]["ms_backward"] = round(t_mx, 4)
+    out["nvfp4"]["ms_backward"] = round(t_nv, 4)
+    out["nvfp4"]["stages_ms"] = t_st
+    out["seeds_for_bias"] = n_seeds
+    out["note"] = ("error: one step against the exact gradient of the dequantized forward operands; "
+                   "bias: the mean over the seeds against it (includes the seeds' noise / sqrt(n))")
+    return out
+
+
 def tile16_compare(torch, reps):
     import precision_moe_numerics_nvfp4_amd as nv
     from workloads import gen
@@ -407,6 +489,9 @@ def extras(torch, reps=10):
     # gather in expert order, the grouped GEMM; next to the NVFP4 forward's
     out["mxfp8_forward_small_moe"] = mxfp8_forward_compare(torch, reps)
     torch.cuda.empty_cache()
+    # the NVFP4 backward next to the MXFP8 one: time, error, bias
+    out["nvfp4_backward_small_moe"] = nvfp4_backward_compare(torch, reps)
+    torch.cuda.empty_cache()
     # the rejected 16x16-tile scaling (ablation): weight quantization speed next
     # to the 16-element blocks, same weights, one outer scale per expert
     out["tile16_weight_quantize"] = tile16_compare(torch, reps)
@@ -503,7 +588,10 @@ def main():
         from precision_moe_numerics_nvfp4_amd import build as _b
         _b.build()
     if args.only:
-        print(json.dumps({args.only: ffn_workload(torch, args.only, max(args.steps, 1))}))
+        reps = max(args.steps, 1)
+        rec = (nvfp4_backward_compare(torch, reps) if args.only == "nvfp4-bwd"
+               else ffn_workload(torch, args.only, reps))
+        print(json.dumps({args.only: rec}))
         return
     print("bench: small MoE layer step", file=sys.stderr, flush=True)
     r = main_step_bench(args, torch)

@@ -413,7 +413,8 @@ NVFP4MOE_API int nvfp4_quantize_sr(const void* x, int x_dtype, int64_t rows, int
  *   group g's block [cols, L] at element g * cols * L, element (k, p) at
  *   g * cols * L + k * L + (p - padded_offsets[g]): the transposed weights
  *   [G, K, N] of the dgrad.
- * out_outer holds scratch during the call. Requires cols % 128 == 0,
+ * out_codes and out_outer hold scratch during the call; offsets[G] must not
+ * exceed rows. Requires cols % 128 == 0,
  * P % 128 == 0, codes, out_codes 16-byte aligned, scales 8-byte aligned.
  */
 NVFP4MOE_API int nvfp4_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,

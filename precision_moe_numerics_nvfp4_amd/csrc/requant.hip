@@ -10,8 +10,8 @@
 //  * the NVFP4 backward (nvfp4_requant_sr, nvfp4_quantize_sr colwise): the
 //    same transposes with NVFP4 output: blocks of 16 tokens (two neighbouring
 //    lanes), E4M3 block scales rounded up, E2M1 codes rounded stochastically,
-//    one outer scale per group from a maximum pass over the group's rows
-//    (k_group_amax_rows) run before; optionally written per group
+//    one outer scale per group from maximum passes over the group's rows
+//    (k_row_amax, k_group_max) run before; optionally written per group
 //    ([G, cols, group length], the transposed weights of each expert).
 //
 // Output [cols, P]: input rows [offsets[g], offsets[g+1]) of group g land in
@@ -79,68 +79,94 @@ struct Tile<Src::F32> {
   float v[TP][PITCH];
 };
 
-// Maximum magnitude of each group's rows, as float bits (non-negative floats
-// order like their bits): one wavefront per row, rows walked by the grid up to
-// offsets[G]; NVFP4 rows give max |e2m1 * S| times their outer scale, the
-// value the transpose dequantizes them to. bits must be zero beforehand.
+// Group maxima for the NVFP4 outputs, in two passes without atomics:
+// k_row_amax writes each live row's maximum magnitude (float bits) to a
+// scratch array, k_group_max reduces each group's rows with one workgroup.
+// NVFP4 rows give max |e2m1 * S| times their outer scale, the value the
+// transpose dequantizes them to (rounding is monotone, so the maximum of the
+// rounded products is the rounded product of the maximum).
 template <Src S>
-__global__ __launch_bounds__(256) void k_group_amax_rows(
+__global__ __launch_bounds__(256) void k_row_amax(
     const void* __restrict__ src, const uint8_t* __restrict__ src_scales,
     const float* __restrict__ src_outer, int64_t rpg, int64_t cols,
-    const int64_t* __restrict__ offsets, int G, uint32_t* __restrict__ bits) {
+    const int64_t* __restrict__ offsets, int G, uint32_t* __restrict__ row_bits) {
   const int lane = threadIdx.x & 63;
   const int64_t rows = offsets[G];
-  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows;
-       r += (int64_t)gridDim.x * 4) {
+  // lane-partial maximum of one 16-byte chunk at byte c of row r
+  auto chunk_max = [&](int64_t r, int64_t c) -> float {
     float m = 0.0f;
     if constexpr (S == Src::NVFP4) {
-      // 16 code bytes (two blocks) per lane and step
-      const uint8_t* rc = static_cast<const uint8_t*>(src) + r * (cols / 2);
-      const uint8_t* rs = src_scales + r * (cols / 16);
-      for (int64_t c = 16 * lane; c < cols / 2; c += 16 * 64) {
-        const uint4 w = *reinterpret_cast<const uint4*>(rc + c);
-        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(rs + c / 8);
-        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) +
+                                                      r * (cols / 2) + c);
+      const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(src_scales + r * (cols / 16) + c / 8);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          uint32_t mx = 0;                    // largest magnitude code (order = value order)
+      for (int blk = 0; blk < 2; ++blk) {
+        uint32_t mx = 0;                      // largest magnitude code (order = value order)
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int n = 0; n < 8; ++n) mx = max(mx, (wd[2 * blk + h] >> (4 * n)) & 7u);
-          float e0, e1;
-          e2m1x2_to_f32(mx, 0, e0, e1);
-          m = fmaxf(m, __fmul_rn(e0, e4m3_pos_to_f32((sc2 >> (8 * blk)) & 0x7Fu)));
-        }
+          for (int n = 0; n < 8; ++n) mx = max(mx, (wd[2 * blk + h] >> (4 * n)) & 7u);
+        float e0, e1;
+        e2m1x2_to_f32(mx, 0, e0, e1);
+        m = fmaxf(m, __fmul_rn(e0, e4m3_pos_to_f32((sc2 >> (8 * blk)) & 0x7Fu)));
       }
-      m = __fmul_rn(m, src_outer[rpg ? r / rpg : r]);      // rounding is monotone
     } else {
       constexpr int EB = (S == Src::BF16) ? 2 : 4;
-      const uint8_t* rx = static_cast<const uint8_t*>(src) + r * cols * EB;
-      for (int64_t c = 16 * lane; c < cols * EB; c += 16 * 64) {
-        const uint4 w = *reinterpret_cast<const uint4*>(rx + c);
-        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) +
+                                                      r * cols * EB + c);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (S == Src::BF16) {
-            m = fmaxf(m, fabsf(u2f(wd[j] << 16)));
-            m = fmaxf(m, fabsf(u2f(wd[j] & 0xFFFF0000u)));
-          } else {
-            m = fmaxf(m, fabsf(u2f(wd[j])));
-          }
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (S == Src::BF16) {
+          m = fmaxf(m, fabsf(u2f(wd[j] << 16)));
+          m = fmaxf(m, fabsf(u2f(wd[j] & 0xFFFF0000u)));
+        } else {
+          m = fmaxf(m, fabsf(u2f(wd[j])));
         }
       }
     }
-    m = wave_max(m);
-    if (lane == 0) {
-      int lo = 0, hi = G;                   // last g with offsets[g] <= r
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (offsets[mid] <= r) lo = mid; else hi = mid;
-      }
-      atomicMax(bits + lo, f2u(m));
+    return m;
+  };
+  const int64_t row_bytes = S == Src::NVFP4 ? cols / 2 : cols * (S == Src::BF16 ? 2 : 4);
+  constexpr int U = 4;                        // rows whose loads are in flight together
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t rb = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * U; rb < rows; rb += nw * U) {
+    float m[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = 0.0f;
+    for (int64_t c = 16 * lane; c < row_bytes; c += 16 * 64) {
+      float part[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) part[u] = chunk_max(rb + u < rows ? rb + u : rows - 1, c);
+#pragma unroll
+      for (int u = 0; u < U; ++u) m[u] = fmaxf(m[u], part[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = rb + u;
+      float mu = wave_max(m[u]);
+      if constexpr (S == Src::NVFP4) mu = __fmul_rn(mu, src_outer[rpg ? (r < rows ? r : 0) / rpg
+                                                                        : (r < rows ? r : 0)]);
+      if (lane == 0 && r < rows) row_bits[r] = f2u(mu);
     }
   }
+}
+
+// bits[g] = maximum of row_bits over group g's rows (0 for an empty group).
+__global__ __launch_bounds__(256) void k_group_max(const uint32_t* __restrict__ row_bits,
+                                                   const int64_t* __restrict__ offsets,
+                                                   uint32_t* __restrict__ bits) {
+  __shared__ uint32_t part[4];
+  const int g = blockIdx.x;
+  const int64_t a = offsets[g], b = offsets[g + 1];
+  uint32_t m = 0;
+  for (int64_t r = a + threadIdx.x; r < b; r += 256) m = max(m, row_bits[r]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) bits[g] = max(max(part[0], part[1]), max(part[2], part[3]));
 }
 
 __global__ void k_zero_u32(uint32_t* __restrict__ p, int n) {
@@ -431,8 +457,8 @@ hipError_t run(const void* src, const uint8_t* sc, const float* so, int64_t rpg,
   return hipGetLastError();
 }
 
-// NVFP4 output: zero the group maxima (kept in out_outer), take them, run the
-// transpose, turn the maxima into outer scales.
+// NVFP4 output: row maxima into out (free until the transpose writes it),
+// group maxima into out_outer, the transpose, maxima into outer scales.
 template <Src S, bool BLK>
 hipError_t run_nv(const void* src, const uint8_t* sc, const float* so, int64_t rpg, int64_t cols,
                   const int64_t* offsets, const int64_t* padded, int G, int64_t P, uint64_t seed,
@@ -440,13 +466,16 @@ hipError_t run_nv(const void* src, const uint8_t* sc, const float* so, int64_t r
                   int64_t m_cap, hipStream_t stream) {
   if (G == 0) return hipSuccess;
   uint32_t* bits = reinterpret_cast<uint32_t*>(out_outer);
-  k_zero_u32<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(bits, G);
+  uint32_t* row_bits = reinterpret_cast<uint32_t*>(out);
   if (cols > 0 && m_cap > 0) {
-    int64_t grid = (m_cap + 3) / 4;
-    const int64_t most = (int64_t)device_cu_count() * 16;
+    int64_t grid = (m_cap + 15) / 16;         // four rows per wavefront and round
+    const int64_t most = (int64_t)device_cu_count() * 8;
     if (grid > most) grid = most;
-    k_group_amax_rows<S><<<(unsigned)grid, 256, 0, stream>>>(src, sc, so, rpg, cols, offsets, G,
-                                                             bits);
+    k_row_amax<S><<<(unsigned)grid, 256, 0, stream>>>(src, sc, so, rpg, cols, offsets, G,
+                                                      row_bits);
+    k_group_max<<<(unsigned)G, 256, 0, stream>>>(row_bits, offsets, bits);
+  } else {
+    k_zero_u32<<<(unsigned)((G + 255) / 256), 256, 0, stream>>>(bits, G);
   }
   hipError_t e = run<S, true, false, true, BLK>(src, sc, so, rpg, 0, cols, offsets, padded, G, P,
                                                 seed, tag, out, out_sc, stream, nullptr, nullptr,

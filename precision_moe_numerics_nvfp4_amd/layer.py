@@ -8,6 +8,11 @@ re-quantize the saved NVFP4 activations and weights to MXFP8 with stochastic
 rounding through a float32 transpose, quantize dY to MXFP8 in both
 orientations, run the dgrad and wgrad grouped GEMMs.
 
+Also here: the expert FFN around the layer (ExpertFFNStep: down-projection,
+per-token re-quantization of the intermediate, weighted combine, backward
+through both projections) and the NVFP4 backward (NVFP4BackwardStep), the
+alternative the pages report as tried first and given up.
+
 Every step is a library call on the current stream; buffers are allocated
 once here (torch is the device allocator) so a step allocates nothing.
 """
@@ -196,3 +201,57 @@ class ExpertFFNStep:
         self.quantize_weights(w1, w2)
         self.forward(x, topk_ids, gate)
         self.backward(dout, gate)
+
+
+class NVFP4BackwardStep:
+    """The layer's backward with NVFP4 gradient operands instead of MXFP8, on
+    the saved forward state of an ExpertLayerStep: saved activations and
+    weights re-quantized to NVFP4 through a float32 transpose, dY quantized to
+    NVFP4 in both orientations, all with stochastic rounding; dgrad on the
+    forward grouped GEMM (per-expert transposed weights), wgrad on its
+    weight-gradient mode. Token groups of the transposed operands are padded
+    to 128. Philox tags: 5 = activations, 6 = weights, 7 = dY row-wise,
+    8 = dY transposed."""
+
+    def __init__(self, layer, device="cuda"):
+        self.L = layer
+        T, K, N, E, k = layer.T, layer.K, layer.N, layer.E, layer.k
+        dev = torch.device(device)
+        u8, f32 = torch.uint8, torch.float32
+        cap = T * k
+        self.P = ((cap + 127 * E + 127) // 128) * 128
+        P = self.P
+        e = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=dev)
+        nvfp4 = lambda r, c, n_outer: (e(r, c // 2), e(r, c // 16), e(n_outer, dt=f32))
+        self.poff = e(E + 1, dt=torch.int64)
+        self.xT = nvfp4(K, P, E)
+        self.wT = nvfp4(E * K, N, E)
+        self.dy = nvfp4(cap, N, cap)
+        self.dyT = nvfp4(N, P, E)
+        self.dx = e(cap, K, dt=layer.dx.dtype)
+        self.dw = e(E, N, K, dt=f32)
+
+    def requant(self):
+        L, p = self.L, self.L.perm
+        B.moe_padded_offsets(p["offsets"], 128, out=self.poff)
+        B.nvfp4_requant_sr(p["codes"], p["scales"], p["outer"], p["offsets"], self.poff, self.P,
+                           L.seed, 5, out=self.xT)
+        B.nvfp4_requant_sr(*L.wq, L.w_off, L.w_off, L.E * L.N, L.seed, 6, rows_per_group=L.N,
+                           per_group_layout=True, out=self.wT)
+
+    def quantize_dy(self, dy):
+        L, p = self.L, self.L.perm
+        B.nvfp4_quantize_sr(dy, L.seed, 7, *self.dy)
+        B.nvfp4_quantize_sr_colwise(dy, p["offsets"], self.poff, self.P, L.seed, 8, out=self.dyT)
+
+    def dgrad(self):
+        return B.moe_fwd_grouped_gemm(*self.dy, *self.wT, self.L.perm["offsets"], y=self.dx)
+
+    def wgrad(self):
+        return B.moe_bwd_wgrad_nvfp4(self.dyT, self.xT, self.poff, self.L.N, self.L.K, dw=self.dw)
+
+    def backward(self, dy):
+        self.requant()
+        self.quantize_dy(dy)
+        self.dgrad()
+        self.wgrad()
