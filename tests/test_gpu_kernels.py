@@ -438,8 +438,14 @@ def _mx(x):
     return MX.quantize_rne(np.asarray(x, np.float32))
 
 
-@pytest.mark.parametrize("counts,N,K", [([100, 0, 37, 250], 256, 384), ([64], 512, 256), ([129, 3], 128, 128)])
-def test_dgrad(nv, counts, N, K):
+# 128-row tiles (few rows per group); 256 x 128 tiles (256-row tiles that
+# would not fill the chip: ragged groups, an empty one, a 32-row contraction
+# tail); 256 x 256 tiles (a large capacity)
+@pytest.mark.parametrize("counts,N,K,extra", [([100, 0, 37, 250], 256, 384, 33), ([64], 512, 256, 33),
+                                              ([129, 3], 128, 128, 33),
+                                              ([300, 700, 0, 600], 512, 256, 33),
+                                              ([1000, 24], 256, 512, 8000)])
+def test_dgrad(nv, counts, N, K, extra):
     import torch
     off, pad = _groups_from_counts(counts)
     M, G = int(off[-1]), len(counts)
@@ -447,7 +453,7 @@ def test_dgrad(nv, counts, N, K):
     wT = gen.normal(801 + N, 1, (K, G * N), std=0.02)
     dq, de = _mx(dy)
     wq, we = _mx(wT)
-    cap = M + 33
+    cap = M + extra
     ddq = torch.zeros((cap, N), dtype=torch.uint8, device="cuda")
     ddq[:M] = to_dev(dq)
     dde = torch.zeros((cap, N // 32), dtype=torch.uint8, device="cuda")
