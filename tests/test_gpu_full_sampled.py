@@ -1,0 +1,292 @@
+"""GPU parity of the expert FFN and of the NVFP4 backward at the full workload
+sizes, in the launch configuration the benchmark times (ExpertFFNStep and
+NVFP4BackwardStep on the same shapes and inputs).
+
+Each check isolates one call: its oracle inputs are the GPU's outputs of the
+calls before it. Quantizers are compared bit for bit, on the whole tensor
+where the oracle is quick and otherwise on sampled rows (a row-wise quantizer
+row depends on nothing else) or sampled output rows of a transpose (the
+oracle's stochastic rounding takes the draw index base of the sampled rows);
+GEMMs on sampled rows (dgrad, forward) or sampled experts and rows (wgrad),
+within 1e-3 of the group's largest magnitude plus half a bfloat16 unit where
+the output is bfloat16.
+"""
+
+import numpy as np
+import pytest
+
+from helpers import ensure_built, from_dev, to_dev
+from oracle import ffn as FF
+from oracle import formats as F
+from oracle import gemm as GM
+from oracle import mxfp8 as MX
+from oracle import nvfp4 as Q
+from oracle import nvfp4_bwd as NB
+from oracle import permute as PM
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    ensure_built()
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import precision_moe_numerics_nvfp4_amd as nv
+    return nv
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _f64(a):
+    a = np.asarray(a)
+    return (F.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+def _close(got, ref, bf16_out, what, tol=1e-3):
+    got = _f64(got)
+    bound = tol * np.abs(ref).max() + (2.0 ** -8 * np.abs(ref) if bf16_out else 0.0)
+    d = np.abs(got - ref)
+    assert np.all(d <= bound + 1e-38), f"{what}: worst {d.max():.3e}"
+
+
+def _sample_rows(off, n, seed, n_groups=6):
+    """n random routed rows plus the first and last row of a few groups (the
+    first, the last and random ones)."""
+    M = int(off[-1])
+    G = off.shape[0] - 1
+    r = np.random.default_rng(seed)
+    gs = np.unique(np.concatenate([[0, G - 1], r.choice(G, min(G, n_groups), replace=False)]))
+    s = np.concatenate([r.choice(M, min(n, M), replace=False), off[gs], off[gs + 1] - 1])
+    return np.unique(s[(s >= 0) & (s < M)])
+
+
+def _mx_requant_rows(q, off, poff, P, seed, tag, c0, rpg=None, ncols=32):
+    """Output rows c0 .. c0+ncols of mxfp8_requant_sr (the draws keep their
+    absolute index): a column slice of the saved NVFP4 tensor."""
+    codes, scales, outer = q
+    v = Q.dequantize(codes[:, c0 // 2:(c0 + ncols) // 2], scales[:, c0 // 16:(c0 + ncols) // 16],
+                     outer, rows_per_group=rpg)
+    t = MX.transpose_grouped(v, off, poff, P)
+    return MX.quantize_sr(t, seed, tag, idx_base=c0 * P)
+
+
+def _mx_deq(q):
+    return MX.dequantize(*q)
+
+
+# ---------------------------------------------------------------- FFN
+
+def _ffn_inputs(shape):
+    if shape == "small_moe":
+        c = gen.ffn_case(2, T=4096, K=1024, F=2048, E=8, k=2)
+        return (c["x"], c["w1"].reshape(8 * 2048, 1024), c["w2"].reshape(8 * 1024, 2048), c["topk"],
+                c["gate"], c["dout"], 8, 2048, 0)
+    w3 = gen.expert_share()
+    T, K = w3["T"], w3["K"]
+    return (w3["x"], w3["w1"], w3["w2"], w3["topk"], gen.gates(3, T, 8),
+            gen.to_bf16_bits(gen.normal(3, 3, (T, K), std=1e-3)), w3["E"], w3["N"], w3["e0"])
+
+
+@pytest.mark.parametrize("shape", ["small_moe", "expert_share"])
+def test_expert_ffn_full_size_sampled(nv, shape):
+    from precision_moe_numerics_nvfp4_amd.layer import ExpertFFNStep
+    x, w1, w2, topk, gate, dout, E, Fw, e0 = _ffn_inputs(shape)
+    T, K = x.shape
+    k = topk.shape[1]
+    seed = 0x5EED0002
+    print(f"[ffn full] {shape}: T={T} K={K} F={Fw} E={E} k={k}", flush=True)
+    L = ExpertFFNStep(T, K, Fw, E, k, e0=e0, seed=seed)
+    L.step(to_dev(x), to_dev(w1), to_dev(w2), to_dev(topk), to_dev(gate), to_dev(dout))
+    _sync()
+    h = from_dev
+    rng = np.random.default_rng(7)
+    # quantizers: sampled tokens and experts
+    toks = np.sort(rng.choice(T, 256, replace=False))
+    for got, ref in zip(L.xq, Q.quantize(x[toks])):
+        assert np.array_equal(_bits(h(got)[toks]) if ref.dtype == np.float32 else h(got)[toks],
+                              _bits(ref) if ref.dtype == np.float32 else ref)
+    for g in sorted({0, E // 2, E - 1}):
+        for wt, q, n in ((w1, L.w1q, Fw), (w2, L.w2q, K)):
+            sl = slice(g * n, (g + 1) * n)
+            c, s, o = Q.quantize(wt[sl], rows_per_group=n)
+            assert np.array_equal(h(q[0][sl]), c) and np.array_equal(h(q[1][sl]), s)
+            assert _bits(h(q[2])[g]) == _bits(o)[0]
+    # permutation and its inverse: whole
+    off, poff, rt, rs = PM.permute(topk, e0, E)
+    M = int(off[-1])
+    p = {kk: h(v) for kk, v in L.perm.items()}
+    assert np.array_equal(p["offsets"], off) and np.array_equal(p["padded_offsets"], poff)
+    assert np.array_equal(p["row_token"][:M], rt) and np.array_equal(p["row_slot"][:M], rs)
+    assert np.array_equal(p["pair_row"], FF.pair_rows(topk, e0, E))
+    xp = tuple(a[:M] for a in (p["codes"], p["scales"], p["outer"]))
+    samp = _sample_rows(off, 96, 8)
+    grp = np.searchsorted(off, samp, side="right") - 1
+    w1q = tuple(h(a) for a in L.w1q)
+    w2q = tuple(h(a) for a in L.w2q)
+    H, HQ = h(L.h), tuple(h(a) for a in L.hq)
+    Y2 = h(L.y2)
+    # forward GEMMs and the intermediate's quantizer on sampled rows
+    for g in np.unique(grp):
+        rows = samp[grp == g]
+        o1 = np.array([0, rows.size])
+        ref = GM.fwd_grouped(*(a[rows] for a in xp), w1q[0][g * Fw:(g + 1) * Fw],
+                             w1q[1][g * Fw:(g + 1) * Fw], w1q[2][g:g + 1], o1, Fw, accum="fp64")
+        _close(H[rows], ref, True, f"H group {g}")
+        for got, refq in zip((a[rows] for a in HQ), Q.quantize(H[rows])):
+            assert np.array_equal(_bits(got) if refq.dtype == np.float32 else got,
+                                  _bits(refq) if refq.dtype == np.float32 else refq)
+        ref = GM.fwd_grouped(*(a[rows] for a in HQ), w2q[0][g * K:(g + 1) * K],
+                             w2q[1][g * K:(g + 1) * K], w2q[2][g:g + 1], o1, K, accum="fp64")
+        _close(Y2[rows], ref, True, f"Y2 group {g}")
+    # combine on sampled tokens
+    pr = p["pair_row"]
+    y2full = np.zeros((T * k, K), np.uint16)
+    y2full[:M] = Y2[:M]
+    out = _f64(h(L.out)[toks])
+    ref = FF.combine(y2full, pr[toks], gate[toks])
+    mag = FF.combine(np.abs(_f64(y2full)), pr[toks], gate[toks])
+    assert np.all(np.abs(out - ref) <= (k + 1) * 2.0 ** -24 * mag + 2.0 ** -8 * np.abs(ref) + 1e-38)
+    # combine backward: dY2 on sampled rows (bit-exact), dgate on them
+    dy2 = h(L.dy2)
+    dy2_ref, dg_ref = FF.combine_bwd(dout, rt, rs, M, gate, Y2[:M])
+    assert np.array_equal(dy2[samp], FF._bf16(dy2_ref[samp]))
+    dg = h(L.dgate)
+    t_s, j_s = rt[samp], rs[samp]
+    dmag = np.sum(np.abs(_f64(dout)[t_s]) * np.abs(_f64(Y2[samp])), axis=1)
+    assert np.all(np.abs(dg[t_s, j_s] - dg_ref[t_s, j_s]) <= (K + 1) * 2.0 ** -24 * dmag + 1e-38)
+    P = L.P
+    # backward of each projection: quantizers on sampled rows / output rows, GEMMs sampled
+    for name, gy, y8, yT, sq, sT, wq, wT, tag_s, tag_w, Nout, Kin, dxb, dwb in (
+            ("down", dy2, L.dy2_8, L.dy2T, HQ, L.hT, w2q, L.w2T, FF.TAG_H, FF.TAG_W2, K, Fw,
+             L.dh, L.dw2),
+            ("up", h(L.dh), L.dh8, L.dhT, xp, L.xT, w1q, L.w1T, FF.TAG_X, FF.TAG_W1, Fw, K,
+             L.dxp, L.dw1)):
+        y8h = tuple(h(a) for a in y8)
+        r8 = MX.quantize_rowwise(gy[samp])
+        assert np.array_equal(y8h[0][samp], r8[0]) and np.array_equal(y8h[1][samp], r8[1]), name
+        yTh = tuple(h(a) for a in yT)
+        sTh = tuple(h(a) for a in sT)
+        wTh = tuple(h(a) for a in wT)
+        pt = int(poff[-1])
+        woff = np.arange(E + 1, dtype=np.int64) * Nout
+        for c0 in sorted({0, (Nout // 2) // 32 * 32, Nout - 32}):
+            cT = MX.quantize_colwise_grouped(gy[:M, c0:c0 + 32], off, poff, P)
+            assert np.array_equal(yTh[0][c0:c0 + 32, :pt], cT[0][:, :pt]), name
+            assert np.array_equal(yTh[1][c0:c0 + 32, :pt // 32], cT[1][:, :pt // 32]), name
+        for c0 in sorted({0, (Kin // 2) // 32 * 32, Kin - 32}):
+            ref = _mx_requant_rows(sq, off, poff, P, seed, tag_s, c0)
+            assert np.array_equal(sTh[0][c0:c0 + 32, :pt], ref[0][:, :pt]), name
+            assert np.array_equal(sTh[1][c0:c0 + 32, :pt // 32], ref[1][:, :pt // 32]), name
+            ref = _mx_requant_rows(wq, woff, woff, E * Nout, seed, tag_w, c0, rpg=Nout)
+            assert np.array_equal(wTh[0][c0:c0 + 32], ref[0]), name
+            assert np.array_equal(wTh[1][c0:c0 + 32], ref[1]), name
+        # dgrad rows: dX[r] = dY8[r] . W8[:, g*Nout:(g+1)*Nout]^T
+        DY = _mx_deq((y8h[0][samp], y8h[1][samp]))
+        dx = h(dxb)
+        for g in np.unique(grp):
+            sel = grp == g
+            Wg = _mx_deq((wTh[0][:, g * Nout:(g + 1) * Nout], wTh[1][:, g * Nout // 32:(g + 1) * Nout // 32]))
+            _close(dx[samp[sel]], DY[sel] @ Wg.T, True, f"{name} dgrad group {g}")
+        # wgrad: sampled experts, sampled output rows
+        dw = h(dwb)
+        for g in sorted({0, E - 1}):
+            a, b = int(poff[g]), int(poff[g + 1])
+            if b == a:
+                continue
+            nrows = np.sort(rng.choice(Nout, 24, replace=False))
+            A = _mx_deq((yTh[0][nrows, a:b], yTh[1][nrows, a // 32:b // 32]))
+            B = _mx_deq((sTh[0][:, a:b], sTh[1][:, a // 32:b // 32]))
+            ref = A @ B.T
+            d = np.abs(dw[g][nrows].astype(np.float64) - ref)
+            assert d.max() <= 1e-3 * np.abs(ref).max() + 1e-38, f"{name} wgrad expert {g}"
+    # un-permute sum of dX on sampled tokens
+    dxp = h(L.dxp)
+    dfull = np.zeros((T * k, K), np.uint16)
+    dfull[:M] = dxp[:M]
+    got = _f64(h(L.dx)[toks])
+    ref = FF.combine(dfull, pr[toks])
+    mag = FF.combine(np.abs(_f64(dfull)), pr[toks])
+    assert np.all(np.abs(got - ref) <= (k + 1) * 2.0 ** -24 * mag + 2.0 ** -8 * np.abs(ref) + 1e-38)
+
+
+# ---------------------------------------------------------- NVFP4 backward
+
+def test_nvfp4_backward_small_moe_full(nv):
+    """The small MoE layer (4096 tokens, d_model 1024, 8 experts, top-2, FFN
+    1024 -> 2048) with dY ~ N(0, 1e-3): every NVFP4 quantizer of the backward
+    on the whole tensors, dgrad on sampled rows, wgrad on sampled experts."""
+    import torch
+    from precision_moe_numerics_nvfp4_amd.layer import ExpertLayerStep, NVFP4BackwardStep
+    w = gen.small_moe()
+    T, K, N, E, k = w["T"], w["K"], w["N"], w["E"], w["k"]
+    dy = gen.backward_dy(T * k, N)
+    print(f"[nvfp4 bwd full] T={T} K={K} N={N} E={E}", flush=True)
+    L = ExpertLayerStep(T, K, N, E, k, out_dtype=torch.float32)
+    L.quantize_x(to_dev(w["x"]))
+    L.quantize_w(to_dev(w["w"]))
+    L.permute(to_dev(w["topk"]))
+    B = NVFP4BackwardStep(L)
+    B.backward(to_dev(dy))
+    _sync()
+    h = from_dev
+    off = h(L.perm["offsets"])
+    M = int(off[-1])
+    poff = NB.padded_offsets(off)
+    assert np.array_equal(h(B.poff), poff)
+    P, pt, seed = B.P, int(poff[-1]), L.seed
+    xp = tuple(h(a)[:M] for a in (L.perm["codes"], L.perm["scales"], L.perm["outer"]))
+    wq = tuple(h(a) for a in L.wq)
+    # the four quantizers, whole
+    ref = NB.requant_sr(*xp, off, poff, P, seed, NB.TAG_X)
+    got = tuple(h(a) for a in B.xT)
+    assert np.array_equal(_bits(got[2]), _bits(ref[2]))
+    assert np.array_equal(got[1][:, :pt // 16], ref[1][:, :pt // 16])
+    assert np.array_equal(got[0][:, :pt // 2], ref[0][:, :pt // 2])
+    ref = NB.requant_weights_sr(*wq, E, seed, NB.TAG_W)
+    for a, b in zip((h(t) for t in B.wT), ref):
+        assert np.array_equal(_bits(a) if b.dtype == np.float32 else a,
+                              _bits(b) if b.dtype == np.float32 else b)
+    ref = NB.quantize_sr_rows(dy, seed, NB.TAG_DY_ROW)
+    for a, b in zip((h(t) for t in B.dy), ref):
+        assert np.array_equal(_bits(a) if b.dtype == np.float32 else a,
+                              _bits(b) if b.dtype == np.float32 else b)
+    ref = NB.quantize_sr_grouped_T(Q._as_f32(dy[:M]), off, poff, P, seed, NB.TAG_DY_COL)
+    got = tuple(h(a) for a in B.dyT)
+    assert np.array_equal(_bits(got[2]), _bits(ref[2]))
+    assert np.array_equal(got[0][:, :pt // 2], ref[0][:, :pt // 2])
+    assert np.array_equal(got[1][:, :pt // 16], ref[1][:, :pt // 16])
+    # dgrad on sampled rows, wgrad on sampled experts and rows, from the GPU's operands
+    dyq = tuple(h(a) for a in B.dy)
+    wT = tuple(h(a) for a in B.wT)
+    samp = _sample_rows(off, 128, 9)
+    grp = np.searchsorted(off, samp, side="right") - 1
+    dx = h(B.dx)
+    for g in np.unique(grp):
+        rows = samp[grp == g]
+        ref = NB.dgrad(tuple(a[rows] for a in dyq), (wT[0][g * K:(g + 1) * K], wT[1][g * K:(g + 1) * K],
+                                                     wT[2][g:g + 1]), np.array([0, rows.size]), K,
+                       accum="fp64")
+        _close(dx[rows], ref, False, f"dgrad group {g}")
+    dyT = tuple(h(a) for a in B.dyT)
+    xT = tuple(h(a) for a in B.xT)
+    dw = h(B.dw)
+    rng = np.random.default_rng(10)
+    for g in (0, E - 1):
+        a, b = int(poff[g]), int(poff[g + 1])
+        nrows = np.sort(rng.choice(N, 32, replace=False))
+        A = Q.dequantize(dyT[0][nrows, a // 2:b // 2], dyT[1][nrows, a // 16:b // 16], None,
+                         apply_outer=False).astype(np.float64)
+        Bx = Q.dequantize(xT[0][:, a // 2:b // 2], xT[1][:, a // 16:b // 16], None,
+                          apply_outer=False).astype(np.float64)
+        ref = (A @ Bx.T) * float(dyT[2][g]) * float(xT[2][g])
+        d = np.abs(dw[g][nrows].astype(np.float64) - ref)
+        assert d.max() <= 1e-3 * np.abs(ref).max() + 1e-38, f"wgrad expert {g}"
