@@ -555,17 +555,35 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* lsm, const Operand& A, con
   asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");     // stage 0 landed
   Frag f0, f1;
   read(0, f0);
+  // One stage: the 12 DMA issues for stage kt+3 and the 24 fragment reads of
+  // stage kt+1 are spread over the 16 MFMAs of stage kt (one DMA and two
+  // reads after each of the first 12), the fragment masks after the last
+  // four. The MFMAs still queue behind the DMA issues (each holds the
+  // wavefront for tens of cycles), but less than when they come back to back.
+  auto stage = [&](int64_t kt_issue, int64_t kt_read, const Frag& cur, Frag& nxt) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt_issue);
+    read(kt_read, nxt);
+    mfmas(cur);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
+      if (m < 12) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                // 1 DMA issue
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                // 2 LDS reads
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);               // fragment masks
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
   for (int64_t kt = 0; kt < nk; kt += 2) {
     // stage kt+1 has landed once only stage kt+2's loads are pending; every
     // wavefront is past its reads of stage kt-1, whose buffer stage kt+3 reuses
     asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-    issue(kt + DS - 1);
-    read(kt + 1, f1);
-    mfmas(f0);
+    stage(kt + DS - 1, kt + 1, f0, f1);
     asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-    issue(kt + DS);
-    read(kt + 2, f0);
-    mfmas(f1);                         // all zero past the end
+    stage(kt + DS, kt + 2, f1, f0);     // all zero past the end
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");      // ring drained, LDS free
 }
