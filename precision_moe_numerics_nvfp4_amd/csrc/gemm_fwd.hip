@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ao,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bo,
     const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y,
-    int64_t P = 0) {
+    int64_t P, int skip_tails) {
   constexpr int TM = 4, TN = 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
 
@@ -384,7 +384,9 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
                   : part == 1 ? (rem > LT / 2 ? 1 : 0) : (rem != 0 && rem <= LT / 2 ? 1 : 0);
       return n * ntn;
     }, pre);
-    const int nfull = pre[G], nbig = pre[2 * G], total = pre[3 * G];
+    // skip_tails: the partial m-tiles of at most 128 rows are left to the
+    // streaming kernel, launched right after this one
+    const int nfull = pre[G], nbig = pre[2 * G], total = skip_tails ? nbig : pre[3 * G];
     if ((int)blockIdx.x >= total) return;
     const int t = (int)blockIdx.x;
     const int tt = t < nfull ? (int)xcd_tile(t, nfull)
@@ -715,7 +717,7 @@ template <int NS>
 hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
                        const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
                        int64_t m_cap, int64_t N, int64_t K, void* y, bool y_bf16,
-                       hipStream_t stream) {
+                       bool skip_tails, hipStream_t stream) {
   const size_t lds = (size_t)NS * kStageBytes;
   const int64_t tiles = ((m_cap + LT - 1) / LT + G) * (N / LT);   // bound on live tiles
   auto k = y_bf16 ? k_fwd_lds4<NS, true> : k_fwd_lds4<NS, false>;
@@ -726,7 +728,8 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
-  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, 0);
+  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, 0,
+                                           skip_tails ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -782,15 +785,23 @@ template <bool OUT_BF16>
 __global__ __launch_bounds__(512, 1) void k_fwd_stream(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ao,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bo,
-    const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y) {
+    const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y,
+    int tail) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
   float* red = reinterpret_cast<float*>(lsm + SK_S * SK_STAGE);      // [4][64 lanes][4]
   int64_t* off = reinterpret_cast<int64_t*>(lsm + SK_S * SK_STAGE + SK_RED);   // [G+1]
   int* pre = reinterpret_cast<int*>(off + G + 1);                     // [G+1]
   const int nnb = (int)(N / SK_N);
   for (int e = threadIdx.x; e <= G; e += 512) off[e] = offsets[e];
+  // Rows of group e that this launch covers: all of them, or (tail) only the
+  // last partial 256-row tile when it has at most 128 rows, the rows the
+  // 256 x 256 tile kernel leaves out; they end at the group's end either way.
+  auto rows_of = [&](int64_t a, int64_t b) -> int64_t {
+    const int64_t m = b - a, rem = m % LT;
+    return !tail ? m : (rem != 0 && rem <= LT / 2 ? rem : 0);
+  };
   tile_prefix(G, [&](int e) {
-    return (int)((offsets[e + 1] - offsets[e] + SK_T - 1) / SK_T) * nnb;
+    return (int)((rows_of(offsets[e], offsets[e + 1]) + SK_T - 1) / SK_T) * nnb;
   }, pre);
   const int total = pre[G];
   if ((int)blockIdx.x >= total) return;
@@ -818,7 +829,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
     u.g = __builtin_amdgcn_readfirstlane(tile_group(pre, G, t));
     const int loc = t - pre[u.g];
     u.nb = __builtin_amdgcn_readfirstlane(loc % nnb);
-    u.row0 = rfl64(off[u.g] + (int64_t)(loc / nnb) * SK_T);
+    u.row0 = rfl64(off[u.g + 1] - rows_of(off[u.g], off[u.g + 1]) + (int64_t)(loc / nnb) * SK_T);
     u.row_end = rfl64(off[u.g + 1]);
     return u;
   };
@@ -995,7 +1006,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
 hipError_t launch_stream(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
                          const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
                          int64_t m_cap, int64_t N, int64_t K, void* y, bool y_bf16,
-                         hipStream_t stream) {
+                         bool tail, hipStream_t stream) {
   auto k = y_bf16 ? k_fwd_stream<true> : k_fwd_stream<false>;
   const size_t base = (size_t)SK_S * SK_STAGE + SK_RED;
   const size_t lds = base + (size_t)(G + 1) * (sizeof(int64_t) + sizeof(int));
@@ -1007,10 +1018,13 @@ hipError_t launch_stream(const uint8_t* ac, const uint8_t* as, const float* ao, 
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
-  const int64_t bound = ((m_cap + SK_T - 1) / SK_T + G) * (N / SK_N);   // units, upper bound
+  int64_t rb = (m_cap + SK_T - 1) / SK_T + G;                  // row units, upper bound
+  if (tail && rb > (int64_t)G * (LT / 2 / SK_T)) rb = (int64_t)G * (LT / 2 / SK_T);
+  const int64_t bound = rb * (N / SK_N);
   const int64_t slots = device_cu_count();
   const int64_t grid = bound < slots ? bound : slots;
-  k<<<(unsigned)grid, 512, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y);
+  k<<<(unsigned)grid, 512, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y,
+                                          tail ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1043,12 +1057,21 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
   // a few rows per expert (decode): weight streaming, 16-row tiles
   if (m_cap <= 32 * (int64_t)G && K % SK_K == 0 && N % SK_N == 0 && G <= SK_MAXG &&
       ((m_cap + SK_T - 1) / SK_T + G) * (N / SK_N) < (int64_t)1 << 31)
-    return launch_stream(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, stream);
+    return launch_stream(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, false,
+                         stream);
   // 32-row tiles, the wavefronts split N
   if (m_cap <= 64 * (int64_t)G || N % 256 != 0 || G > 8192)
     return launch_cfg<32, 128, 1, 4>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
                                      stream);
-  return launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, stream);
+  // 256 x 256 tiles; the partial last m-tiles of at most 128 rows go to the
+  // streaming kernel right after (a second round of 256 x 256 workgroups for
+  // a few rows each would cost nearly as much as the first)
+  const bool tails = K % SK_K == 0 && N % SK_N == 0 && G <= SK_MAXG &&
+                     (int64_t)G * (LT / 2 / SK_T) * (N / SK_N) < (int64_t)1 << 31;
+  hipError_t e = launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, tails,
+                                stream);
+  if (e != hipSuccess || !tails) return e;
+  return launch_stream(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, true, stream);
 }
 
 // NVFP4 weight gradient (see WG above).
@@ -1068,7 +1091,7 @@ hipError_t launch_wgrad_nvfp4(const uint8_t* ac, const uint8_t* as, const float*
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, padded, G, N, K, dw, P);
+  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, padded, G, N, K, dw, P, 0);
   return hipGetLastError();
 }
 
