@@ -34,6 +34,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats -> two bf16 in one word (a in the low half), rounded to nearest
+// even by gfx950's packed conversion (one instruction; the same result as
+// f32_to_bf16_rne for every non-NaN input).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // ----------------------------------------------------------------- E2M1
 
 // Eight floats -> eight E2M1 codes packed in a word (element j in bits

@@ -36,10 +36,10 @@ template <bool BF16>
 __device__ __forceinline__ void store8(void* base, int64_t elem, const float (&v)[8]) {
   if constexpr (BF16) {
     uint4 a;
-    a.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-    a.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-    a.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
-    a.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+    a.x = pk_bf16(v[0], v[1]);
+    a.y = pk_bf16(v[2], v[3]);
+    a.z = pk_bf16(v[4], v[5]);
+    a.w = pk_bf16(v[6], v[7]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + elem) = a;
   } else {
     uint4* p = reinterpret_cast<uint4*>(static_cast<float*>(base) + elem);

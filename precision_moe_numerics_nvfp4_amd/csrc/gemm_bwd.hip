@@ -607,8 +607,8 @@ __device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)
       for (int q = 0; q < 4; ++q) {
         uint8_t* d = ep + r32 * RS + (j * 32 + 8 * q + 4 * half) * ES;
         if constexpr (ES == 2) {
-          const uint32_t lo = f32_to_bf16_rne(acc[i][j][4 * q]) | (f32_to_bf16_rne(acc[i][j][4 * q + 1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[i][j][4 * q + 2]) | (f32_to_bf16_rne(acc[i][j][4 * q + 3]) << 16);
+          const uint32_t lo = pk_bf16(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          const uint32_t hi = pk_bf16(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           *reinterpret_cast<uint2*>(d) = make_uint2(lo, hi);
         } else {
           *reinterpret_cast<float4*>(d) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],

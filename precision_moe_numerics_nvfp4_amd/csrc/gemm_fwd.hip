@@ -692,8 +692,8 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
         for (int t = 0; t < 4; ++t) v[t] = __fmul_rn(__fmul_rn(acc[i][j][4 * q + t], sx), sw);
         uint8_t* d = ep + r32 * RS + (j * 32 + 8 * q + 4 * half) * ES;
         if constexpr (OUT_BF16) {
-          const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+          const uint32_t lo = pk_bf16(v[0], v[1]);
+          const uint32_t hi = pk_bf16(v[2], v[3]);
           *reinterpret_cast<uint2*>(d) = make_uint2(lo, hi);
         } else {
           *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
@@ -982,8 +982,8 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
           for (int v = 0; v < 4; ++v) o[v] = __fmul_rn(__fmul_rn(acc[v], sx), sg);
           const int64_t col = (int64_t)u.nb * SK_N + 16 * wn + 4 * q;
           if constexpr (OUT_BF16) {
-            const uint32_t lo = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-            const uint32_t hi = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+            const uint32_t lo = pk_bf16(o[0], o[1]);
+            const uint32_t hi = pk_bf16(o[2], o[3]);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + row * N + col) =
                 make_uint2(lo, hi);
           } else {
