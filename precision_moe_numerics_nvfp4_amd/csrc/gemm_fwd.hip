@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ao,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bo,
     const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y,
-    int64_t P, int skip_tails) {
+    int64_t P, int tail_cus) {
   constexpr int TM = 4, TN = 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
 
@@ -384,9 +384,12 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
                   : part == 1 ? (rem > LT / 2 ? 1 : 0) : (rem != 0 && rem <= LT / 2 ? 1 : 0);
       return n * ntn;
     }, pre);
-    // skip_tails: the partial m-tiles of at most 128 rows are left to the
-    // streaming kernel, launched right after this one
-    const int nfull = pre[G], nbig = pre[2 * G], total = skip_tails ? nbig : pre[3 * G];
+    // tail_cus > 0 (the compute-unit count): when the full and larger
+    // partial tiles fit in one round of workgroups and the short tails would
+    // start a second one, the tails are left to the streaming kernel launched
+    // right after this one (it takes the same decision)
+    const int nfull = pre[G], nbig = pre[2 * G], all = pre[3 * G];
+    const int total = tail_cus > 0 && nbig <= tail_cus && all > tail_cus ? nbig : all;
     if ((int)blockIdx.x >= total) return;
     const int t = (int)blockIdx.x;
     const int tt = t < nfull ? (int)xcd_tile(t, nfull)
@@ -717,7 +720,7 @@ template <int NS>
 hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
                        const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
                        int64_t m_cap, int64_t N, int64_t K, void* y, bool y_bf16,
-                       bool skip_tails, hipStream_t stream) {
+                       int tail_cus, hipStream_t stream) {
   const size_t lds = (size_t)NS * kStageBytes;
   const int64_t tiles = ((m_cap + LT - 1) / LT + G) * (N / LT);   // bound on live tiles
   auto k = y_bf16 ? k_fwd_lds4<NS, true> : k_fwd_lds4<NS, false>;
@@ -729,7 +732,7 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
     attr_set[y_bf16] = true;
   }
   k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, 0,
-                                           skip_tails ? 1 : 0);
+                                           tail_cus);
   return hipGetLastError();
 }
 
@@ -793,13 +796,30 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
   int* pre = reinterpret_cast<int*>(off + G + 1);                     // [G+1]
   const int nnb = (int)(N / SK_N);
   for (int e = threadIdx.x; e <= G; e += 512) off[e] = offsets[e];
-  // Rows of group e that this launch covers: all of them, or (tail) only the
-  // last partial 256-row tile when it has at most 128 rows, the rows the
+  // Rows of group e that this launch covers: all of them, or (tail > 0) only
+  // the last partial 256-row tile when it has at most 128 rows, the rows the
   // 256 x 256 tile kernel leaves out; they end at the group's end either way.
   auto rows_of = [&](int64_t a, int64_t b) -> int64_t {
     const int64_t m = b - a, rem = m % LT;
     return !tail ? m : (rem != 0 && rem <= LT / 2 ? rem : 0);
   };
+  if (tail) {
+    // the 256 x 256 kernel's decision (tail = its compute-unit count): the
+    // tails are here only if its other tiles fit in one round and the tails
+    // would have started a second
+    const int ntn = (int)(N / LT);
+    tile_prefix(G, [&](int e) {
+      const int64_t m = offsets[e + 1] - offsets[e];
+      return (int)(m / LT + (m % LT > LT / 2 ? 1 : 0)) * ntn;
+    }, pre);
+    const int nbig = pre[G];
+    tile_prefix(G, [&](int e) {
+      const int64_t rem = (offsets[e + 1] - offsets[e]) % LT;
+      return rem != 0 && rem <= LT / 2 ? ntn : 0;
+    }, pre);
+    const int nsmall = pre[G];
+    if (!(nbig <= tail && nbig + nsmall > tail)) return;     // the same for the whole workgroup
+  }
   tile_prefix(G, [&](int e) {
     return (int)((rows_of(offsets[e], offsets[e + 1]) + SK_T - 1) / SK_T) * nnb;
   }, pre);
@@ -1024,7 +1044,7 @@ hipError_t launch_stream(const uint8_t* ac, const uint8_t* as, const float* ao, 
   const int64_t slots = device_cu_count();
   const int64_t grid = bound < slots ? bound : slots;
   k<<<(unsigned)grid, 512, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y,
-                                          tail ? 1 : 0);
+                                          tail ? (int)device_cu_count() : 0);
   return hipGetLastError();
 }
 
@@ -1063,13 +1083,14 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
   if (m_cap <= 64 * (int64_t)G || N % 256 != 0 || G > 8192)
     return launch_cfg<32, 128, 1, 4>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
                                      stream);
-  // 256 x 256 tiles; the partial last m-tiles of at most 128 rows go to the
-  // streaming kernel right after (a second round of 256 x 256 workgroups for
-  // a few rows each would cost nearly as much as the first)
+  // 256 x 256 tiles; when the partial last m-tiles of at most 128 rows would
+  // be all that runs in a second round of 256 x 256 workgroups (nearly as
+  // costly as the first, for a few rows each), they go to the streaming
+  // kernel right after instead (decided on the device from the offsets)
   const bool tails = K % SK_K == 0 && N % SK_N == 0 && G <= SK_MAXG &&
                      (int64_t)G * (LT / 2 / SK_T) * (N / SK_N) < (int64_t)1 << 31;
-  hipError_t e = launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, tails,
-                                stream);
+  hipError_t e = launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
+                                tails ? (int)device_cu_count() : 0, stream);
   if (e != hipSuccess || !tails) return e;
   return launch_stream(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, true, stream);
 }

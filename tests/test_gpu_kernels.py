@@ -393,15 +393,17 @@ def _fwd_counts_case(seed, counts, K, N):
     return xc[:M], xs[:M], xo[:M], wc, ws, wo, off
 
 
-# Groups whose row count is just past a multiple of 256. When K % 512 == 0
-# the last partial 256-row tile of a group runs in the weight-streaming
-# kernel if it has at most 128 rows (tails of 5, 32, 31, 33, 44, 1, 128 and
-# whole groups of 20 and 100 rows) and in the 256 x 256 kernel otherwise (129
-# and 200 rows); with K = 384 every tail is a partial 256-row tile.
+# Groups whose row count is just past a multiple of 256 (tails of 5, 32, 31,
+# 33, 44, 1, 128 rows, larger partial tiles of 129 and 200 rows, whole
+# groups of 20 and 100 rows): with at most one round of workgroups every tail
+# is a partial 256-row tile. The last case has 300 tiles of 256 x 256 on
+# MI355X's 256 compute units, 100 of them full: its 200 tails (44 and 100
+# rows) run in the weight-streaming kernel after one round of full tiles.
 @pytest.mark.parametrize("counts,K,N", [([261, 544, 33, 20, 256, 0, 300, 287], 1024, 512),
                                         ([261, 544, 33, 20, 256, 0, 300, 287], 384, 256),
                                         ([257, 288, 300], 1536, 256),
-                                        ([384, 385, 100, 0, 456, 1037], 512, 768)])
+                                        ([384, 385, 100, 0, 456, 1037], 512, 768),
+                                        ([300, 100] * 100, 512, 256)])
 def test_fwd_grouped_gemm_tails(nv, counts, K, N):
     import torch
     ac, asc, ao, wc, ws, wo, off = _fwd_counts_case(800 + K, counts, K, N)
