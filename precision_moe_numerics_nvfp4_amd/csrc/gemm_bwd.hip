@@ -416,15 +416,49 @@ __global__ __launch_bounds__(256, 1) void k_wgrad(const uint8_t* __restrict__ dy
 // fragments and its scale set to 1.
 constexpr int DK = 64;                                // contraction elements per stage
 constexpr int DS = 4;                                 // stages in the ring
-constexpr int D_A = 0, D_B = 256 * DK;                // code planes [256][64]
-constexpr int D_SC = 2 * 256 * DK;                    // scale planes [op][byte][256 rows][4]
-constexpr int D_STAGE = D_SC + 2 * 2 * 256 * 4;       // 36 KiB
-constexpr int D_DMA = 12;                             // DMA instructions per stage and wavefront
+
+// Workgroup tile BM x BN (rows of A x rows of B), 2 x 2 wavefronts of
+// (BM/2) x (BN/2), that is TM x TN MFMA tiles of 32 x 32 each. A code DMA
+// instruction fills 16 rows, a scale DMA instruction one scale byte of 64
+// rows; the scale instructions are dealt to the wavefronts round-robin, the
+// count padded to a multiple of 4 by repeating the last ones (same bytes to
+// the same place), so every wavefront issues NL loads per stage.
+template <int BM, int BN>
+struct DmaTile {
+  static constexpr int TM = BM / 64, TN = BN / 64;
+  static constexpr int CA = BM / 64, CB = BN / 64;    // code loads per stage and wavefront
+  static constexpr int NA = BM / 64, NB = BN / 64;    // 64-row blocks
+  static constexpr int SI = 2 * (NA + NB);            // scale loads per stage (workgroup)
+  static constexpr int SW = (SI + 3) / 4;             // ... per wavefront
+  static constexpr int NL = CA + CB + SW;
+  static constexpr int A0 = 0, B0 = BM * DK;          // code planes [rows][64]
+  static constexpr int SC = (BM + BN) * DK;           // scale planes [op][byte][rows][4]
+  static constexpr int STAGE = SC + 2 * (BM + BN) * 4;
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && SI >= 4, "tile shape");
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void mainloop_dma(uint8_t* lsm, const Operand& A, const Operand& B,
-                                             int64_t L, f32x16 (&acc)[4][4]) {
+// s_waitcnt vmcnt(N) then s_barrier (N an immediate: the tile shapes' load counts)
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N == 11 || N == 12 || N == 22 || N == 24, "add the count");
+  if constexpr (N == 11) asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 22) asm volatile("s_waitcnt vmcnt(22)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+}
+
+// Workgroup tile (64 TM_) x (64 TN_). (A class template's member rather than
+// a function template: the kernels that call it are templates whose host-side
+// instantiation would otherwise reject the device-only callee.)
+template <int TM_, int TN_>
+struct DmaLoop {
+static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const Operand& B,
+                                           int64_t L, f32x16 (&acc)[TM_][TN_]) {
+  constexpr int BM = 64 * TM_, BN = 64 * TN_;
+  using C = DmaTile<BM, BN>;
+  constexpr int TM = C::TM, TN = C::TN, NL = C::NL;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -438,7 +472,8 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* lsm, const Operand& A, con
 #pragma unroll
   for (int o = 0; o < 2; ++o) {
     const Operand& X = o ? B : A;
-    const int64_t n = X.row_end - X.row0 < 256 ? X.row_end - X.row0 : 256;   // the tile's rows
+    const int64_t cap = o ? BN : BM;
+    const int64_t n = X.row_end - X.row0 < cap ? X.row_end - X.row0 : cap;   // the tile's rows
     nrow[o] = __builtin_amdgcn_readfirstlane((int)n);
     ld[o] = X.ld;
     c0[o] = X.c0;
@@ -448,77 +483,92 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* lsm, const Operand& A, con
                                               uniform_u32(n * (X.ld / 32)), kBufferWord3);
   }
   // lane offsets: code instruction i of this wavefront fills rows 16m .. 16m+15
-  // (m = 4i + wave; lane: row 16m + lane/4, position lane%4); scale instruction
-  // j fills byte (wave & 1) of rows 64j + lane of operand wave >> 1
-  uint32_t oq[2][4], oe[4];
+  // (m = 4i + wave; lane: row 16m + lane/4, position lane%4). Scale item q
+  // (q = 4j + wave; past the last item, q - 4) is byte `sbyte` of rows
+  // 64 blk + lane of operand `sop`: items A byte 0, A byte 1, B byte 0, B byte 1.
+  constexpr int CM = C::CA > C::CB ? C::CA : C::CB;
+  uint32_t oq[2][CM], oe[C::SW];
+  int sop[C::SW], sdst[C::SW];
 #pragma unroll
   for (int o = 0; o < 2; ++o)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < (o ? C::CB : C::CA); ++i) {
       const int row = 16 * (4 * i + wave) + (lane >> 2);
       const int piece = (lane & 3) ^ ((row >> 2) & 3);
       const int rr = row < nrow[o] ? row : 0;
       oq[o][i] = (uint32_t)(rr * ld[o] + c0[o] + piece * 16);
     }
-  const int so = wave >> 1, sb = wave & 1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 64 * j + lane;
-    const int rr = row < nrow[so] ? row : 0;
-    oe[j] = (uint32_t)(rr * (ld[so] / 32) + c0[so] / 32 + sb);
+  for (int j = 0; j < C::SW; ++j) {
+    int q = 4 * j + wave;
+    if (q >= C::SI) q -= 4;
+    const int o = q < 2 * C::NA ? 0 : 1;
+    const int qq = o ? q - 2 * C::NA : q, nb = o ? C::NB : C::NA;
+    const int byte = qq / nb, blk = qq - byte * nb;
+    const int row = 64 * blk + lane;
+    const int rr = row < nrow[o] ? row : 0;
+    sop[j] = __builtin_amdgcn_readfirstlane(o);
+    oe[j] = (uint32_t)(rr * (ld[o] / 32) + c0[o] / 32 + byte);
+    sdst[j] = __builtin_amdgcn_readfirstlane(
+        C::SC + ((o ? 2 * BM : 0) + byte * (o ? BN : BM) + 64 * blk) * 4);
   }
   // stage kt -> buffer kt % DS; past the end: offsets outside the ranges
   // (zeros, no memory traffic) so every stage has the same load count
   auto issue = [&](int64_t kt) {
-    uint8_t* st = lsm + (kt % DS) * D_STAGE;
+    uint8_t* st = lsm + (kt % DS) * C::STAGE;
     const bool real = kt < nk;
     const uint32_t away = real ? 0u : 0x40000000u;
     const uint32_t kq = real ? (uint32_t)(kt * DK) : 0u, ke = real ? (uint32_t)(kt * 2) : 0u;
 #pragma unroll
     for (int o = 0; o < 2; ++o)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < (o ? C::CB : C::CA); ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rq[o], (lds_void*)(st + (o ? D_B : D_A) + (4 * i + wave) * 1024), 16,
+            rq[o], (lds_void*)(st + (o ? C::B0 : C::A0) + (4 * i + wave) * 1024), 16,
             oq[o][i] + kq + away, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C::SW; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          so ? re[1] : re[0], (lds_void*)(st + D_SC + ((so * 2 + sb) * 256 + 64 * j) * 4), 1,
-          oe[j] + ke + away, 0, 0, 0);
+          sop[j] ? re[1] : re[0], (lds_void*)(st + sdst[j]), 1, oe[j] + ke + away, 0, 0, 0);
   };
 
   // fragment addresses (stage-relative)
-  int fa[4][2], fb[4][2], sa[4], sbo[4];
+  int fa[TM][2], fb[TN][2], sa[TM], sbo[TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ra = wm * 128 + i * 32 + r32, rb = wn * 128 + i * 32 + r32;
+  for (int i = 0; i < TM; ++i) {
+    const int ra = wm * (BM / 2) + i * 32 + r32;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      fa[i][c] = D_A + ra * DK + (((2 * c + half) ^ ((ra >> 2) & 3)) << 4);
-      fb[i][c] = D_B + rb * DK + (((2 * c + half) ^ ((rb >> 2) & 3)) << 4);
-    }
-    sa[i] = D_SC + ((0 * 2 + half) * 256 + ra) * 4;
-    sbo[i] = D_SC + ((1 * 2 + half) * 256 + rb) * 4;
+    for (int c = 0; c < 2; ++c) fa[i][c] = C::A0 + ra * DK + (((2 * c + half) ^ ((ra >> 2) & 3)) << 4);
+    sa[i] = C::SC + (half * BM + ra) * 4;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int rb = wn * (BN / 2) + j * 32 + r32;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) fb[j][c] = C::B0 + rb * DK + (((2 * c + half) ^ ((rb >> 2) & 3)) << 4);
+    sbo[j] = C::SC + (2 * BM + half * BN + rb) * 4;
   }
   struct Frag {
-    i32x8 a[4], b[4];
-    int32_t as[4], bs[4];
+    i32x8 a[TM], b[TN];
+    int32_t as[TM], bs[TN];
   };
   auto read = [&](int64_t kt, Frag& f) {
-    const uint8_t* st = lsm + (kt % DS) * D_STAGE;
+    const uint8_t* st = lsm + (kt % DS) * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TM; ++i) {
       const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + fa[i][0]);
       const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + fa[i][1]);
       f.a[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                      (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      const u32x4 y0 = *reinterpret_cast<const u32x4*>(st + fb[i][0]);
-      const u32x4 y1 = *reinterpret_cast<const u32x4*>(st + fb[i][1]);
-      f.b[i] = i32x8{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3],
-                     (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
       f.as[i] = *reinterpret_cast<const uint8_t*>(st + sa[i]);
-      f.bs[i] = *reinterpret_cast<const uint8_t*>(st + sbo[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const u32x4 y0 = *reinterpret_cast<const u32x4*>(st + fb[j][0]);
+      const u32x4 y1 = *reinterpret_cast<const u32x4*>(st + fb[j][1]);
+      f.b[j] = i32x8{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3],
+                     (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
+      f.bs[j] = *reinterpret_cast<const uint8_t*>(st + sbo[j]);
     }
     // Contraction elements past L are zero: MX block 1 of a last stage that
     // holds 32 elements, and whole stages past the end (the loop runs an even
@@ -527,49 +577,59 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* lsm, const Operand& A, con
     const int keep0 = rem > 0 ? -1 : 0, keep1 = rem > 32 ? -1 : 0;
     const int keeps = half ? keep1 : keep0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         f.a[i][e] &= keep0;
-        f.b[i][e] &= keep0;
         f.a[i][e + 4] &= keep1;
-        f.b[i][e + 4] &= keep1;
       }
       f.as[i] = keeps ? f.as[i] : 127;
-      f.bs[i] = keeps ? f.bs[i] : 127;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f.b[j][e] &= keep0;
+        f.b[j][e + 4] &= keep1;
+      }
+      f.bs[j] = keeps ? f.bs[j] : 127;
     }
   };
   auto mfmas = [&](const Frag& f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TN; ++j)
         // B (output-column operand) first: the lane then holds 4 consecutive columns
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f.b[j], f.a[i], acc[i][j], 0 /*E4M3*/, 0 /*E4M3*/, 0, f.bs[j], 0, f.as[i]);
   };
 
-  static_assert(D_DMA == 12 && DS == 4, "the wait counts assume 12 loads per stage, 4 stages");
+  static_assert(DS == 4 && 2 * NL < 64, "the wait counts assume 4 stages, NL loads per stage");
 #pragma unroll
   for (int p = 0; p < DS - 1; ++p) issue(p);
-  asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");     // stage 0 landed
+  wait_vm_barrier<2 * NL>();                                          // stage 0 landed
   Frag f0, f1;
   read(0, f0);
-  // One stage: the 12 DMA issues for stage kt+3 and the 24 fragment reads of
-  // stage kt+1 are spread over the 16 MFMAs of stage kt (one DMA and two
-  // reads after each of the first 12), the fragment masks after the last
-  // four. The MFMAs still queue behind the DMA issues (each holds the
-  // wavefront for tens of cycles), but less than when they come back to back.
+  // One stage: the NL DMA issues for stage kt+3 and the fragment reads of
+  // stage kt+1 are spread over the TM x TN MFMAs of stage kt (with 256 x 256
+  // tiles: one DMA and two reads after each of the first 12 of 16), the
+  // fragment masks after the rest. The MFMAs still queue behind the DMA
+  // issues (each holds the wavefront for tens of cycles), but less than when
+  // they come back to back.
   auto stage = [&](int64_t kt_issue, int64_t kt_read, const Frag& cur, Frag& nxt) {
     __builtin_amdgcn_sched_barrier(0);
     issue(kt_issue);
     read(kt_read, nxt);
     mfmas(cur);
+    constexpr int NM = TM * TN;
+    constexpr int PD = (NL + NM - 1) / NM;                // DMA issues per MFMA
+    constexpr int ND = (NL + PD - 1) / PD;                // MFMAs that carry them
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < NM; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
-      if (m < 12) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                // 1 DMA issue
+      if (m < ND) {
+        __builtin_amdgcn_sched_group_barrier(0x020, PD, 0);               // DMA issues
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                // 2 LDS reads
       } else {
         __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);               // fragment masks
@@ -580,29 +640,33 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* lsm, const Operand& A, con
   for (int64_t kt = 0; kt < nk; kt += 2) {
     // stage kt+1 has landed once only stage kt+2's loads are pending; every
     // wavefront is past its reads of stage kt-1, whose buffer stage kt+3 reuses
-    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    wait_vm_barrier<NL>();
     stage(kt + DS - 1, kt + 1, f0, f1);
-    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    wait_vm_barrier<NL>();
     stage(kt + DS, kt + 2, f1, f0);     // all zero past the end
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");      // ring drained, LDS free
 }
+};
 
 // Epilogue through LDS: acc[i][j][4q+v] = C[row, col] with row = wm*128 + i*32
 // + lane%32 and col = wn*128 + j*32 + 8q + 4*(lane/32) + v. Each wavefront
 // stages 32-row blocks in LDS, then writes 16 bytes per lane along the rows.
-template <typename OutT, typename Store>
-__device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)[4][4],
+// Workgroup tile (64 TM) x (64 TN), read from the accumulator array's shape.
+template <typename OutT, int TM, int TN, typename Store>
+__device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)[TM][TN],
                                                int64_t rows_left, Store store) {
+  constexpr int BM = 64 * TM, BN = 64 * TN;
   constexpr int ES = sizeof(OutT);
-  constexpr int RS = 128 * ES + 16;
+  constexpr int WC = BN / 2;                           // columns of a wavefront
+  constexpr int RS = WC * ES + 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, half = lane >> 5, r32 = lane & 31;
   uint8_t* ep = lsm + wave * (32 * RS);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint8_t* d = ep + r32 * RS + (j * 32 + 8 * q + 4 * half) * ES;
@@ -615,18 +679,18 @@ __device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)
                                                       acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
       }
-    constexpr int PPR = 128 * ES / 16;               // 16-byte pieces per row
+    constexpr int PPR = WC * ES / 16;                // 16-byte pieces per row
 #pragma unroll
     for (int it = 0; it < 32 * PPR / 64; ++it) {
       const int pc = it * 64 + lane, r = pc / PPR, c = pc % PPR;
       const u32x4 val = *reinterpret_cast<const u32x4*>(ep + r * RS + c * 16);
-      const int lr = wm * 128 + i * 32 + r;          // tile row
+      const int lr = wm * (BM / 2) + i * 32 + r;     // tile row
       if (lr < rows_left) store(lr, c * 16 / ES, val);
     }
   }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int BM, int BN>
 __global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict__ dy,
                                                       const uint8_t* __restrict__ dye,
                                                       const uint8_t* __restrict__ w,
@@ -636,12 +700,12 @@ __global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict_
                                                       void* __restrict__ dx) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
   const int64_t N = L, K = ncols;                 // contraction, output columns
-  const int ntn = (int)(K / 256);
+  const int ntn = (int)(K / BN);
   int g, nt;
   int64_t row0, row_end;
   {
     int* pre = reinterpret_cast<int*>(lsm);
-    tile_prefix(G, [&](int e) { return (int)((offsets[e + 1] - offsets[e] + 255) / 256) * ntn; }, pre);
+    tile_prefix(G, [&](int e) { return (int)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * ntn; }, pre);
     const int total = pre[G];
     if ((int)blockIdx.x >= total) return;
     const int t = (int)xcd_tile(blockIdx.x, total);
@@ -649,24 +713,30 @@ __global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict_
     const int loc = t - pre[g];
     const int64_t a = offsets[g];
     row_end = offsets[g + 1];
-    const int mt = (int)((row_end - a + 255) / 256);
+    const int mt = (int)((row_end - a + BM - 1) / BM);
     // Within a group, tiles go in blocks of 4 n-tiles, m-tiles then n-tiles
     // inside a block, so the ~32 consecutive tiles one XCD runs together
     // share 8 A tiles and 4 B tiles in its L2.
     int mi, ni;
     block_order(loc, mt, ntn, mi, ni);
     nt = ni;
-    row0 = a + (int64_t)mi * 256;
+    row0 = a + (int64_t)mi * BM;
     __syncthreads();
   }
-  const int64_t k0 = (int64_t)nt * 256;
+  const int64_t k0 = (int64_t)nt * BN;
   Operand A{dy, dye, N, 0, row0, row_end};
   const int64_t br0 = (int64_t)g * bl.row_step + k0;
-  Operand B{w, we, bl.ld, (int64_t)g * bl.c0_step, br0, br0 + 256};
-  f32x16 acc[4][4];
-  zero<4>(acc);
-  mainloop_dma(lsm, A, B, N, acc);
-  const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * 128;
+  Operand B{w, we, bl.ld, (int64_t)g * bl.c0_step, br0, br0 + BN};
+  constexpr int TM = DmaTile<BM, BN>::TM, TN = DmaTile<BM, BN>::TN;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  DmaLoop<TM, TN>::run(lsm, A, B, N, acc);
+  const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * (BN / 2);
   if constexpr (OUT_BF16)
     store_tile_lds<uint16_t>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dx) + (row0 + lr) * K + col0 + col) = v;
@@ -713,7 +783,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_dma(const uint8_t* __restrict_
   Operand B{xT, xTe, P, c0, k0, k0 + 256};
   f32x16 acc[4][4];
   zero<4>(acc);
-  mainloop_dma(lsm, A, B, L, acc);
+  DmaLoop<4, 4>::run(lsm, A, B, L, acc);
   float* out = dw + (int64_t)g * N * K;
   const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * 128;
   store_tile_lds<float>(lsm, acc, 256, [&](int lr, int col, const u32x4& v) {
@@ -747,6 +817,20 @@ hipError_t dgrad_t(const uint8_t* dy, const uint8_t* dye, const uint8_t* w, cons
   return hipGetLastError();
 }
 
+template <int BM, int BN>
+hipError_t rowxrow_dma(const uint8_t* a, const uint8_t* ae, const uint8_t* b, const uint8_t* be,
+                       const int64_t* offsets, int G, int64_t m_cap, int64_t L, int64_t ncols,
+                       BLayout bl, void* out, bool out_bf16, hipStream_t stream) {
+  static bool done[2] = {false, false};
+  auto k = out_bf16 ? k_dgrad_dma<true, BM, BN> : k_dgrad_dma<false, BM, BN>;
+  const size_t lds = (size_t)DS * DmaTile<BM, BN>::STAGE;
+  hipError_t e = set_lds(k, lds, done[out_bf16]);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((m_cap + BM - 1) / BM + G) * (ncols / BN);   // bound on live tiles
+  k<<<(unsigned)tiles, 256, lds, stream>>>(a, ae, b, be, offsets, G, L, ncols, bl, out);
+  return hipGetLastError();
+}
+
 // Grouped row x row MXFP8 GEMM: out[r, c] = sum_l A[r, l] * B(g)[c, l] for the
 // rows r of group g, out [m_cap, ncols] row-major.
 hipError_t launch_rowxrow(const uint8_t* a, const uint8_t* ae, const uint8_t* b,
@@ -755,14 +839,16 @@ hipError_t launch_rowxrow(const uint8_t* a, const uint8_t* ae, const uint8_t* b,
                           hipStream_t stream) {
   if (m_cap == 0 || G == 0) return hipSuccess;
   if (ncols % 256 == 0 && m_cap >= 256 * (int64_t)G && G <= 8192) {
-    static bool done[2] = {false, false};
-    auto k = out_bf16 ? k_dgrad_dma<true> : k_dgrad_dma<false>;
-    const size_t lds = (size_t)DS * D_STAGE;
-    hipError_t e = set_lds(k, lds, done[out_bf16]);
-    if (e != hipSuccess) return e;
-    const int64_t tiles = ((m_cap + 255) / 256 + G) * (ncols / 256);   // bound on live tiles
-    k<<<(unsigned)tiles, 256, lds, stream>>>(a, ae, b, be, offsets, G, L, ncols, bl, out);
-    return hipGetLastError();
+    // 320 x 128 tiles when about one round of them covers the problem: then
+    // they keep every compute unit busy where 256 x 256 tiles leave many idle
+    // (e.g. 8 groups of ~1024 rows, 1024 columns: ~144 tiles of 256 x 256 on
+    // 256 compute units; 256 tiles of 320 x 128)
+    const int64_t cus = device_cu_count();
+    const int64_t est = (m_cap / 320 + G / 2) * (ncols / 128);
+    if (est <= cus) return rowxrow_dma<320, 128>(a, ae, b, be, offsets, G, m_cap, L, ncols, bl, out,
+                                                 out_bf16, stream);
+    return rowxrow_dma<256, 256>(a, ae, b, be, offsets, G, m_cap, L, ncols, bl, out, out_bf16,
+                                 stream);
   }
   return dgrad_t<128>(a, ae, b, be, offsets, G, m_cap, L, ncols, bl, out, out_bf16, stream);
 }
@@ -804,7 +890,7 @@ hipError_t launch_wgrad(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* 
   if (G == 0) return hipSuccess;
   if (N % 256 == 0 && K % 256 == 0) {
     static bool done = false;
-    const size_t lds = (size_t)DS * D_STAGE;
+    const size_t lds = (size_t)DS * DmaTile<256, 256>::STAGE;
     hipError_t e = set_lds(k_wgrad_dma, lds, done);
     if (e != hipSuccess) return e;
     const int64_t tiles = (int64_t)G * (N / 256) * (K / 256);

@@ -445,10 +445,14 @@ def _mx(x):
 # 128-row tiles (few rows per group); 256 x 128 tiles (256-row tiles that
 # would not fill the chip: ragged groups, an empty one, a 32-row contraction
 # tail); 256 x 256 tiles (a large capacity)
+# Tile paths: 128 x 128 (the first three), 320 x 128 (about one round of
+# them covers the output: the next three), 256 x 256 (the last).
 @pytest.mark.parametrize("counts,N,K,extra", [([100, 0, 37, 250], 256, 384, 33), ([64], 512, 256, 33),
                                               ([129, 3], 128, 128, 33),
                                               ([300, 700, 0, 600], 512, 256, 33),
-                                              ([1000, 24], 256, 512, 8000)])
+                                              ([1000, 24], 256, 512, 8000),
+                                              ([1037, 1018, 992, 1068], 512, 1024, 5),
+                                              ([2000, 1500, 900], 256, 4096, 33)])
 def test_dgrad(nv, counts, N, K, extra):
     import torch
     off, pad = _groups_from_counts(counts)
