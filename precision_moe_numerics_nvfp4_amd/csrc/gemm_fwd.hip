@@ -1087,7 +1087,9 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
   // be all that runs in a second round of 256 x 256 workgroups (nearly as
   // costly as the first, for a few rows each), they go to the streaming
   // kernel right after instead (decided on the device from the offsets)
-  const bool tails = K % SK_K == 0 && N % SK_N == 0 && G <= SK_MAXG &&
+  // (no second launch when even the bound on the tile count fits one round)
+  const bool tails = ((m_cap + LT - 1) / LT + G) * (N / LT) > (int64_t)device_cu_count() &&
+                     K % SK_K == 0 && N % SK_N == 0 && G <= SK_MAXG &&
                      (int64_t)G * (LT / 2 / SK_T) * (N / SK_N) < (int64_t)1 << 31;
   hipError_t e = launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
                                 tails ? (int)device_cu_count() : 0, stream);
