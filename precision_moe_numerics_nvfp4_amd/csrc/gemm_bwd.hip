@@ -19,8 +19,16 @@
 // covers the all-MXFP8 forward GEMM:
 //   fwd:   Y[r, n]     = sum_k X8[r, k] * W8[g*N + n, k]     (weights stored [G, N, K])
 //
-// Structure. A workgroup of 4 wavefronts owns a 256 x 256 output tile; each
-// wavefront owns 128 x 128 (4 x 4 MFMA tiles, 256 accumulator registers).
+// Two kernel families. The main one (further down) streams both operands
+// into an LDS ring by DMA, with 256 x 256 workgroup tiles, or 320 x 128 for
+// the row x row GEMM when about one round of those covers the output (8
+// groups of ~1024 rows x 1024 columns: 256 tiles of 320 x 128 keep every
+// compute unit busy where ~140 tiles of 256 x 256 leave 116 idle). The
+// fallback for shapes it does not take (sizes not multiples of 256, few rows
+// per group) stages through registers:
+//
+// Structure (fallback). A workgroup of 4 wavefronts owns a T x T output tile
+// (T = 128 as launched); each wavefront owns (T/2) x (T/2).
 // The contraction advances 128 bytes (4 MX blocks) per stage, so every
 // operand row contributes one full 128-byte line per stage. Each thread loads
 // its 16-byte chunks of stage kt+1 into registers at the top of iteration kt
@@ -401,12 +409,12 @@ __global__ __launch_bounds__(256, 1) void k_wgrad(const uint8_t* __restrict__ dy
 }
 
 // ---------------------------------------------------------------------------
-// 256 x 256 tiles through an LDS ring filled by DMA.
+// BM x BN tiles (256 x 256 or 320 x 128) through an LDS ring filled by DMA.
 //
 // The operands' bytes go from global memory straight into LDS (buffer loads
 // with the LDS-destination bit), four 64-element stages in flight, so the
-// wavefronts hold no staging registers. A stage is 256 rows x 64 bytes of
-// each operand (16-byte pieces, piece c of row r at position
+// wavefronts hold no staging registers. A stage is BM (A) and BN (B) rows x
+// 64 bytes (16-byte pieces, piece c of row r at position
 // c ^ ((r >> 2) & 3), so the 16 rows of a read phase hit distinct banks) plus
 // the two scale bytes of each row (one byte per 4-byte LDS slot, as the
 // byte-wide DMA writes them). Each stage is one 64-deep MFMA step; the
