@@ -747,11 +747,14 @@ __global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict_
   const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * (BN / 2);
   if constexpr (OUT_BF16)
     store_tile_lds<uint16_t>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dx) + (row0 + lr) * K + col0 + col) = v;
+      // non-temporal: the gradients are read back much later, not from this L2
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dx) + (row0 + lr) * K + col0 + col));
     });
   else
     store_tile_lds<float>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
-      *reinterpret_cast<u32x4*>(static_cast<float*>(dx) + (row0 + lr) * K + col0 + col) = v;
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(static_cast<float*>(dx) + (row0 + lr) * K + col0 + col));
     });
 }
 
@@ -795,7 +798,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_dma(const uint8_t* __restrict_
   float* out = dw + (int64_t)g * N * K;
   const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * 128;
   store_tile_lds<float>(lsm, acc, 256, [&](int lr, int col, const u32x4& v) {
-    *reinterpret_cast<u32x4*>(out + (n0 + lr) * K + col0 + col) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (n0 + lr) * K + col0 + col));
   });
 }
 
