@@ -28,8 +28,11 @@
 // the live tiles are split into 8 contiguous ranges, one per XCD, and the
 // workgroups running together on one XCD share B (weight) tiles in its L2.
 //
-// Small groups (decode: a few rows per expert) use a 32-row variant in which
-// the four wavefronts split N instead of M.
+// Small groups (decode: a few rows per expert) use a weight-streaming kernel
+// (16-row units), or a 32-row variant in which the four wavefronts split N
+// instead of M. With 256 x 256 tiles, the short tails of the groups (at most
+// 128 rows past a multiple of 256) go to the weight-streaming kernel in a
+// second launch when they alone would start a second round of workgroups.
 #include <type_traits>
 
 #include "codecs.hpp"
