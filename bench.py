@@ -556,12 +556,20 @@ def cpu_baseline(inputs, budget_s):
     T_s = 512
     while T_s * 2 <= w["T"] and dt0 * (T_s * 2) / 512 <= budget_s:
         T_s *= 2
+    # the whole workload may take less than the budget: repeat it while the
+    # total stays within three quarters of the budget and report the mean
     dt, M = run(T_s)
+    reps = 1
+    while T_s == w["T"] and dt * (reps + 1) / reps <= 0.75 * budget_s:
+        dt += run(T_s)[0]
+        reps += 1
+    dt /= reps
     flop = 3 * 2.0 * M * N * K
     return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOPS", "cores": int(cores),
             "kind": "oracle",
             "sample": f"first {T_s} of {w['T']} tokens ({M} routed rows) of the same workload, whole "
-                      f"step (weight quantize/requant at full size), {dt:.1f} s",
+                      f"step (weight quantize/requant at full size), {dt:.1f} s per step, "
+                      f"mean of {reps}",
             "seconds": round(dt, 2)}
 
 
