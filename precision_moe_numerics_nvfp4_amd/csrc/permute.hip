@@ -308,14 +308,17 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ ws, int64_t
   const int64_t per = (n_chunks + parts - 1) / parts;
   const int64_t c0 = active ? (int64_t)part * per : 0;
   const int64_t c1 = active ? (c0 + per < n_chunks ? c0 + per : n_chunks) : 0;
-  // the thread's chunks of expert e are contiguous in the table
-  int32_t* col = ws + (active ? (int64_t)e * n_chunks + c0 : 0);
+  // the thread's chunks of expert e are contiguous in the table; an empty
+  // range (c0 >= n_chunks, when parts * per overshoots the chunk count)
+  // points at its expert's first entry
+  const int cnt_c = (int)(c1 > c0 ? c1 - c0 : 0);
+  int32_t* col = ws + (active ? (int64_t)e * n_chunks + (cnt_c > 0 ? c0 : 0) : 0);
   // First kScanRegs entries stay in registers across the block scan (the
   // whole range in the common case: one round of loads); longer ranges
-  // re-read the rest in batches. Loads are unconditional: a range plus
-  // kScanRegs - 1 entries stays inside the workspace (its 256 spare bytes),
-  // and entries past the range are masked to zero.
-  const int cnt_c = (int)(c1 > c0 ? c1 - c0 : 0);
+  // re-read the rest in batches. Loads are unconditional: every range starts
+  // inside the table and ends at most at its end, so a range plus
+  // kScanRegs - 1 entries stays inside the workspace (the table and its 256
+  // spare bytes), and entries past the range are masked to zero.
   int32_t a[kScanRegs];
   int32_t s = 0;
 #pragma unroll

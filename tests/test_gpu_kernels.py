@@ -162,7 +162,8 @@ def test_nvfp4_quantize_tile16(nv, bf16, rows, cols, rpg):
 @pytest.mark.parametrize("case,K", [("uniform", 256), ("zipf", 256), ("one_expert", 256),
                                     ("none_local", 256), ("single", 256), ("empty", 256),
                                     ("many_experts", 256), ("uniform", 160), ("zipf", 96),
-                                    ("zipf_many", 256)])
+                                    ("zipf_many", 256), ("above_small", 256),
+                                    ("one_local_big", 128)])
 def test_moe_permute(nv, case, K):
     import torch
     if case == "uniform":
@@ -179,6 +180,10 @@ def test_moe_permute(nv, case, K):
         topk, e0, nl = gen.route_uniform(205, 900, 1024, 4), 0, 1024
     elif case == "single":
         topk, e0, nl = np.zeros((64, 1), np.int32), 0, 1
+    elif case == "above_small":        # 16640 pairs: three-launch form, 8 local experts
+        topk, e0, nl = gen.route_uniform(207, 8320, 8, 2), 0, 8
+    elif case == "one_local_big":      # 16385 pairs over one local expert
+        topk, e0, nl = gen.route_uniform(208, 16385, 4, 1), 2, 1
     else:
         topk, e0, nl = np.zeros((0, 2), np.int32), 0, 4
     T, k = topk.shape
