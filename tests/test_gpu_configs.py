@@ -1,16 +1,18 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (ExpertLayerStep / the same entry points and shapes).
 
-Where the oracle can run the whole workload in seconds it does (single
-expert; small MoE layer forward and backward; decode); elsewhere it computes
-sampled outputs one by one: sampled token rows of the per-token quantizer,
-sampled experts of the per-expert quantizer, sampled GEMM rows, sampled
-output rows of the streaming re-quantization.
+Every output is compared whole. At the expert-share and streaming sizes the
+oracle runs in independent chunks on a thread pool (tests/oracle_chunks.py):
+row chunks of the per-token quantizer, one expert at a time for the
+per-expert quantizer and the forward GEMMs, output-row chunks of the SR
+re-quantization of a transpose. Oracle inputs are the workload's own arrays
+and the oracle's own results, never the GPU's.
 """
 
 import numpy as np
 import pytest
 
+import oracle_chunks as OC
 from helpers import assert_gemm_close, ensure_built, from_dev, sr_mean_sd, to_dev
 from oracle import formats as F
 from oracle import gemm as GM
@@ -123,113 +125,159 @@ def test_small_moe_forward_and_backward_workload(torch_nv):
     total = 0
     for v, sr, e in ((v_x, sr_x, e_x), (v_w, sr_w, e_w)):
         bias = (sr - v).mean()
-        assert abs(bias) <= 5 * sr_mean_sd(v, e) + 1e-30
+        assert abs(bias) <= 4 * sr_mean_sd(v, e) + 1e-30
         total += v.size
     assert total >= 10_000_000
 
 
-def test_expert_share_workload_sampled(torch_nv):
+def _eq(got, ref, what):
+    """Bytes equal (float32 compared by bit pattern); names the first mismatch."""
+    g = _bits(got) if ref.dtype == np.float32 else np.asarray(got)
+    r = _bits(ref) if ref.dtype == np.float32 else ref
+    assert g.shape == r.shape, f"{what}: shape {g.shape} vs {r.shape}"
+    bad = np.flatnonzero((g != r).reshape(-1))
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at flat index {bad[0]}"
+
+
+@pytest.fixture(scope="module")
+def expert_share(torch_nv):
     """32768 tokens top-8 Zipf(1.1) over 384 experts, experts 144..191 local,
-    d_model 4096, FFN 4096 -> 1536 -> 4096; sampled rows and experts."""
+    d_model 4096, FFN 4096 -> 1536 -> 4096: the GPU's quantizers, permutation
+    and both forward GEMMs (float32 output), and the oracle's whole results."""
     torch, nv = torch_nv
     w = gen.expert_share()
     T, K, F_, E = w["T"], w["K"], w["N"], w["E"]
+    print(f"[expert share] T={T} K={K} F={F_} E={E}", flush=True)
+    d = {}
     x_d = to_dev(w["x"])
-    xq = nv.nvfp4_quantize(x_d)
-    w1q = nv.nvfp4_quantize(to_dev(w["w1"]), rows_per_group=F_)
-    w2q = nv.nvfp4_quantize(to_dev(w["w2"]), rows_per_group=K)
-    perm = nv.moe_permute(to_dev(w["topk"]), w["e0"], E, *xq)
+    d["xq"] = nv.nvfp4_quantize(x_d)
+    d["w1q"] = nv.nvfp4_quantize(to_dev(w["w1"]), rows_per_group=F_)
+    d["w2q"] = nv.nvfp4_quantize(to_dev(w["w2"]), rows_per_group=K)
+    perm = nv.moe_permute(to_dev(w["topk"]), w["e0"], E, *d["xq"])
     torch.cuda.synchronize()
-    r = np.random.default_rng(31)
-    # per-token quantizer on sampled tokens (a row depends on nothing else)
-    rows = np.sort(r.choice(T, 512, replace=False))
-    rc, rs_, ro = Q.quantize(w["x"][rows])
-    assert np.array_equal(from_dev(xq[0])[rows], rc) and np.array_equal(from_dev(xq[1])[rows], rs_)
-    assert np.array_equal(_bits(from_dev(xq[2])[rows]), _bits(ro))
-    # per-expert quantizer on sampled experts (an expert depends on nothing else)
-    for g in (0, 17, 47):
-        for wt, q, n_rows in ((w["w1"], w1q, F_), (w["w2"], w2q, K)):
-            sl = slice(g * n_rows, (g + 1) * n_rows)
-            c, s, o = Q.quantize(wt[sl], rows_per_group=n_rows)
-            assert np.array_equal(from_dev(q[0][sl]), c) and np.array_equal(from_dev(q[1][sl]), s)
-            assert _bits(from_dev(q[2])[g]) == _bits(o)[0]
-    # permutation: full
-    off, pad, rt, rs = PM.permute(w["topk"], w["e0"], E)
-    M = int(off[-1])
-    assert np.array_equal(from_dev(perm["offsets"]), off)
-    assert np.array_equal(from_dev(perm["row_token"])[:M], rt)
-    assert 0.10 * T * 8 < M < 0.14 * T * 8
-    # GEMM1 (4096 -> 1536) and GEMM2 (1536 -> 4096) on sampled rows
-    h = gen.expert_share_hidden(M, F_)
-    hq = nv.nvfp4_quantize(to_dev(h))
-    y1 = nv.moe_fwd_grouped_gemm(perm["codes"], perm["scales"], perm["outer"], *w1q, perm["offsets"],
-                                 out_dtype=torch.bfloat16)
-    y2 = nv.moe_fwd_grouped_gemm(*hq, *w2q, perm["offsets"], out_dtype=torch.bfloat16)
+    M = int(perm["offsets"][-1].item())
+    hid = gen.expert_share_hidden(M, F_)            # stand-in for act(Y1), bf16 [M, F]
+    d["hq"] = nv.nvfp4_quantize(to_dev(hid))
+    y1 = nv.moe_fwd_grouped_gemm(perm["codes"], perm["scales"], perm["outer"], *d["w1q"],
+                                 perm["offsets"], out_dtype=torch.float32)
+    y2 = nv.moe_fwd_grouped_gemm(*d["hq"], *d["w2q"], perm["offsets"], out_dtype=torch.float32)
     torch.cuda.synchronize()
-    pc, ps, po = (from_dev(t)[:M] for t in (perm["codes"], perm["scales"], perm["outer"]))
-    hc, hs, ho = (from_dev(t) for t in hq)
-    y1h, y2h = from_dev(y1[:M]), from_dev(y2)
-    samp = np.sort(np.concatenate([r.choice(M, 192, replace=False), off[1:-1] - 1, off[:-1]]))
-    samp = np.unique(samp[(samp >= 0) & (samp < M)])
-    gidx = np.searchsorted(off, samp, side="right") - 1
-    w1c, w1s, w1o = (from_dev(t) for t in w1q)
-    w2c, w2s, w2o = (from_dev(t) for t in w2q)
-    for rows_, g in ((samp[gidx == gg], gg) for gg in np.unique(gidx)):
-        o1 = np.array([0, rows_.size])
-        ref1 = GM.fwd_grouped(pc[rows_], ps[rows_], po[rows_], w1c[g * F_:(g + 1) * F_],
-                              w1s[g * F_:(g + 1) * F_], w1o[g:g + 1], o1, F_, accum="fp64")
-        ref2 = GM.fwd_grouped(hc[rows_], hs[rows_], ho[rows_], w2c[g * K:(g + 1) * K],
-                              w2s[g * K:(g + 1) * K], w2o[g:g + 1], o1, K, accum="fp64")
-        for got, ref in ((y1h[rows_], ref1), (y2h[rows_], ref2)):
-            gb = F.bf16_bits_to_f32(got).astype(np.float64)
-            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-38))) - 7)
-            assert np.all(np.abs(gb - ref) <= ulp * 1.0000001)
+    h = lambda q: tuple(from_dev(t) for t in q)
+    gpu = {"xq": h(d["xq"]), "w1q": h(d["w1q"]), "w2q": h(d["w2q"]), "hq": h(d["hq"]),
+           "perm": {kk: from_dev(v) for kk, v in perm.items()},
+           "y1": from_dev(y1[:M]), "y2": from_dev(y2)}
+    del d, perm, y1, y2, x_d
+    torch.cuda.empty_cache()
+    ref = {"xq": OC.quantize_rows(w["x"]), "w1q": OC.quantize_groups(w["w1"], F_),
+           "w2q": OC.quantize_groups(w["w2"], K), "hq": OC.quantize_rows(hid)}
+    ref["perm"] = PM.permute(w["topk"], w["e0"], E)
+    ref["gath"] = PM.gather_rows(ref["perm"][2], *ref["xq"])
+    return w, M, gpu, ref
+
+
+def test_expert_share_quantizers_and_permute_whole(expert_share):
+    """Per-token NVFP4 of X [32768, 4096] and of H [M, 1536], per-expert NVFP4
+    of W1 [48 x 1536, 4096] and W2 [48 x 4096, 1536], the permutation and the
+    gathered NVFP4 rows: every byte."""
+    w, M, gpu, ref = expert_share
+    for name in ("xq", "w1q", "w2q", "hq"):
+        for i, part in enumerate(("codes", "scales", "outer")):
+            _eq(gpu[name][i], ref[name][i], f"{name} {part}")
+    off, pad, rt, rs = ref["perm"]
+    p = gpu["perm"]
+    assert M == int(off[-1]) and 0.10 * w["T"] * 8 < M < 0.14 * w["T"] * 8
+    _eq(p["offsets"], off, "offsets")
+    _eq(p["padded_offsets"], pad, "padded offsets")
+    _eq(p["row_token"][:M], rt, "row_token")
+    _eq(p["row_slot"][:M], rs, "row_slot")
+    for i, part in enumerate(("codes", "scales", "outer")):
+        _eq(p[part][:M], ref["gath"][i], f"gathered {part}")
+
+
+def test_expert_share_forward_gemms_whole(expert_share):
+    """Both forward grouped GEMMs (4096 -> 1536 on the gathered X rows,
+    1536 -> 4096 on H) in float32 output on every routed row, against the
+    oracle's float32 GEMM on its own quantized operands: per expert
+    max|y - ref| <= 1e-3 max|ref|, and elementwise 1e-3 where |ref| >= 1e-2
+    of the expert's largest."""
+    w, M, gpu, ref = expert_share
+    K, F_ = w["K"], w["N"]
+    off = ref["perm"][0]
+    groups = [(int(off[g]), int(off[g + 1])) for g in range(w["E"])]
+    y1_ref = OC.fwd_grouped(ref["gath"], ref["w1q"], off, F_)
+    assert_gemm_close(gpu["y1"], y1_ref.astype(np.float64), groups, what="GEMM1 4096->1536")
+    del y1_ref
+    y2_ref = OC.fwd_grouped(tuple(a[:M] for a in ref["hq"]), ref["w2q"], off, K)
+    assert_gemm_close(gpu["y2"], y2_ref.astype(np.float64), groups, what="GEMM2 1536->4096")
 
 
 def test_decode_workload(torch_nv):
     """512 tokens top-8 uniform over 384 experts, 48 local (~10 rows/expert),
-    d_model 4096, FFN 1536, pre-quantized NVFP4 weights: full comparison."""
+    d_model 4096, FFN 1536, pre-quantized NVFP4 weights: both forward GEMMs
+    (4096 -> 1536 and 1536 -> 4096) compared whole in float32 output."""
     torch, nv = torch_nv
     w = gen.decode()
     K, F_, E = w["K"], w["N"], w["E"]
     xq = nv.nvfp4_quantize(to_dev(w["x"]))
     w1q = nv.nvfp4_quantize(to_dev(w["w1"]), rows_per_group=F_)
+    w2q = nv.nvfp4_quantize(to_dev(w["w2"]), rows_per_group=K)
     perm = nv.moe_permute(to_dev(w["topk"]), w["e0"], E, *xq)
-    y = nv.moe_fwd_grouped_gemm(perm["codes"], perm["scales"], perm["outer"], *w1q, perm["offsets"])
+    torch.cuda.synchronize()
+    M = int(perm["offsets"][-1].item())
+    hid = gen.expert_share_hidden(M, F_, cfg=5)
+    hq = nv.nvfp4_quantize(to_dev(hid))
+    y1 = nv.moe_fwd_grouped_gemm(perm["codes"], perm["scales"], perm["outer"], *w1q, perm["offsets"])
+    y2 = nv.moe_fwd_grouped_gemm(*hq, *w2q, perm["offsets"])
     torch.cuda.synchronize()
     off, pad, rt, rs = PM.permute(w["topk"], w["e0"], E)
-    M = int(off[-1])
-    xc, xs, xo = Q.quantize(w["x"])
-    ac, asc, ao = PM.gather_rows(rt, xc, xs, xo)
-    wc, ws, wo = (from_dev(t) for t in w1q)
-    ref = GM.fwd_grouped(ac, asc, ao, wc, ws, wo, off, F_, accum="fp64")
-    assert_gemm_close(from_dev(y)[:M], ref, [(off[g], off[g + 1]) for g in range(E)], what="decode")
+    assert M == int(off[-1])
+    xr = Q.quantize(w["x"])
+    w1r = OC.quantize_groups(w["w1"], F_)
+    w2r = OC.quantize_groups(w["w2"], K)
+    hr = Q.quantize(hid)
+    for name, got, ref in (("w1q", w1q, w1r), ("w2q", w2q, w2r), ("hq", hq, hr)):
+        for i in range(3):
+            _eq(from_dev(got[i]), ref[i], f"decode {name}[{i}]")
+    groups = [(int(off[g]), int(off[g + 1])) for g in range(E)]
+    ref1 = OC.fwd_grouped(PM.gather_rows(rt, *xr), w1r, off, F_, accum="fp64")
+    assert_gemm_close(from_dev(y1)[:M], ref1, groups, what="decode GEMM1 4096->1536")
+    ref2 = OC.fwd_grouped(hr, w2r, off, K, accum="fp64")
+    assert_gemm_close(from_dev(y2)[:M], ref2, groups, what="decode GEMM2 1536->4096")
 
 
-def test_streaming_quantize_and_requant_sampled(torch_nv):
-    """1 GiB bf16 [262144 x 2048]: per-token NVFP4 quantize (sampled rows) and
-    the SR re-quantization of its transpose (sampled output rows)."""
+@pytest.fixture(scope="module")
+def streaming(torch_nv):
+    """1 GiB bf16 [262144 x 2048] ~ N(0, 1): per-token NVFP4 quantize, then
+    the SR re-quantization of its transpose (one segment, P = 262144)."""
     torch, nv = torch_nv
     rows, cols = 262144, 2048
     x = gen.streaming(rows, cols)
+    print(f"[streaming] {rows} x {cols}", flush=True)
     xd = to_dev(x)
     q = nv.nvfp4_quantize(xd)
     off = np.array([0, rows], np.int64)
     seed, tag = gen.philox_seed(5), 2
     o8, e8 = nv.mxfp8_requant_sr(*q, to_dev(off), to_dev(off), rows, seed, tag)
     torch.cuda.synchronize()
-    del xd
-    r = np.random.default_rng(55)
-    samp = np.sort(r.choice(rows, 1024, replace=False))
-    rc, rs_, ro = Q.quantize(x[samp])
-    qc, qs, qo = (from_dev(t) for t in q)
-    assert np.array_equal(qc[samp], rc) and np.array_equal(qs[samp], rs_)
-    assert np.array_equal(_bits(qo[samp]), _bits(ro))
-    got8 = from_dev(o8)
-    gote = from_dev(e8)
-    for k in (0, 1, 777, 2047):
-        kb = k // 16
-        v = Q.dequantize(np.ascontiguousarray(qc[:, kb * 8:(kb + 1) * 8]),
-                         np.ascontiguousarray(qs[:, kb:kb + 1]), qo)[:, k % 16]
-        c, e = MX.quantize_sr(v[None, :], seed, tag, idx_base=k * rows)
-        assert np.array_equal(got8[k], c[0]) and np.array_equal(gote[k], e[0])
+    gq = tuple(from_dev(t) for t in q)
+    g8 = (from_dev(o8), from_dev(e8))
+    del xd, q, o8, e8
+    torch.cuda.empty_cache()
+    return x, off, seed, tag, gq, g8, OC.quantize_rows(x)
+
+
+def test_streaming_quantize_whole(streaming):
+    """Every code, block scale and outer scale of the 1 GiB per-token quantize."""
+    x, off, seed, tag, gq, g8, ref = streaming
+    for i, part in enumerate(("codes", "scales", "outer")):
+        _eq(gq[i], ref[i], f"streaming {part}")
+
+
+def test_streaming_requant_whole(streaming):
+    """Every E4M3 byte and E8M0 exponent of the SR re-quantization of the
+    transpose [2048, 262144], from the oracle's own quantization of X."""
+    x, off, seed, tag, gq, g8, q = streaming
+    rows = x.shape[0]
+    r8, re = OC.requant_cols(q, off, off, rows, seed, tag)
+    _eq(g8[0], r8, "streaming requant E4M3")
+    _eq(g8[1], re, "streaming requant E8M0")

@@ -25,7 +25,9 @@ from oracle import nvfp4_bwd as NB
 from oracle import permute as PM
 from workloads import gen
 
-pytestmark = pytest.mark.gpu
+# an overflow inside the oracle means it was fed something other than the
+# path's outputs (e.g. unwritten capacity rows): fail instead of warning
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("error::RuntimeWarning")]
 
 
 @pytest.fixture(scope="module")
@@ -132,7 +134,8 @@ def test_expert_ffn_full_size_sampled(nv, shape):
     grp = np.searchsorted(off, samp, side="right") - 1
     w1q = tuple(h(a) for a in L.w1q)
     w2q = tuple(h(a) for a in L.w2q)
-    H, HQ = h(L.h), tuple(h(a) for a in L.hq)
+    # only the first M rows of the capacity-sized buffers are written
+    H, HQ = h(L.h)[:M], tuple(h(a)[:M] for a in L.hq)
     Y2 = h(L.y2)
     # forward GEMMs and the intermediate's quantizer on sampled rows
     for g in np.unique(grp):
