@@ -155,6 +155,29 @@ NVFP4MOE_API int moe_permute(const int32_t* topk_ids, int64_t T, int k, int e0, 
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, results and kernels without the workspace, whose table
+ * lives instead in a 4 MiB array the library holds on each GPU it runs on
+ * until the process ends. Makes no allocating call.
+ *
+ * Returns NVFP4MOE_EWORKSPACE, before any HIP call, when the call would need
+ * more than 4 MiB of table: nvfp4moe_permute_workspace_size(T, k, n_local) >
+ * 4 MiB, i.e. ceil(T*k / 256) * n_local > 1048512 (T*k up to about 5.59 M
+ * pairs with 48 local experts, 261,888 with 1024). The other argument rules
+ * are moe_permute's. Calls issued on one GPU share its array: calls that
+ * overlap in time on one GPU (on different streams, or from different host
+ * threads without ordering) race and must not be made. Nothing needs
+ * clearing between calls: each call writes every table entry it reads.
+ */
+NVFP4MOE_API int moe_permute_noalloc(const int32_t* topk_ids, int64_t T, int k, int e0,
+                int n_local, const uint8_t* xq_codes, const uint8_t* xq_scales,
+                const float* xq_outer, int64_t K,
+                int64_t* offsets, int64_t* padded_offsets,
+                int32_t* row_token, int32_t* row_slot, int32_t* pair_row,
+                uint8_t* xperm_codes, uint8_t* xperm_scales, float* xperm_outer, void* stream);
+
+/*
  * NVFP4 forward grouped GEMM.
  * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), section
  * "NVFP4 forward, MXFP8 backward" (expert-layer matmuls in NVFP4).

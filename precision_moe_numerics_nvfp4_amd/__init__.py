@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     moe_fwd_grouped_gemm_mxfp8,
     moe_padded_offsets,
     moe_permute,
+    moe_permute_noalloc,
     mxfp8_gather_rows,
     mxfp8_quantize,
     mxfp8_quantize_dual,

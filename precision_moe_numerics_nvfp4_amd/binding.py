@@ -30,6 +30,8 @@ SIGNATURES = {
     "nvfp4moe_permute_workspace_size": ([_c_i64, _c_int, _c_int], _c_size),
     "moe_permute": ([_p, _c_i64, _c_int, _c_int, _c_int, _p, _p, _p, _c_i64, _p, _p, _p, _p,
                      _p, _p, _p, _p, _p, _c_size, _p], _c_int),
+    "moe_permute_noalloc": ([_p, _c_i64, _c_int, _c_int, _c_int, _p, _p, _p, _c_i64, _p, _p, _p,
+                             _p, _p, _p, _p, _p, _p], _c_int),
     "moe_fwd_grouped_gemm": ([_p, _p, _p, _p, _p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p,
                               _c_int, _p], _c_int),
     "mxfp8_requant_sr": ([_p, _p, _p, _c_int, _c_i64, _c_i64, _c_i64, _p, _p, _c_int, _c_i64,
@@ -208,6 +210,31 @@ def moe_permute(topk_ids, e0, n_local, xq_codes, xq_scales, xq_outer, workspace=
                            _ptr(workspace), workspace.numel(), _stream(topk_ids))
     _check("moe_permute", st)
     return o
+
+
+def moe_permute_noalloc(topk_ids, e0, n_local, xq_codes, xq_scales, xq_outer, out):
+    """moe_permute through the entry point that allocates nothing: the
+    library keeps the count table in its own per-GPU array (at most 4 MiB,
+    see the header), and every output buffer comes from the caller in `out`
+    (the dict moe_permute returns or takes; "pair_row" optional)."""
+    torch = _torch()
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    T, k = topk_ids.shape
+    _dev(xq_codes, "xq_codes", torch.uint8, 2)
+    _dev(xq_scales, "xq_scales", torch.uint8, 2)
+    _dev(xq_outer, "xq_outer", torch.float32, 1)
+    K = xq_codes.shape[1] * 2
+    for name in ("offsets", "padded_offsets", "row_token", "row_slot", "codes", "scales", "outer"):
+        if name not in out:
+            raise ValueError(f"moe_permute_noalloc: out lacks {name}")
+    st = lib().moe_permute_noalloc(_ptr(topk_ids), T, k, int(e0), int(n_local), _ptr(xq_codes),
+                                   _ptr(xq_scales), _ptr(xq_outer), K, _ptr(out["offsets"]),
+                                   _ptr(out["padded_offsets"]), _ptr(out["row_token"]),
+                                   _ptr(out["row_slot"]), _ptr(out.get("pair_row")),
+                                   _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["outer"]),
+                                   _stream(topk_ids))
+    _check("moe_permute_noalloc", st)
+    return out
 
 
 def moe_fwd_grouped_gemm(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer, offsets,

@@ -89,6 +89,29 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int k, int e0, int n_local,
                                    xperm_scales, xperm_outer, workspace, as_stream(stream)));
 }
 
+int moe_permute_noalloc(const int32_t* topk_ids, int64_t T, int k, int e0, int n_local,
+                        const uint8_t* xq_codes, const uint8_t* xq_scales, const float* xq_outer,
+                        int64_t K, int64_t* offsets, int64_t* padded_offsets, int32_t* row_token,
+                        int32_t* row_slot, int32_t* pair_row, uint8_t* xperm_codes,
+                        uint8_t* xperm_scales, float* xperm_outer, void* stream) {
+  REQUIRE(T >= 0 && K >= 0 && k > 0 && n_local > 0, NVFP4MOE_EINVAL);
+  REQUIRE(offsets && padded_offsets, NVFP4MOE_EINVAL);
+  if (T > 0)
+    REQUIRE(topk_ids && xq_codes && xq_scales && xq_outer && row_token && row_slot &&
+                xperm_codes && xperm_scales && xperm_outer,
+            NVFP4MOE_EINVAL);
+  REQUIRE(n_local <= 1024 && k <= 64, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(K % 32 == 0 && K > 0, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(T * (int64_t)k < (int64_t)1 << 31, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(permute_workspace_bytes(T, k, n_local) <= permute_scratch_bytes(), NVFP4MOE_EWORKSPACE);
+  REQUIRE(aligned16(xq_codes) && aligned16(xperm_codes), NVFP4MOE_EUNSUPPORTED);
+  void* ws = nullptr;
+  if (permute_scratch_address(&ws) != hipSuccess) return NVFP4MOE_EHIP;
+  return hip_status(launch_permute(topk_ids, T, k, e0, n_local, xq_codes, xq_scales, xq_outer,
+                                   K, offsets, padded_offsets, row_token, row_slot, pair_row,
+                                   xperm_codes, xperm_scales, xperm_outer, ws, as_stream(stream)));
+}
+
 int moe_fwd_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
                          const uint8_t* b_codes, const uint8_t* b_scales, const float* b_outer,
                          const int64_t* offsets, int G, int64_t m_cap, int64_t N, int64_t K,

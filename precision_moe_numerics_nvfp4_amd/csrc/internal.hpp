@@ -36,6 +36,8 @@ hipError_t launch_combine_bwd(const void* dout, bool dout_bf16, int64_t N, int k
 
 // permute.hip
 size_t permute_workspace_bytes(int64_t T, int k, int n_local);
+size_t permute_scratch_bytes();
+hipError_t permute_scratch_address(void** out);
 hipError_t launch_permute(const int32_t* topk_ids, int64_t T, int k, int e0, int n_local,
                           const uint8_t* xq_codes, const uint8_t* xq_scales,
                           const float* xq_outer, int64_t K, int64_t* offsets,

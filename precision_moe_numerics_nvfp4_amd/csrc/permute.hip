@@ -32,6 +32,8 @@
 // In both forms the workgroup then copies the NVFP4 rows (codes, scales, outer
 // scale) of its routed pairs to their output rows: all 256 threads walk the
 // (row, 16-byte piece) pairs with eight loads in flight before the stores.
+#include <mutex>
+
 #include "codecs.hpp"
 #include "internal.hpp"
 
@@ -535,6 +537,39 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int k, int e0, int n_lo
           pair_row, pc, ps, po);
   }
   return hipGetLastError();
+}
+
+// Library-owned scratch for moe_permute_noalloc: the three-launch form's
+// per-(expert, chunk) count table lives here instead of in a caller's
+// workspace. Every GPU the library runs on holds its own copy for the life of
+// the process. The histogram pass writes every table entry a call reads, so
+// nothing needs clearing between calls; calls that overlap on one GPU share
+// the table and race.
+constexpr size_t kPermuteScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kPermuteScratchBytes];
+
+size_t permute_scratch_bytes() { return kPermuteScratchBytes; }
+
+// Device address of `scratch` on the current device. In host code the
+// array's name is only a host-side stand-in, so the address is looked up once
+// per device (with that device current) and cached.
+hipError_t permute_scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace nvfp4moe
