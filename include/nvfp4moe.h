@@ -26,7 +26,23 @@
  *     produced by moe_permute and never copied to the host, so grids are sized
  *     for the capacity (`m_cap`, `P`) and kernels read the real extents.
  *   - Calls are stateless apart from a per-process device-property cache, and
- *     may be issued concurrently on different streams with disjoint outputs.
+ *     may be issued concurrently on different streams with disjoint outputs
+ *     (moe_permute_noalloc excepted: see there).
+ *
+ * Where this interface departs from the one first planned for the path:
+ *   - `stream` is a `void*` holding a hipStream_t, so the header needs no HIP
+ *     include and binds from any language with a C FFI;
+ *   - moe_permute takes one more output, `pair_row` (the inverse map, NULL
+ *     allowed), which the combine and its backward read;
+ *   - sizes are narrower than "multiple of 16": the quantizer takes
+ *     cols % 32 == 0 and cols <= 8192 (one wavefront per row), the forward
+ *     GEMM N % 128 == 0 and K % 128 == 0, the re-quantization cols % 128 == 0
+ *     and P % 32 == 0, the MXFP8 GEMMs N and K multiples of 128 (each returns
+ *     NVFP4MOE_EUNSUPPORTED otherwise);
+ *   - entry points beyond the seven of the path: the all-MXFP8 forward, the
+ *     routed FFN's combine and intermediate quantizer, the 16x16-tile and
+ *     NVFP4-backward variants, the one-pass dual dY quantizer and
+ *     moe_permute_noalloc.
  *
  * Formats (NVFP4 and MXFP8 as named on "Inkling 2 Small uses four-bit
  * training ..." (ai-primer), section "Block scales and per-token activations"):

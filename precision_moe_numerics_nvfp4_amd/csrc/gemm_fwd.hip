@@ -12,27 +12,32 @@
 // exact products, float32 accumulation. The per-row and per-expert outer
 // scales are applied in the epilogue: y = (acc * s_x[row]) * s_w[g].
 //
-// Structure (large tiles). A workgroup of 4 wavefronts owns a 256 x 256 tile
-// (tokens x outputs) of one expert; each wavefront owns 128 x 128 (4 x 4 MFMA
-// tiles, 256 accumulator registers). The K loop moves 64 elements per stage:
-// every thread loads its share of the stage's NVFP4 bytes from HBM one stage
-// ahead, dequantizes them once per workgroup (v_cvt_scalef32_pk_f16_fp4 with
-// a unit scale, then an exact v_pk_mul_f16 by the block's E4M3 scale) and
-// stores f16 into a double-buffered LDS tile whose 16-byte chunks are
-// XOR-swizzled by row, so the fragment reads (ds_read_b128, 32 rows at one
-// k offset) spread over the banks. HBM traffic stays at 4.5 bits per element.
+// Structure (large tiles, k_fwd_lds4). A workgroup of 4 wavefronts owns a
+// 256 x 256 tile (tokens x outputs) of one expert; each wavefront owns
+// 128 x 128 (4 x 4 MFMA tiles, 256 accumulator registers, one wavefront per
+// SIMD), its 32-row blocks alternating with the other wavefront row's (block
+// 2i + wm), so a partial tile's rows are spread over all four wavefronts.
+// The K loop moves 128 elements per stage: the stage's raw NVFP4 bytes (64
+// code bytes and 8 scale bytes per row of A and of B) go from global memory
+// straight into LDS by buffer loads with the LDS-destination bit, three
+// stages in flight, so LDS carries 4.5 bits per element and no registers
+// stage the loads. Each wavefront reads the raw codes of its own fragment
+// rows and converts them to f16 right before the MFMAs that use them
+// (v_cvt_scalef32_pk_f16_fp4 at unit scale, then an exact v_pk_mul_f16 by the
+// block's E4M3 scale), interleaved with the previous step's MFMAs so the
+// conversions co-execute with the matrix pipe. One barrier per stage.
 //
-// Tile order. Tiles are enumerated expert by expert, n-tile by n-tile, m-tile
-// fastest, and only the live ones (sum over g of ceil(M_g/BM) * N/BN, read
-// from the device offsets) are handed out; workgroup w goes to XCD w % 8, so
-// the live tiles are split into 8 contiguous ranges, one per XCD, and the
-// workgroups running together on one XCD share B (weight) tiles in its L2.
+// Tile order. Every group's full 256-row tiles first, then the partial last
+// tiles of more than 128 rows, then those of at most 128; each part is split
+// into 8 contiguous ranges, one per XCD (workgroup w runs on XCD w % 8), and
+// within a group the tiles go in blocks of 4 n-tiles, m-tile fastest, so the
+// workgroups an XCD runs together share weight and activation tiles in its L2.
 //
-// Small groups (decode: a few rows per expert) use a weight-streaming kernel
-// (16-row units), or a 32-row variant in which the four wavefronts split N
-// instead of M. With 256 x 256 tiles, the short tails of the groups (at most
-// 128 rows past a multiple of 256) go to the weight-streaming kernel in a
-// second launch when they alone would start a second round of workgroups.
+// Other kernels. k_fwd_stream streams the weights for groups of a few rows
+// (decode: 16-row units), and takes the short tails of the 256-row tiles in a
+// second launch when they alone would start a second round of workgroups;
+// k_fwd (32 x 128 tiles, f16 dequantized into LDS) covers the shapes the
+// other two do not.
 #include <type_traits>
 
 #include "codecs.hpp"
@@ -511,11 +516,14 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
 
   const int64_t nk = WG ? (offsets[g + 1] - offsets[g]) / LBK : K / LBK;
 
-  // per-lane LDS byte offsets of the fragment reads (stage-relative)
+  // per-lane LDS byte offsets of the fragment reads (stage-relative). The
+  // tile's 32-row blocks alternate between the two rows of wavefronts (block
+  // 2i + wm is the wavefront's i-th), so a partial tile's valid blocks are
+  // shared by all four wavefronts instead of leaving two without rows.
   int fa[TM][2], fb[TN][2], sa_off[TM], sb_off[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int r = wm * 128 + i * 32 + r32;
+    const int r = (2 * i + wm) * 32 + r32;
 #pragma unroll
     for (int c = 0; c < 2; ++c) fa[i][c] = r * LCB + (((2 * half + c) ^ ((r >> 2) & 3)) << 4);
     sa_off[i] = 2 * LT * LCB + r * LSB + half * 4;
@@ -663,7 +671,9 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   if constexpr (WG) {
     mainloop(std::integral_constant<int, 4>{});        // weight-gradient tiles are full
   } else {
-    const int act = (arows - wm * 128 + 31) >> 5;      // valid 32-row blocks of this wavefront
+    // valid 32-row blocks of this wavefront: blocks wm, wm + 2, ... below nblk
+    const int nblk = (arows + 31) >> 5;
+    const int act = nblk > wm ? (nblk - wm + 1) >> 1 : 0;
     if (act >= 4) mainloop(std::integral_constant<int, 4>{});
     else if (act == 3) mainloop(std::integral_constant<int, 3>{});
     else if (act == 2) mainloop(std::integral_constant<int, 2>{});
@@ -671,7 +681,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     else mainloop(std::integral_constant<int, 0>{});
   }
 
-  // Epilogue. acc[i][j][4q+v] = Y[row, col] with row = wm*128 + i*32 + lane%32
+  // Epilogue. acc[i][j][4q+v] = Y[row, col] with row = (2i + wm)*32 + lane%32
   // and col = wn*128 + j*32 + 8q + 4*half + v (the MFMAs took W first). Each
   // wavefront stages one 32-row block at a time in LDS (row-major, scaled and
   // converted), then writes it out 16 bytes per lane along the rows, so the
@@ -686,8 +696,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   const int64_t obase = WG ? (int64_t)g * N * K : 0;    // WG: expert g's dW
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int rl = i * 32 + r32;                         // row within the wavefront's block
-    const int64_t row = row0 + wm * 128 + rl;
+    const int64_t row = row0 + (2 * i + wm) * 32 + r32;
     const float sx = WG ? ao[g] : (row < row_end ? ao[row] : 0.0f);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -711,7 +720,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     for (int it = 0; it < 32 * PPR / 64; ++it) {
       const int pc = it * 64 + lane, r = pc / PPR, c = pc % PPR;
       const u32x4 val = *reinterpret_cast<const u32x4*>(ep + r * RS + c * 16);
-      const int64_t orow = row0 + wm * 128 + i * 32 + r;
+      const int64_t orow = row0 + (2 * i + wm) * 32 + r;
       // non-temporal: every workgroup writes its tile at about the same time,
       // 32 MB on the small MoE layer, past what the L2s hold (2 us faster)
       if (orow < row_end)
