@@ -417,50 +417,66 @@ __global__ __launch_bounds__(256, 1) void k_wgrad(const uint8_t* __restrict__ dy
 // ---------------------------------------------------------------------------
 // BM x BN tiles (256 x 256 or 320 x 128) through an LDS ring filled by DMA.
 //
-// The operands' bytes go from global memory straight into LDS (buffer loads
-// with the LDS-destination bit), four 64-element stages in flight, so the
-// wavefronts hold no staging registers. A stage is BM (A) and BN (B) rows x
-// 64 bytes (16-byte pieces, piece c of row r at position
-// c ^ ((r >> 2) & 3), so the 16 rows of a read phase hit distinct banks) plus
-// the two scale bytes of each row (one byte per 4-byte LDS slot, as the
-// byte-wide DMA writes them). Each stage is one 64-deep MFMA step; the
-// fragments of stage kt+1 are read from LDS while the MFMAs of stage kt run.
+// The operands' code bytes go from global memory straight into LDS (buffer
+// loads with the LDS-destination bit), four 64-element stages in flight, so
+// the wavefronts hold no staging registers for them. A stage is BM (A) and
+// BN (B) rows x 64 bytes (16-byte pieces, piece c of row r at position
+// c ^ ((r >> 2) & 3), so the 16 rows of a read phase hit distinct banks).
+// Each stage is one 64-deep MFMA step; the fragments of stage kt+1 are read
+// from LDS while the MFMAs of stage kt run.
+//
+// The E8M0 scales (two bytes per row and stage) come in blocks of SB = 4
+// stages: each thread loads the 12 bytes from the dword below a row's 8
+// bytes (the row's scales for 4 stages start at whatever byte alignment the
+// group's contraction offset and the row pitch give; buffer loads address
+// whole dwords), shifts the 8 out with v_alignbyte and writes them to a
+// two-block LDS ring, [block % 2][row][8].
+// Loaded per stage, one byte per lane, they cost one cache line per lane and
+// byte: twice the line traffic of the codes themselves.
+//
 // A ragged contraction end (wgrad) is a multiple of 32: when the last stage
 // holds only its first MX block, the second block's bytes are zeroed in the
 // fragments and its scale set to 1.
 constexpr int DK = 64;                                // contraction elements per stage
 constexpr int DS = 4;                                 // stages in the ring
+constexpr int SB = 4;                                 // stages per scale block (8 bytes a row)
 
 // Workgroup tile BM x BN (rows of A x rows of B), 2 x 2 wavefronts of
 // (BM/2) x (BN/2), that is TM x TN MFMA tiles of 32 x 32 each. A code DMA
-// instruction fills 16 rows, a scale DMA instruction one scale byte of 64
-// rows; the scale instructions are dealt to the wavefronts round-robin, the
-// count padded to a multiple of 4 by repeating the last ones (same bytes to
-// the same place), so every wavefront issues NL loads per stage.
+// instruction fills 16 rows, so every wavefront issues NL = (BM + BN) / 64
+// loads per stage; a scale block is NSL loads per thread (row t, t + 256, ...
+// of the BM + BN rows; threads past the last row load row 0 into a spare
+// slot, so every wavefront issues the same count).
 template <int BM, int BN>
 struct DmaTile {
   static constexpr int TM = BM / 64, TN = BN / 64;
   static constexpr int CA = BM / 64, CB = BN / 64;    // code loads per stage and wavefront
-  static constexpr int NA = BM / 64, NB = BN / 64;    // 64-row blocks
-  static constexpr int SI = 2 * (NA + NB);            // scale loads per stage (workgroup)
-  static constexpr int SW = (SI + 3) / 4;             // ... per wavefront
-  static constexpr int NL = CA + CB + SW;
+  static constexpr int NL = CA + CB;
+  static constexpr int R = BM + BN;                   // scale rows
+  static constexpr int NSL = (R + 255) / 256;         // scale loads per thread and block
   static constexpr int A0 = 0, B0 = BM * DK;          // code planes [rows][64]
-  static constexpr int SC = (BM + BN) * DK;           // scale planes [op][byte][rows][4]
-  static constexpr int STAGE = SC + 2 * (BM + BN) * 4;
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && SI >= 4, "tile shape");
+  static constexpr int STAGE = (BM + BN) * DK;
+  static constexpr int SBLK = (NSL * 256) * 8;        // one scale block, spare rows included
+  static constexpr int SC = DS * STAGE;               // scale ring after the code stages
+  static constexpr int LDS = SC + 2 * SBLK;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile shape");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// s_waitcnt vmcnt(N) then s_barrier (N an immediate: the tile shapes' load counts)
-template <int N>
+// s_waitcnt vmcnt(N) [lgkmcnt(0)] then s_barrier (N an immediate: the tile
+// shapes' load counts)
+template <int N, bool LGKM = false>
 __device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N == 11 || N == 12 || N == 22 || N == 24, "add the count");
-  if constexpr (N == 11) asm volatile("s_waitcnt vmcnt(11)\n\ts_barrier" ::: "memory");
-  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-  if constexpr (N == 22) asm volatile("s_waitcnt vmcnt(22)\n\ts_barrier" ::: "memory");
-  if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+  static_assert(N == 7 || N == 8 || N == 9 || N == 10 || N == 14 || N == 16, "add the count");
+#define NVFP4MOE_WAIT(n)                                                              \
+  if constexpr (N == n) {                                                             \
+    if constexpr (LGKM) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+    else asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory");           \
+  }
+  NVFP4MOE_WAIT(7) NVFP4MOE_WAIT(8) NVFP4MOE_WAIT(9) NVFP4MOE_WAIT(10) NVFP4MOE_WAIT(14)
+  NVFP4MOE_WAIT(16)
+#undef NVFP4MOE_WAIT
 }
 
 // Workgroup tile (64 TM_) x (64 TN_). (A class template's member rather than
@@ -472,7 +488,7 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
                                            int64_t L, f32x16 (&acc)[TM_][TN_]) {
   constexpr int BM = 64 * TM_, BN = 64 * TN_;
   using C = DmaTile<BM, BN>;
-  constexpr int TM = C::TM, TN = C::TN, NL = C::NL;
+  constexpr int TM = C::TM, TN = C::TN, NL = C::NL, NSL = C::NSL;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -497,12 +513,9 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
                                               uniform_u32(n * (X.ld / 32)), kBufferWord3);
   }
   // lane offsets: code instruction i of this wavefront fills rows 16m .. 16m+15
-  // (m = 4i + wave; lane: row 16m + lane/4, position lane%4). Scale item q
-  // (q = 4j + wave; past the last item, q - 4) is byte `sbyte` of rows
-  // 64 blk + lane of operand `sop`: items A byte 0, A byte 1, B byte 0, B byte 1.
+  // (m = 4i + wave; lane: row 16m + lane/4, position lane%4)
   constexpr int CM = C::CA > C::CB ? C::CA : C::CB;
-  uint32_t oq[2][CM], oe[C::SW];
-  int sop[C::SW], sdst[C::SW];
+  uint32_t oq[2][CM];
 #pragma unroll
   for (int o = 0; o < 2; ++o)
 #pragma unroll
@@ -512,27 +525,13 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
       const int rr = row < nrow[o] ? row : 0;
       oq[o][i] = (uint32_t)(rr * ld[o] + c0[o] + piece * 16);
     }
-#pragma unroll
-  for (int j = 0; j < C::SW; ++j) {
-    int q = 4 * j + wave;
-    if (q >= C::SI) q -= 4;
-    const int o = q < 2 * C::NA ? 0 : 1;
-    const int qq = o ? q - 2 * C::NA : q, nb = o ? C::NB : C::NA;
-    const int byte = qq / nb, blk = qq - byte * nb;
-    const int row = 64 * blk + lane;
-    const int rr = row < nrow[o] ? row : 0;
-    sop[j] = __builtin_amdgcn_readfirstlane(o);
-    oe[j] = (uint32_t)(rr * (ld[o] / 32) + c0[o] / 32 + byte);
-    sdst[j] = __builtin_amdgcn_readfirstlane(
-        C::SC + ((o ? 2 * BM : 0) + byte * (o ? BN : BM) + 64 * blk) * 4);
-  }
   // stage kt -> buffer kt % DS; past the end: offsets outside the ranges
   // (zeros, no memory traffic) so every stage has the same load count
   auto issue = [&](int64_t kt) {
     uint8_t* st = lsm + (kt % DS) * C::STAGE;
     const bool real = kt < nk;
     const uint32_t away = real ? 0u : 0x40000000u;
-    const uint32_t kq = real ? (uint32_t)(kt * DK) : 0u, ke = real ? (uint32_t)(kt * 2) : 0u;
+    const uint32_t kq = real ? (uint32_t)(kt * DK) : 0u;
 #pragma unroll
     for (int o = 0; o < 2; ++o)
 #pragma unroll
@@ -540,27 +539,61 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rq[o], (lds_void*)(st + (o ? C::B0 : C::A0) + (4 * i + wave) * 1024), 16,
             oq[o][i] + kq + away, 0, 0, 0);
+  };
+  // scale rows of this thread: row q = tid + 256 u of the BM + BN (A first);
+  // rows past the tile's valid rows read the tile's first row; q >= BM + BN
+  // (spare slots) read row 0 of A
+  uint32_t eo[NSL], esh[NSL];          // dword-aligned offset, byte shift
+  bool eb_[NSL];
 #pragma unroll
-    for (int j = 0; j < C::SW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          sop[j] ? re[1] : re[0], (lds_void*)(st + sdst[j]), 1, oe[j] + ke + away, 0, 0, 0);
+  for (int u = 0; u < NSL; ++u) {
+    const int q = tid + 256 * u;
+    const int o = q < BM ? 0 : (q < C::R ? 1 : 0);
+    const int rr0 = q < BM ? q : (q < C::R ? q - BM : 0);
+    const int rr = rr0 < nrow[o] ? rr0 : 0;
+    eb_[u] = o == 1;
+    const uint32_t byte_off = (uint32_t)(rr * (ld[o] / 32) + c0[o] / 32);
+    eo[u] = byte_off & ~3u;
+    esh[u] = byte_off & 3u;
+  }
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
+  u32x3v sreg[NSL];
+  // block blk's 8 bytes of each of this thread's rows into registers (past
+  // the operand's end the loads return zeros; bytes past the contraction's
+  // end belong to stages that are masked below)
+  auto load_scales = [&](int64_t blk) {
+    const uint32_t off = (uint32_t)(blk * 2 * SB);
+#pragma unroll
+    for (int u = 0; u < NSL; ++u)
+      sreg[u] = __builtin_bit_cast(
+          u32x3v, __builtin_amdgcn_raw_buffer_load_b96(eb_[u] ? re[1] : re[0], eo[u] + off, 0, 0));
+  };
+  auto store_scales = [&](int64_t blk) {
+    uint8_t* d = lsm + C::SC + (blk & 1) * C::SBLK;
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      const u32x2v w = {__builtin_amdgcn_alignbyte(sreg[u][1], sreg[u][0], esh[u]),
+                        __builtin_amdgcn_alignbyte(sreg[u][2], sreg[u][1], esh[u])};
+      *reinterpret_cast<u32x2v*>(d + (tid + 256 * u) * 8) = w;
+    }
   };
 
-  // fragment addresses (stage-relative)
+  // fragment addresses (stage-relative) and scale rows (block-relative)
   int fa[TM][2], fb[TN][2], sa[TM], sbo[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int ra = wm * (BM / 2) + i * 32 + r32;
 #pragma unroll
     for (int c = 0; c < 2; ++c) fa[i][c] = C::A0 + ra * DK + (((2 * c + half) ^ ((ra >> 2) & 3)) << 4);
-    sa[i] = C::SC + (half * BM + ra) * 4;
+    sa[i] = C::SC + ra * 8 + half;
   }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int rb = wn * (BN / 2) + j * 32 + r32;
 #pragma unroll
     for (int c = 0; c < 2; ++c) fb[j][c] = C::B0 + rb * DK + (((2 * c + half) ^ ((rb >> 2) & 3)) << 4);
-    sbo[j] = C::SC + (2 * BM + half * BN + rb) * 4;
+    sbo[j] = C::SC + (BM + rb) * 8 + half;
   }
   struct Frag {
     i32x8 a[TM], b[TN];
@@ -568,13 +601,15 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
   };
   auto read = [&](int64_t kt, Frag& f) {
     const uint8_t* st = lsm + (kt % DS) * C::STAGE;
+    // stage kt's scale bytes: block kt / SB in the ring, bytes 2 (kt % SB) + half
+    const int so = (int)(((kt / SB) & 1) * C::SBLK + 2 * (kt % SB));
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + fa[i][0]);
       const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + fa[i][1]);
       f.a[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                      (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      f.as[i] = *reinterpret_cast<const uint8_t*>(st + sa[i]);
+      f.as[i] = *reinterpret_cast<const uint8_t*>(lsm + sa[i] + so);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -582,7 +617,7 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
       const u32x4 y1 = *reinterpret_cast<const u32x4*>(st + fb[j][1]);
       f.b[j] = i32x8{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3],
                      (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
-      f.bs[j] = *reinterpret_cast<const uint8_t*>(st + sbo[j]);
+      f.bs[j] = *reinterpret_cast<const uint8_t*>(lsm + sbo[j] + so);
     }
     // Contraction elements past L are zero: MX block 1 of a last stage that
     // holds 32 elements, and whole stages past the end (the loop runs an even
@@ -620,14 +655,19 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
   };
 
   static_assert(DS == 4 && 2 * NL < 64, "the wait counts assume 4 stages, NL loads per stage");
+  static_assert(SB == 4, "a loop iteration is half a scale block");
+  // prologue: scale block 0 to LDS, stages 0-2 in flight; once stage 0 has
+  // landed and the scale writes are done, everybody may read stage 0
+  load_scales(0);
 #pragma unroll
   for (int p = 0; p < DS - 1; ++p) issue(p);
-  wait_vm_barrier<2 * NL>();                                          // stage 0 landed
+  store_scales(0);
+  wait_vm_barrier<2 * NL, true>();
   Frag f0, f1;
   read(0, f0);
   // One stage: the NL DMA issues for stage kt+3 and the fragment reads of
   // stage kt+1 are spread over the TM x TN MFMAs of stage kt (with 256 x 256
-  // tiles: one DMA and two reads after each of the first 12 of 16), the
+  // tiles: one DMA and two reads after each of the first 8 of 16), the
   // fragment masks after the rest. The MFMAs still queue behind the DMA
   // issues (each holds the wavefront for tens of cycles), but less than when
   // they come back to back.
@@ -651,12 +691,25 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  // An iteration runs stages kt, kt+1 and reads stages kt+1, kt+2. In the
+  // first half of scale block b (kt = 4b) it loads block b+1's scales into
+  // registers; in the second half (kt = 4b + 2) it writes them to the ring
+  // slot of block b-1, which every wavefront finished reading with stage 4b,
+  // before the barrier that precedes the read of stage 4b + 4.
+  //
+  // Waits: before a stage that reads stage k+1, every load but the most
+  // recent NL (stage k+2's DMAs) is complete. The scale loads (NSL) go right
+  // after the first wait of a first half, before that stage's DMAs, so the
+  // next wait allows NL + NSL outstanding; they are complete at the wait
+  // after that, long before the second half writes them out.
   for (int64_t kt = 0; kt < nk; kt += 2) {
-    // stage kt+1 has landed once only stage kt+2's loads are pending; every
-    // wavefront is past its reads of stage kt-1, whose buffer stage kt+3 reuses
+    const bool second = (kt & 2) != 0;                   // uniform
     wait_vm_barrier<NL>();
+    if (!second) load_scales(kt / SB + 1);
+    else store_scales(kt / SB + 1);
     stage(kt + DS - 1, kt + 1, f0, f1);
-    wait_vm_barrier<NL>();
+    if (second) wait_vm_barrier<NL, true>();             // scale writes visible
+    else wait_vm_barrier<NL + NSL>();
     stage(kt + DS, kt + 2, f1, f0);     // all zero past the end
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");      // ring drained, LDS free
@@ -840,7 +893,7 @@ hipError_t rowxrow_dma(const uint8_t* a, const uint8_t* ae, const uint8_t* b, co
                        BLayout bl, void* out, bool out_bf16, hipStream_t stream) {
   static bool done[2] = {false, false};
   auto k = out_bf16 ? k_dgrad_dma<true, BM, BN> : k_dgrad_dma<false, BM, BN>;
-  const size_t lds = (size_t)DS * DmaTile<BM, BN>::STAGE;
+  const size_t lds = (size_t)DmaTile<BM, BN>::LDS;
   hipError_t e = set_lds(k, lds, done[out_bf16]);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((m_cap + BM - 1) / BM + G) * (ncols / BN);   // bound on live tiles
@@ -907,7 +960,7 @@ hipError_t launch_wgrad(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* 
   if (G == 0) return hipSuccess;
   if (N % 256 == 0 && K % 256 == 0) {
     static bool done = false;
-    const size_t lds = (size_t)DS * DmaTile<256, 256>::STAGE;
+    const size_t lds = (size_t)DmaTile<256, 256>::LDS;
     hipError_t e = set_lds(k_wgrad_dma, lds, done);
     if (e != hipSuccess) return e;
     const int64_t tiles = (int64_t)G * (N / 256) * (K / 256);
