@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ao,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bo,
     const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y,
-    int64_t P, int tail_cus) {
+    int64_t P, int tail_cus, int persist) {
   constexpr int TM = 4, TN = 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
 
@@ -368,23 +368,13 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   // the ones left for a second round are the cheapest (a partial tile runs
   // MFMAs only for its valid row blocks).
   const int ntn = (int)(N / LT);
-  int g, nt;
-  int64_t row0, row_end;
-  if constexpr (WG) {
-    // tiles expert by expert; inside an expert, blocks of 4 output-column
-    // tiles with the output-row tile fastest
-    const int nrt = (int)(N / LT), nct = (int)(K / LT);
-    const int per = nrt * nct, total = G * per;
-    if ((int)blockIdx.x >= total) return;
-    const int tt = (int)xcd_tile(blockIdx.x, total);
-    g = tt / per;
-    int mi, ni;
-    block_order(tt - g * per, nrt, nct, mi, ni);
-    nt = ni;
-    row0 = (int64_t)mi * LT;
-    row_end = row0 + LT;
-  } else {
-    int* pre = reinterpret_cast<int*>(lsm);            // [3G+1], before any stage load
+  // persist: the grid is at most one workgroup per compute unit and
+  // workgroup w runs the tiles w, w + gridDim, ... in the order above (the
+  // scan of tile counts kept in LDS past the stage buffers); otherwise one
+  // tile per workgroup (the scan's memory is then reused by the stages).
+  int* pre = reinterpret_cast<int*>(persist ? lsm + NS * kStageBytes : lsm);   // [3G+1]
+  int nfull = 0, nbig = 0, total = 0;
+  if constexpr (!WG) {
     tile_prefix(3 * G, [&](int e) {
       const int part = e / G, gg = e - part * G;
       const int64_t m = offsets[gg + 1] - offsets[gg], rem = m % LT;
@@ -396,10 +386,30 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     // partial tiles fit in one round of workgroups and the short tails would
     // start a second one, the tails are left to the streaming kernel launched
     // right after this one (it takes the same decision)
-    const int nfull = pre[G], nbig = pre[2 * G], all = pre[3 * G];
-    const int total = tail_cus > 0 && nbig <= tail_cus && all > tail_cus ? nbig : all;
-    if ((int)blockIdx.x >= total) return;
-    const int t = (int)blockIdx.x;
+    nfull = pre[G];
+    nbig = pre[2 * G];
+    const int all = pre[3 * G];
+    total = tail_cus > 0 && nbig <= tail_cus && all > tail_cus ? nbig : all;
+  }
+  for (int v = (int)blockIdx.x;; v += (int)gridDim.x) {
+  int g, nt;
+  int64_t row0, row_end;
+  if constexpr (WG) {
+    // tiles expert by expert; inside an expert, blocks of 4 output-column
+    // tiles with the output-row tile fastest
+    const int nrt = (int)(N / LT), nct = (int)(K / LT);
+    const int per = nrt * nct, total_wg = G * per;
+    if (v >= total_wg) return;
+    const int tt = (int)xcd_tile(v, total_wg);
+    g = tt / per;
+    int mi, ni;
+    block_order(tt - g * per, nrt, nct, mi, ni);
+    nt = ni;
+    row0 = (int64_t)mi * LT;
+    row_end = row0 + LT;
+  } else {
+    if (v >= total) return;
+    const int t = v;
     const int tt = t < nfull ? (int)xcd_tile(t, nfull)
                  : t < nbig  ? nfull + (int)xcd_tile(t - nfull, nbig - nfull)
                              : nbig + (int)xcd_tile(t - nbig, total - nbig);
@@ -420,7 +430,9 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
       nt = loc;
       row0 = o0 + fm * LT;
     }
-    __syncthreads();                                   // pre's memory is reused below
+    // the scan's memory (one tile), or the previous tile's epilogue staging
+    // (persistent), is overwritten by the stages below
+    __syncthreads();
   }
   const int64_t n0 = (int64_t)nt * LT;
 
@@ -729,25 +741,46 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
                                           (obase + orow * ldo + col0) * ES + c * 16));
     }
   }
+  if (WG || !persist) return;
+  }
 }
+
+#ifndef NVFP4MOE_FWD_PERSIST
+#define NVFP4MOE_FWD_PERSIST 1
+#endif
+constexpr bool kFwdPersist = NVFP4MOE_FWD_PERSIST != 0;
+constexpr int kPersistFactor = 2;            // bound on tiles above this many per CU
+constexpr size_t kMaxPreBytes = 16384;       // tile-count scan kept in LDS (G <= 1365)
 
 template <int NS>
 hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
                        const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
                        int64_t m_cap, int64_t N, int64_t K, void* y, bool y_bf16,
                        int tail_cus, hipStream_t stream) {
-  const size_t lds = (size_t)NS * kStageBytes;
   const int64_t tiles = ((m_cap + LT - 1) / LT + G) * (N / LT);   // bound on live tiles
+  // Persistent (one workgroup per compute unit, each looping over tiles)
+  // when the bound on the tile count is well above the live tiles it may
+  // hold: workgroups past the live tiles only start and exit, but the
+  // dispatcher issues them one after another at the end of the launch
+  // (e.g. a capacity-sized down-projection: 17152 workgroups for 2336 tiles).
+  // The tile-count scan then stays in LDS beside the stages.
+  const int64_t cus = device_cu_count();
+  const size_t pre_bytes = ((size_t)(3 * G + 1) * 4 + 15) & ~(size_t)15;
+  const bool persist = kFwdPersist && pre_bytes <= kMaxPreBytes &&
+                       tiles > (int64_t)kPersistFactor * cus;
+  const size_t lds = (size_t)NS * kStageBytes + (persist ? pre_bytes : 0);
   auto k = y_bf16 ? k_fwd_lds4<NS, true> : k_fwd_lds4<NS, false>;
   static bool attr_set[2] = {false, false};
   if (!attr_set[y_bf16]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)((size_t)NS * kStageBytes + kMaxPreBytes));
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
-  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, 0,
-                                           tail_cus);
+  const int64_t grid = persist ? cus : tiles;
+  k<<<(unsigned)grid, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, 0,
+                                          tail_cus, persist ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1129,7 +1162,7 @@ hipError_t launch_wgrad_nvfp4(const uint8_t* ac, const uint8_t* as, const float*
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, padded, G, N, K, dw, P, 0);
+  k<<<(unsigned)tiles, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, padded, G, N, K, dw, P, 0, 0);
   return hipGetLastError();
 }
 
