@@ -335,7 +335,13 @@ constexpr int LBK = 128;                  // K elements per stage
 constexpr int LCB = LBK / 2;              // code bytes per row per stage
 constexpr int LSB = LBK / 16;             // scale bytes per row per stage
 constexpr int LT = 256;                   // tile rows (A) and columns (B)
-constexpr int kStageBytes = 2 * LT * LCB + 2 * LT * LSB;
+constexpr int kStageBytes = 2 * LT * LCB;           // one stage's codes, A then B
+constexpr int SBK = 4;                                // stages per scale block
+constexpr int kScaleRow = SBK * LSB;                  // scale bytes of a row per block
+constexpr int kScaleSlot = 2 * LT * kScaleRow;        // one block, A rows then B rows
+constexpr int kScaleRing = 2 * kScaleSlot;            // two blocks
+template <int NS>
+constexpr int kMainLds = NS * kStageBytes + kScaleRing;
 constexpr int kBufWord3 = 0x00020000;     // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   // workgroup w runs the tiles w, w + gridDim, ... in the order above (the
   // scan of tile counts kept in LDS past the stage buffers); otherwise one
   // tile per workgroup (the scan's memory is then reused by the stages).
-  int* pre = reinterpret_cast<int*>(persist ? lsm + NS * kStageBytes : lsm);   // [3G+1]
+  int* pre = reinterpret_cast<int*>(persist ? lsm + kMainLds<NS> : lsm);      // [3G+1]
   int nfull = 0, nbig = 0, total = 0;
   if constexpr (!WG) {
     tile_prefix(3 * G, [&](int e) {
@@ -458,11 +464,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   const __amdgpu_buffer_rsrc_t rbs = __builtin_amdgcn_make_buffer_rsrc(
       first_lane_ptr(bs + brow0 * KSB + sb0), (short)0, (int)(uint32_t)(LT * KSB), kBufWord3);
 
-  // DMA offsets of this lane. Codes: instruction i of wavefront w fills rows
-  // (4i + w) * 16 + lane / 4 at position lane % 4; scales: instruction j
-  // fills rows (4j + w) * 32 + lane / 2, dword lane % 2. Rows past the group
-  // end read the tile's first row (results discarded).
-  uint32_t oac[4], obc[4], oas[2], obs[2];
+  // DMA offsets of this lane: code instruction i of wavefront w fills rows
+  // (4i + w) * 16 + lane / 4 at position lane % 4. Rows past the group end
+  // read the tile's first row (results discarded).
+  uint32_t oac[4], obc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (4 * i + wave) * 16 + (lane >> 2);
@@ -471,12 +476,17 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     oac[i] = (uint32_t)(ra * KB + c * 16);
     obc[i] = (uint32_t)(r * KB + c * 16);
   }
+  // Scales. A block of SBK stages holds 32 scale bytes per row ([slot][A rows,
+  // then B rows][32]); in stage s of a block each thread loads the 16-byte
+  // half tid & 1 of row s * 128 + tid / 2 of the 512 (A for s < 2, B after)
+  // of the next block, and writes it to the ring in stage s + 1, before that
+  // stage's barrier. Rows past the group end read the tile's first row.
+  uint32_t osc[SBK];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = (4 * j + wave) * 32 + (lane >> 1);
-    const int ra = r < arows ? r : 0;
-    oas[j] = (uint32_t)(ra * KSB + (lane & 1) * 4);
-    obs[j] = (uint32_t)(r * KSB + (lane & 1) * 4);
+  for (int q = 0; q < SBK; ++q) {
+    const int r = (q & 1) * 128 + (tid >> 1);
+    const int rr = q < 2 ? (r < arows ? r : 0) : r;
+    osc[q] = (uint32_t)(rr * KSB + (tid & 1) * 16);
   }
   // Stage kt goes to LDS buffer kt % NS. A stage past the end (kt >= nk) is
   // issued too, through buffer resources of size 0: such loads return zeros
@@ -486,37 +496,45 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   // load waits for its predecessor to have read a shared one.
   const __amdgpu_buffer_rsrc_t rnull = __builtin_amdgcn_make_buffer_rsrc(
       first_lane_ptr(bc), (short)0, 0, kBufWord3);
-  // part 0: the A tile's codes and scales, 1: the weight tile's, 2: both
+  // part 0: the A tile's codes, 1: the weight tile's, 2: both
   auto issue = [&](int64_t kt, int64_t nk, int part) {
     uint8_t* st = lsm + (kt % NS) * kStageBytes;
     const bool real = kt < nk;
     const int64_t ks = real ? kt : 0;
-    const int so = (int)(ks * LCB), ss = (int)(ks * LSB);
+    const int so = (int)(ks * LCB);
     const __amdgpu_buffer_rsrc_t xac = real ? rac : rnull, xbc = real ? rbc : rnull;
-    const __amdgpu_buffer_rsrc_t xas = real ? ras : rnull, xbs = real ? rbs : rnull;
     if (part != 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xac, (lds_void*)(st + (4 * i + wave) * 1024), 16,
                                                  oac[i], so, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xas, (lds_void*)(st + 2 * LT * LCB + (4 * j + wave) * 256), 4, oas[j], ss, 0, 0);
     }
     if (part != 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             xbc, (lds_void*)(st + LT * LCB + (4 * i + wave) * 1024), 16, obc[i], so, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xbs, (lds_void*)(st + 2 * LT * LCB + LT * LSB + (4 * j + wave) * 256), 4, obs[j], ss, 0,
-            0);
     }
   };
-  constexpr int kPerStage = 12;            // DMA instructions per stage and wavefront
+  constexpr int kPerStage = 8;             // code DMA instructions per stage and wavefront
+  // the scale piece written in stage kt (group kt % SBK of block kt / SBK + 1),
+  // loaded one stage earlier; blocks past the contraction's end read zeros or
+  // other rows' bytes that only stages past the end would use
+  u32x4 spiece;
+  auto load_piece = [&](int64_t kt) {
+    const int q = (int)(kt % SBK);
+    const int64_t blk = kt / SBK + 1;
+    const uint32_t off = osc[0] * (q == 0) + osc[1] * (q == 1) + osc[2] * (q == 2) +
+                         osc[3] * (q == 3) + (uint32_t)(blk * kScaleRow);
+    spiece = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q < 2 ? ras : rbs,
+                                                                             off, 0, 0));
+  };
+  auto store_piece = [&](int64_t kt) {
+    const int q = (int)(kt % SBK);
+    const int64_t blk = kt / SBK + 1;
+    *reinterpret_cast<u32x4*>(lsm + NS * kStageBytes + (blk & 1) * kScaleSlot + q * 4096 +
+                              tid * 16) = spiece;
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -538,14 +556,14 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     const int r = (2 * i + wm) * 32 + r32;
 #pragma unroll
     for (int c = 0; c < 2; ++c) fa[i][c] = r * LCB + (((2 * half + c) ^ ((r >> 2) & 3)) << 4);
-    sa_off[i] = 2 * LT * LCB + r * LSB + half * 4;
+    sa_off[i] = NS * kStageBytes + r * kScaleRow + half * 4;
   }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int r = wn * 128 + j * 32 + r32;
 #pragma unroll
     for (int c = 0; c < 2; ++c) fb[j][c] = LT * LCB + r * LCB + (((2 * half + c) ^ ((r >> 2) & 3)) << 4);
-    sb_off[j] = 2 * LT * LCB + LT * LSB + r * LSB + half * 4;
+    sb_off[j] = NS * kStageBytes + (LT + r) * kScaleRow + half * 4;
   }
 
   // The wavefront's rows of A: TA of its TM 32-row blocks hold valid rows
@@ -566,12 +584,13 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
 #pragma unroll
     for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const u32x4*>(st + fb[j][c]);
   };
-  auto read_scales = [&](const uint8_t* st) {
+  auto read_scales = [&](int64_t kt) {        // stage kt's: block kt / SBK, bytes 8 (kt % SBK)
     if constexpr (TA == 0) return;
+    const uint8_t* sc = lsm + ((kt / SBK) & 1) * kScaleSlot + (kt % SBK) * LSB;
 #pragma unroll
-    for (int i = 0; i < TA; ++i) sca[i] = *reinterpret_cast<const uint32_t*>(st + sa_off[i]);
+    for (int i = 0; i < TA; ++i) sca[i] = *reinterpret_cast<const uint32_t*>(sc + sa_off[i]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) scb[j] = *reinterpret_cast<const uint32_t*>(st + sb_off[j]);
+    for (int j = 0; j < TN; ++j) scb[j] = *reinterpret_cast<const uint32_t*>(sc + sb_off[j]);
   };
   auto cvt_scales = [&](int p) {       // E4M3 -> f16, exact
     if constexpr (TA == 0) return;
@@ -649,13 +668,32 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   // stage kt+NS (steps 4 and 5) and the reads of chunk 0 and the scales of
   // stage kt+1 (step 6); the lower scale halves are converted before the last
   // region, which converts step 0 of kt+1. One barrier per stage.
-  static_assert(kPerStage == 12, "wait counts assume 12 loads per stage and wavefront");
-  static_assert(NS == 3, "wait counts assume 3 stages in flight");
+  //
+  // Scales: the piece loaded in region 5 of stage kt (before that stage's
+  // code DMAs, so waiting for it never waits for them) is written in region
+  // 1 of stage kt+1, before its barrier; block b+1 is complete at the
+  // barrier of stage 4b+3, whose region 7 reads stage 4b+4's scales. Its
+  // ring slot held block b-1, last read in region 7 of stage 4b-2.
+  static_assert(kPerStage == 8, "wait counts assume 8 code loads per stage and wavefront");
+  static_assert(NS == 3 && SBK == 4, "wait counts assume 3 stages in flight");
+  {
+    // prologue: scale block 0 (four pieces) and the piece stage 0 writes,
+    // then the code stages 0..NS-1
+    u32x4 p0[SBK];
 #pragma unroll
-  for (int p = 0; p < NS; ++p) issue(p, nk, 2);
-  asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");   // stage 0 landed
+    for (int q = 0; q < SBK; ++q)
+      p0[q] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(q < 2 ? ras : rbs, osc[q], 0, 0));
+    load_piece(0);
+#pragma unroll
+    for (int p = 0; p < NS; ++p) issue(p, nk, 2);
+#pragma unroll
+    for (int q = 0; q < SBK; ++q)
+      *reinterpret_cast<u32x4*>(lsm + NS * kStageBytes + q * 4096 + tid * 16) = p0[q];
+  }
+  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 landed
   read_chunk(lsm, 0, c0a, c0b);
-  read_scales(lsm);
+  read_scales(0);
   cvt_scales(0);
   Frags f0, f1;
   deq_step(0, f0);
@@ -664,17 +702,19 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     const uint8_t* st = lsm + (kt % NS) * kStageBytes;
     const uint8_t* sn = lsm + ((kt + 1) % NS) * kStageBytes;
     cvt_scales(1);
-    region(f0, f1, 1, [&] { read_chunk(st, 1, c1a, c1b); }, Z{}, std::integral_constant<int, TA + TN>{});
+    region(f0, f1, 1, [&] { store_piece(kt); read_chunk(st, 1, c1a, c1b); }, Z{},
+           std::integral_constant<int, TA + TN>{});
     region(f1, f0, 2, none, Z{}, Z{});
     region(f0, f1, 3, none, Z{}, Z{});
     region(f1, f0, 4, none, Z{}, Z{});
     // Every wavefront has finished reading stage kt, and stage kt+1 has
     // landed once only stage kt+2's loads are pending. Branch-free: after the
     // last stage the reads below fetch data that is never used.
-    asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    region(f0, f1, 5, [&] { issue(kt + NS, nk, 0); }, std::integral_constant<int, 6>{}, Z{});
-    region(f1, f0, 6, [&] { issue(kt + NS, nk, 1); }, std::integral_constant<int, 6>{}, Z{});
-    region(f0, f1, 7, [&] { read_chunk(sn, 0, c0a, c0b); read_scales(sn); }, Z{},
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    region(f0, f1, 5, [&] { load_piece(kt + 1); issue(kt + NS, nk, 0); },
+           std::integral_constant<int, 5>{}, Z{});
+    region(f1, f0, 6, [&] { issue(kt + NS, nk, 1); }, std::integral_constant<int, 4>{}, Z{});
+    region(f0, f1, 7, [&] { read_chunk(sn, 0, c0a, c0b); read_scales(kt + 1); }, Z{},
            std::integral_constant<int, 2 * (TA + TN)>{});
     cvt_scales(0);
     region(f1, f0, 0, none, Z{}, Z{});   // step 0 of stage kt+1 (unused after the last stage)
@@ -751,6 +791,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
 constexpr bool kFwdPersist = NVFP4MOE_FWD_PERSIST != 0;
 constexpr int kPersistFactor = 2;            // bound on tiles above this many per CU
 constexpr size_t kMaxPreBytes = 16384;       // tile-count scan kept in LDS (G <= 1365)
+static_assert(kMainLds<3> + kMaxPreBytes <= 160 * 1024, "LDS budget of k_fwd_lds4");
 
 template <int NS>
 hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
@@ -768,13 +809,13 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
   const size_t pre_bytes = ((size_t)(3 * G + 1) * 4 + 15) & ~(size_t)15;
   const bool persist = kFwdPersist && pre_bytes <= kMaxPreBytes &&
                        tiles > (int64_t)kPersistFactor * cus;
-  const size_t lds = (size_t)NS * kStageBytes + (persist ? pre_bytes : 0);
+  const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0);
   auto k = y_bf16 ? k_fwd_lds4<NS, true> : k_fwd_lds4<NS, false>;
   static bool attr_set[2] = {false, false};
   if (!attr_set[y_bf16]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)((size_t)NS * kStageBytes + kMaxPreBytes));
+                                       (int)((size_t)kMainLds<NS> + kMaxPreBytes));
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
@@ -1151,7 +1192,7 @@ hipError_t launch_wgrad_nvfp4(const uint8_t* ac, const uint8_t* as, const float*
                               const int64_t* padded, int G, int64_t P, int64_t N, int64_t K,
                               float* dw, hipStream_t stream) {
   constexpr int NS = 3;
-  const size_t lds = (size_t)NS * kStageBytes;
+  const size_t lds = (size_t)kMainLds<NS>;
   const int64_t tiles = (int64_t)G * (N / LT) * (K / LT);
   if (tiles == 0) return hipSuccess;
   auto k = k_fwd_lds4<NS, false, true>;
