@@ -440,26 +440,37 @@ __global__ __launch_bounds__(256, 1) void k_wgrad(const uint8_t* __restrict__ dy
 constexpr int DK = 64;                                // contraction elements per stage
 constexpr int DS = 4;                                 // stages in the ring
 constexpr int SB = 4;                                 // stages per scale block (8 bytes a row)
+#ifndef NVFP4MOE_DMA_WN256
+#define NVFP4MOE_DMA_WN256 4
+#endif
+// wavefront columns of a 256 x 256 tile: 4 (eight wavefronts, two per SIMD) or 2
+constexpr int kDmaWn256 = NVFP4MOE_DMA_WN256;
+static_assert(kDmaWn256 == 2 || kDmaWn256 == 4, "2 or 4 wavefront columns");
 
-// Workgroup tile BM x BN (rows of A x rows of B), 2 x 2 wavefronts of
-// (BM/2) x (BN/2), that is TM x TN MFMA tiles of 32 x 32 each. A code DMA
-// instruction fills 16 rows, so every wavefront issues NL = (BM + BN) / 64
-// loads per stage; a scale block is NSL loads per thread (row t, t + 256, ...
-// of the BM + BN rows; threads past the last row load row 0 into a spare
-// slot, so every wavefront issues the same count).
-template <int BM, int BN>
+// Workgroup tile BM x BN (rows of A x rows of B), 2 x WN wavefronts of
+// (BM/2) x (BN/WN), that is TM x TN MFMA tiles of 32 x 32 each: WN = 2 puts
+// one wavefront on each SIMD, WN = 4 two (so one's loads and barrier waits
+// overlap the other's MFMAs). A code DMA instruction fills 16 rows, so every
+// wavefront issues NL = (BM + BN) / (16 NW) loads per stage; a scale block is
+// NSL loads per thread (row t, t + 64 NW, ... of the BM + BN rows; threads
+// past the last row load row 0 into a spare slot, so every wavefront issues
+// the same count).
+template <int BM, int BN, int WN = 2>
 struct DmaTile {
-  static constexpr int TM = BM / 64, TN = BN / 64;
-  static constexpr int CA = BM / 64, CB = BN / 64;    // code loads per stage and wavefront
+  static constexpr int NW = 2 * WN;                   // wavefronts
+  static constexpr int NT = 64 * NW;                  // threads
+  static constexpr int TM = BM / 64, TN = BN / (32 * WN);
+  static constexpr int CA = BM / (16 * NW), CB = BN / (16 * NW);   // code loads per stage, wavefront
   static constexpr int NL = CA + CB;
   static constexpr int R = BM + BN;                   // scale rows
-  static constexpr int NSL = (R + 255) / 256;         // scale loads per thread and block
+  static constexpr int NSL = (R + NT - 1) / NT;       // scale loads per thread and block
   static constexpr int A0 = 0, B0 = BM * DK;          // code planes [rows][64]
   static constexpr int STAGE = (BM + BN) * DK;
-  static constexpr int SBLK = (NSL * 256) * 8;        // one scale block, spare rows included
+  static constexpr int SBLK = (NSL * NT) * 8;         // one scale block, spare rows included
   static constexpr int SC = DS * STAGE;               // scale ring after the code stages
   static constexpr int LDS = SC + 2 * SBLK;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile shape");
+  static_assert(BM % 64 == 0 && BN % (32 * WN) == 0 && BM % (16 * NW) == 0 &&
+                BN % (16 * NW) == 0 && BN % 64 == 0, "tile shape");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -468,30 +479,31 @@ typedef __attribute__((address_space(3))) void lds_void;
 // shapes' load counts)
 template <int N, bool LGKM = false>
 __device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N == 7 || N == 8 || N == 9 || N == 10 || N == 14 || N == 16, "add the count");
+  static_assert(N == 4 || N == 5 || N == 7 || N == 8 || N == 9 || N == 10 || N == 14 || N == 16,
+                "add the count");
 #define NVFP4MOE_WAIT(n)                                                              \
   if constexpr (N == n) {                                                             \
     if constexpr (LGKM) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
     else asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory");           \
   }
-  NVFP4MOE_WAIT(7) NVFP4MOE_WAIT(8) NVFP4MOE_WAIT(9) NVFP4MOE_WAIT(10) NVFP4MOE_WAIT(14)
-  NVFP4MOE_WAIT(16)
+  NVFP4MOE_WAIT(4) NVFP4MOE_WAIT(5) NVFP4MOE_WAIT(7) NVFP4MOE_WAIT(8) NVFP4MOE_WAIT(9)
+  NVFP4MOE_WAIT(10) NVFP4MOE_WAIT(14) NVFP4MOE_WAIT(16)
 #undef NVFP4MOE_WAIT
 }
 
-// Workgroup tile (64 TM_) x (64 TN_). (A class template's member rather than
-// a function template: the kernels that call it are templates whose host-side
-// instantiation would otherwise reject the device-only callee.)
-template <int TM_, int TN_>
+// Workgroup tile BM x BN, 2 x WN wavefronts. (A class template's member
+// rather than a function template: the kernels that call it are templates
+// whose host-side instantiation would otherwise reject the device-only
+// callee.)
+template <int BM, int BN, int WN>
 struct DmaLoop {
+  using C = DmaTile<BM, BN, WN>;
 static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const Operand& B,
-                                           int64_t L, f32x16 (&acc)[TM_][TN_]) {
-  constexpr int BM = 64 * TM_, BN = 64 * TN_;
-  using C = DmaTile<BM, BN>;
-  constexpr int TM = C::TM, TN = C::TN, NL = C::NL, NSL = C::NSL;
+                                           int64_t L, f32x16 (&acc)[C::TM][C::TN]) {
+  constexpr int TM = C::TM, TN = C::TN, NL = C::NL, NSL = C::NSL, NW = C::NW, NT = C::NT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, r32 = lane & 31;
   const int64_t nk = (L + DK - 1) / DK;
   if (nk == 0) return;
@@ -513,45 +525,45 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
                                               uniform_u32(n * (X.ld / 32)), kBufferWord3);
   }
   // lane offsets: code instruction i of this wavefront fills rows 16m .. 16m+15
-  // (m = 4i + wave; lane: row 16m + lane/4, position lane%4)
+  // (m = NW i + wave; lane: row 16m + lane/4, position lane%4)
   constexpr int CM = C::CA > C::CB ? C::CA : C::CB;
   uint32_t oq[2][CM];
 #pragma unroll
   for (int o = 0; o < 2; ++o)
 #pragma unroll
     for (int i = 0; i < (o ? C::CB : C::CA); ++i) {
-      const int row = 16 * (4 * i + wave) + (lane >> 2);
+      const int row = 16 * (NW * i + wave) + (lane >> 2);
       const int piece = (lane & 3) ^ ((row >> 2) & 3);
       const int rr = row < nrow[o] ? row : 0;
       oq[o][i] = (uint32_t)(rr * ld[o] + c0[o] + piece * 16);
     }
   // stage kt -> buffer kt % DS; past the end: offsets outside the ranges
-  // (zeros, no memory traffic) so every stage has the same load count
-  auto issue = [&](int64_t kt) {
+  // (zeros, no memory traffic) so every stage has the same load count.
+  // Load d of a stage: A's code loads first, then B's.
+  auto issue_one = [&](int64_t kt, int d) {
     uint8_t* st = lsm + (kt % DS) * C::STAGE;
     const bool real = kt < nk;
     const uint32_t away = real ? 0u : 0x40000000u;
     const uint32_t kq = real ? (uint32_t)(kt * DK) : 0u;
-#pragma unroll
-    for (int o = 0; o < 2; ++o)
-#pragma unroll
-      for (int i = 0; i < (o ? C::CB : C::CA); ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rq[o], (lds_void*)(st + (o ? C::B0 : C::A0) + (4 * i + wave) * 1024), 16,
-            oq[o][i] + kq + away, 0, 0, 0);
+    const int o = d < C::CA ? 0 : 1, i = d < C::CA ? d : d - C::CA;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rq[o], (lds_void*)(st + (o ? C::B0 : C::A0) + (NW * i + wave) * 1024), 16,
+        oq[o][i] + kq + away, 0, 0, 0);
   };
-  // scale rows of this thread: row q = tid + 256 u of the BM + BN (A first);
+  // scale rows of this thread: row q = tid + NT u of the BM + BN (A first);
   // rows past the tile's valid rows read the tile's first row; q >= BM + BN
   // (spare slots) read row 0 of A
   uint32_t eo[NSL], esh[NSL];          // dword-aligned offset, byte shift
   bool eb_[NSL];
 #pragma unroll
   for (int u = 0; u < NSL; ++u) {
-    const int q = tid + 256 * u;
+    const int q = tid + NT * u;
     const int o = q < BM ? 0 : (q < C::R ? 1 : 0);
     const int rr0 = q < BM ? q : (q < C::R ? q - BM : 0);
     const int rr = rr0 < nrow[o] ? rr0 : 0;
-    eb_[u] = o == 1;
+    // the operand is the same across a wavefront (BM and BM + BN are
+    // multiples of 64): a scalar select of the buffer descriptor
+    eb_[u] = __builtin_amdgcn_readfirstlane(o) == 1;
     const uint32_t byte_off = (uint32_t)(rr * (ld[o] / 32) + c0[o] / 32);
     eo[u] = byte_off & ~3u;
     esh[u] = byte_off & 3u;
@@ -575,53 +587,48 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
     for (int u = 0; u < NSL; ++u) {
       const u32x2v w = {__builtin_amdgcn_alignbyte(sreg[u][1], sreg[u][0], esh[u]),
                         __builtin_amdgcn_alignbyte(sreg[u][2], sreg[u][1], esh[u])};
-      *reinterpret_cast<u32x2v*>(d + (tid + 256 * u) * 8) = w;
+      *reinterpret_cast<u32x2v*>(d + (tid + NT * u) * 8) = w;
     }
   };
 
-  // fragment addresses (stage-relative) and scale rows (block-relative)
-  int fa[TM][2], fb[TN][2], sa[TM], sbo[TN];
+  // fragment addresses (stage-relative) and scale rows (block-relative) of
+  // fragment 0; fragment i sits i * 32 rows further (same swizzle: the piece
+  // position depends on row bits 2-3 only), a constant offset
+  int fa[2], fb[2];
+  const int ra0 = wm * (BM / 2) + r32, rb0 = wn * (BN / WN) + r32;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int ra = wm * (BM / 2) + i * 32 + r32;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) fa[i][c] = C::A0 + ra * DK + (((2 * c + half) ^ ((ra >> 2) & 3)) << 4);
-    sa[i] = C::SC + ra * 8 + half;
+  for (int c = 0; c < 2; ++c) {
+    fa[c] = C::A0 + ra0 * DK + (((2 * c + half) ^ ((ra0 >> 2) & 3)) << 4);
+    fb[c] = C::B0 + rb0 * DK + (((2 * c + half) ^ ((rb0 >> 2) & 3)) << 4);
   }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int rb = wn * (BN / 2) + j * 32 + r32;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) fb[j][c] = C::B0 + rb * DK + (((2 * c + half) ^ ((rb >> 2) & 3)) << 4);
-    sbo[j] = C::SC + (BM + rb) * 8 + half;
-  }
-  struct Frag {
-    i32x8 a[TM], b[TN];
-    int32_t as[TM], bs[TN];
-  };
-  auto read = [&](int64_t kt, Frag& f) {
+  const int sa = C::SC + ra0 * 8 + half, sbo = C::SC + (BM + rb0) * 8 + half;
+  // Fragments: A single-buffered (fragment i of the next stage is read into
+  // the registers of this stage's fragment i right after its last MFMA), B
+  // double-buffered (every MFMA of a stage row uses all of B). The scale
+  // bytes follow their fragments.
+  i32x8 fa_[TM], fb_[2][TN];
+  int32_t fas[TM], fbs[2][TN];
+  auto stage_ptrs = [&](int64_t kt, const uint8_t*& p0, const uint8_t*& p1, const uint8_t*& ps,
+                        int f0, int f1, int fs) {
     const uint8_t* st = lsm + (kt % DS) * C::STAGE;
+    p0 = st + f0;
+    p1 = st + f1;
     // stage kt's scale bytes: block kt / SB in the ring, bytes 2 (kt % SB) + half
-    const int so = (int)(((kt / SB) & 1) * C::SBLK + 2 * (kt % SB));
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + fa[i][0]);
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + fa[i][1]);
-      f.a[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      f.as[i] = *reinterpret_cast<const uint8_t*>(lsm + sa[i] + so);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const u32x4 y0 = *reinterpret_cast<const u32x4*>(st + fb[j][0]);
-      const u32x4 y1 = *reinterpret_cast<const u32x4*>(st + fb[j][1]);
-      f.b[j] = i32x8{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3],
-                     (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
-      f.bs[j] = *reinterpret_cast<const uint8_t*>(lsm + sbo[j] + so);
-    }
-    // Contraction elements past L are zero: MX block 1 of a last stage that
-    // holds 32 elements, and whole stages past the end (the loop runs an even
-    // number of stages). No branch: masks.
+    ps = lsm + fs + (int)(((kt / SB) & 1) * C::SBLK + 2 * (kt % SB));
+  };
+  auto frag = [&](const uint8_t* p0, const uint8_t* p1, int at) {
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(p0 + at);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(p1 + at);
+    return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                 (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+  };
+  // Contraction elements past L are zero: MX block 1 of a last stage that
+  // holds 32 elements, and whole stages past the end (the loop runs an even
+  // number of stages; their DMAs already gave zero codes, the masks also
+  // neutralise the scale bytes there). Applied, on a uniform branch, only to
+  // a stage that ends past L.
+  auto mask = [&](int64_t kt, auto pb) {
+    constexpr int PB = decltype(pb)::value;
     const int64_t rem = L - kt * DK;
     const int keep0 = rem > 0 ? -1 : 0, keep1 = rem > 32 ? -1 : 0;
     const int keeps = half ? keep1 : keep0;
@@ -629,29 +636,20 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        f.a[i][e] &= keep0;
-        f.a[i][e + 4] &= keep1;
+        fa_[i][e] &= keep0;
+        fa_[i][e + 4] &= keep1;
       }
-      f.as[i] = keeps ? f.as[i] : 127;
+      fas[i] = keeps ? fas[i] : 127;
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        f.b[j][e] &= keep0;
-        f.b[j][e + 4] &= keep1;
+        fb_[PB][j][e] &= keep0;
+        fb_[PB][j][e + 4] &= keep1;
       }
-      f.bs[j] = keeps ? f.bs[j] : 127;
+      fbs[PB][j] = keeps ? fbs[PB][j] : 127;
     }
-  };
-  auto mfmas = [&](const Frag& f) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        // B (output-column operand) first: the lane then holds 4 consecutive columns
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            f.b[j], f.a[i], acc[i][j], 0 /*E4M3*/, 0 /*E4M3*/, 0, f.bs[j], 0, f.as[i]);
   };
 
   static_assert(DS == 4 && 2 * NL < 64, "the wait counts assume 4 stages, NL loads per stage");
@@ -660,58 +658,99 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
   // landed and the scale writes are done, everybody may read stage 0
   load_scales(0);
 #pragma unroll
-  for (int p = 0; p < DS - 1; ++p) issue(p);
+  for (int p = 0; p < DS - 1; ++p)
+#pragma unroll
+    for (int d = 0; d < NL; ++d) issue_one(p, d);
   store_scales(0);
   wait_vm_barrier<2 * NL, true>();
-  Frag f0, f1;
-  read(0, f0);
-  // One stage: the NL DMA issues for stage kt+3 and the fragment reads of
-  // stage kt+1 are spread over the TM x TN MFMAs of stage kt (with 256 x 256
-  // tiles: one DMA and two reads after each of the first 8 of 16), the
-  // fragment masks after the rest. The MFMAs still queue behind the DMA
-  // issues (each holds the wavefront for tens of cycles), but less than when
-  // they come back to back.
-  auto stage = [&](int64_t kt_issue, int64_t kt_read, const Frag& cur, Frag& nxt) {
-    __builtin_amdgcn_sched_barrier(0);
-    issue(kt_issue);
-    read(kt_read, nxt);
-    mfmas(cur);
-    constexpr int NM = TM * TN;
-    constexpr int PD = (NL + NM - 1) / NM;                // DMA issues per MFMA
-    constexpr int ND = (NL + PD - 1) / PD;                // MFMAs that carry them
+  {
+    const uint8_t *pa0, *pa1, *psa, *pb0, *pb1, *psb;
+    stage_ptrs(0, pa0, pa1, psa, fa[0], fa[1], sa);
+    stage_ptrs(0, pb0, pb1, psb, fb[0], fb[1], sbo);
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
-      if (m < ND) {
-        __builtin_amdgcn_sched_group_barrier(0x020, PD, 0);               // DMA issues
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                // 2 LDS reads
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);               // fragment masks
-      }
+    for (int i = 0; i < TM; ++i) {
+      fa_[i] = frag(pa0, pa1, i * 32 * DK);
+      fas[i] = psa[i * 32 * 8];
     }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      fb_[0][j] = frag(pb0, pb1, j * 32 * DK);
+      fbs[0][j] = psb[j * 32 * 8];
+    }
+  }
+  // One stage: the MFMAs of stage kt_read - 1 (B buffer PB) in TM rows of TN;
+  // after row i, A fragment i of stage kt_read; B fragment j of stage kt_read
+  // (into the other buffer) and the NL DMA issues of stage kt_issue spread
+  // over the rows. MASK: the stage may end past L (then its fragments are
+  // masked first).
+  constexpr int PD = (NL + TM - 1) / TM;                 // DMA issues per row
+  auto stage = [&](int64_t kt_issue, int64_t kt_read, auto pb, auto masked) {
+    constexpr int PB = decltype(pb)::value, QB = 1 - PB;
+    if constexpr (decltype(masked)::value) mask(kt_read - 1, pb);
+    const uint8_t *pa0, *pa1, *psa, *pb0, *pb1, *psb;
+    stage_ptrs(kt_read, pa0, pa1, psa, fa[0], fa[1], sa);
+    stage_ptrs(kt_read, pb0, pb1, psb, fb[0], fb[1], sbo);
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        // B (output-column operand) first: the lane then holds 4 consecutive columns
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fb_[PB][j], fa_[i], acc[i][j], 0 /*E4M3*/, 0 /*E4M3*/, 0, fbs[PB][j], 0, fas[i]);
+#pragma unroll
+      for (int d = i * PD; d < (i + 1) * PD && d < NL; ++d) issue_one(kt_issue, d);
+      fa_[i] = frag(pa0, pa1, i * 32 * DK);
+      fas[i] = psa[i * 32 * 8];
+      // B fragments of the next stage over the first rows (the first MFMAs of
+      // the next stage need all of them)
+      static_assert(TN <= TM, "one B fragment per row");
+      if (i < TN) {
+        const int j = i;
+        fb_[QB][j] = frag(pb0, pb1, j * 32 * DK);
+        fbs[QB][j] = psb[j * 32 * 8];
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);                // the row's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x020, PD, 0);                // its DMA issues
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                 // its LDS reads
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  // An iteration runs stages kt, kt+1 and reads stages kt+1, kt+2. In the
-  // first half of scale block b (kt = 4b) it loads block b+1's scales into
-  // registers; in the second half (kt = 4b + 2) it writes them to the ring
-  // slot of block b-1, which every wavefront finished reading with stage 4b,
-  // before the barrier that precedes the read of stage 4b + 4.
+  // One scale block: runs stages kt .. kt+3 (kt = 4b) and reads stages kt+1
+  // .. kt+4. After the first wait it loads block b+1's scales into registers;
+  // in the third stage it writes them to the ring slot of block b-1, which
+  // every wavefront finished reading with stage 4b, before the barrier that
+  // precedes the read of stage 4b + 4. No branch inside (a branch lets the
+  // compiler move one stage's MFMAs past the next barrier), except in the
+  // masked last block, which stops after the stage that runs stage nk - 1.
   //
   // Waits: before a stage that reads stage k+1, every load but the most
   // recent NL (stage k+2's DMAs) is complete. The scale loads (NSL) go right
-  // after the first wait of a first half, before that stage's DMAs, so the
-  // next wait allows NL + NSL outstanding; they are complete at the wait
-  // after that, long before the second half writes them out.
-  for (int64_t kt = 0; kt < nk; kt += 2) {
-    const bool second = (kt & 2) != 0;                   // uniform
+  // after the first wait, before that stage's DMAs, so the next wait allows
+  // NL + NSL outstanding; they are complete at the wait after that, long
+  // before the third stage writes them out.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  auto block = [&](int64_t kt, auto masked) {
+    constexpr bool M = decltype(masked)::value;
     wait_vm_barrier<NL>();
-    if (!second) load_scales(kt / SB + 1);
-    else store_scales(kt / SB + 1);
-    stage(kt + DS - 1, kt + 1, f0, f1);
-    if (second) wait_vm_barrier<NL, true>();             // scale writes visible
-    else wait_vm_barrier<NL + NSL>();
-    stage(kt + DS, kt + 2, f1, f0);     // all zero past the end
-  }
+    load_scales(kt / SB + 1);
+    stage(kt + DS - 1, kt + 1, P0{}, masked);
+    if (M && kt + 1 >= nk) return;
+    wait_vm_barrier<NL + NSL>();
+    stage(kt + DS, kt + 2, P1{}, masked);
+    if (M && kt + 2 >= nk) return;
+    wait_vm_barrier<NL>();
+    store_scales(kt / SB + 1);
+    stage(kt + DS + 1, kt + 3, P0{}, masked);
+    if (M && kt + 3 >= nk) return;
+    wait_vm_barrier<NL, true>();                         // scale writes visible
+    stage(kt + DS + 2, kt + 4, P1{}, masked);
+  };
+  const int64_t nfull = L / DK;                          // stages that end at or before L
+  int64_t kt = 0;
+  for (; kt + SB <= nfull; kt += SB) block(kt, std::false_type{});
+  if (kt < nk) block(kt, std::true_type{});
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");      // ring drained, LDS free
 }
 };
@@ -720,15 +759,15 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
 // + lane%32 and col = wn*128 + j*32 + 8q + 4*(lane/32) + v. Each wavefront
 // stages 32-row blocks in LDS, then writes 16 bytes per lane along the rows.
 // Workgroup tile (64 TM) x (64 TN), read from the accumulator array's shape.
-template <typename OutT, int TM, int TN, typename Store>
+template <typename OutT, int WN, int TM, int TN, typename Store>
 __device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)[TM][TN],
                                                int64_t rows_left, Store store) {
-  constexpr int BM = 64 * TM, BN = 64 * TN;
+  constexpr int BM = 64 * TM;
   constexpr int ES = sizeof(OutT);
-  constexpr int WC = BN / 2;                           // columns of a wavefront
+  constexpr int WC = 32 * TN;                          // columns of a wavefront
   constexpr int RS = WC * ES + 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, half = lane >> 5, r32 = lane & 31;
+  const int wm = wave / WN, half = lane >> 5, r32 = lane & 31;
   uint8_t* ep = lsm + wave * (32 * RS);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -757,8 +796,8 @@ __device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)
   }
 }
 
-template <bool OUT_BF16, int BM, int BN>
-__global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict__ dy,
+template <bool OUT_BF16, int BM, int BN, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void k_dgrad_dma(const uint8_t* __restrict__ dy,
                                                       const uint8_t* __restrict__ dye,
                                                       const uint8_t* __restrict__ w,
                                                       const uint8_t* __restrict__ we,
@@ -794,7 +833,7 @@ __global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict_
   Operand A{dy, dye, N, 0, row0, row_end};
   const int64_t br0 = (int64_t)g * bl.row_step + k0;
   Operand B{w, we, bl.ld, (int64_t)g * bl.c0_step, br0, br0 + BN};
-  constexpr int TM = DmaTile<BM, BN>::TM, TN = DmaTile<BM, BN>::TN;
+  constexpr int TM = DmaTile<BM, BN, WN>::TM, TN = DmaTile<BM, BN, WN>::TN;
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -802,22 +841,23 @@ __global__ __launch_bounds__(256, 1) void k_dgrad_dma(const uint8_t* __restrict_
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  DmaLoop<TM, TN>::run(lsm, A, B, N, acc);
-  const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * (BN / 2);
+  DmaLoop<BM, BN, WN>::run(lsm, A, B, N, acc);
+  const int64_t col0 = k0 + ((threadIdx.x >> 6) % WN) * (BN / WN);
   if constexpr (OUT_BF16)
-    store_tile_lds<uint16_t>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
+    store_tile_lds<uint16_t, WN>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
       // non-temporal: the gradients are read back much later, not from this L2
       __builtin_nontemporal_store(
           v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dx) + (row0 + lr) * K + col0 + col));
     });
   else
-    store_tile_lds<float>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
+    store_tile_lds<float, WN>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
       __builtin_nontemporal_store(
           v, reinterpret_cast<u32x4*>(static_cast<float*>(dx) + (row0 + lr) * K + col0 + col));
     });
 }
 
-__global__ __launch_bounds__(256, 1) void k_wgrad_dma(const uint8_t* __restrict__ dyT,
+template <int WN>
+__global__ __launch_bounds__(128 * WN, 1) void k_wgrad_dma(const uint8_t* __restrict__ dyT,
                                                       const uint8_t* __restrict__ dyTe,
                                                       const uint8_t* __restrict__ xT,
                                                       const uint8_t* __restrict__ xTe,
@@ -831,9 +871,9 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_dma(const uint8_t* __restrict_
   int g = 0;
   if (G > 1) {
     int* seg = reinterpret_cast<int*>(lsm);
-    for (int h = threadIdx.x; h < G; h += 256) seg[h] = (int)(padded[h + 1] - padded[h]);
+    for (int h = threadIdx.x; h < G; h += blockDim.x) seg[h] = (int)(padded[h + 1] - padded[h]);
     __syncthreads();
-    for (int h = threadIdx.x; h < G; h += 256) {
+    for (int h = threadIdx.x; h < G; h += blockDim.x) {
       const int lh = seg[h];
       int rk = 0;
       for (int e = 0; e < G; ++e) {
@@ -851,12 +891,18 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_dma(const uint8_t* __restrict_
   const int64_t L = padded[g + 1] - c0;
   Operand A{dyT, dyTe, P, c0, n0, n0 + 256};
   Operand B{xT, xTe, P, c0, k0, k0 + 256};
-  f32x16 acc[4][4];
-  zero<4>(acc);
-  DmaLoop<4, 4>::run(lsm, A, B, L, acc);
+  constexpr int TM = DmaTile<256, 256, WN>::TM, TN = DmaTile<256, 256, WN>::TN;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  DmaLoop<256, 256, WN>::run(lsm, A, B, L, acc);
   float* out = dw + (int64_t)g * N * K;
-  const int64_t col0 = k0 + (threadIdx.x >> 6 & 1) * 128;
-  store_tile_lds<float>(lsm, acc, 256, [&](int lr, int col, const u32x4& v) {
+  const int64_t col0 = k0 + ((threadIdx.x >> 6) % WN) * (256 / WN);
+  store_tile_lds<float, WN>(lsm, acc, 256, [&](int lr, int col, const u32x4& v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (n0 + lr) * K + col0 + col));
   });
 }
@@ -892,12 +938,15 @@ hipError_t rowxrow_dma(const uint8_t* a, const uint8_t* ae, const uint8_t* b, co
                        const int64_t* offsets, int G, int64_t m_cap, int64_t L, int64_t ncols,
                        BLayout bl, void* out, bool out_bf16, hipStream_t stream) {
   static bool done[2] = {false, false};
-  auto k = out_bf16 ? k_dgrad_dma<true, BM, BN> : k_dgrad_dma<false, BM, BN>;
-  const size_t lds = (size_t)DmaTile<BM, BN>::LDS;
+  // 256 x 256 tiles run eight wavefronts (two per SIMD, 2 x 4 of 128 x 64 each),
+  // so one wavefront's MFMA chain covers the other's LDS reads and waits
+  constexpr int WN = (BM == 256 && BN == 256) ? kDmaWn256 : 2;
+  auto k = out_bf16 ? k_dgrad_dma<true, BM, BN, WN> : k_dgrad_dma<false, BM, BN, WN>;
+  const size_t lds = (size_t)DmaTile<BM, BN, WN>::LDS;
   hipError_t e = set_lds(k, lds, done[out_bf16]);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((m_cap + BM - 1) / BM + G) * (ncols / BN);   // bound on live tiles
-  k<<<(unsigned)tiles, 256, lds, stream>>>(a, ae, b, be, offsets, G, L, ncols, bl, out);
+  k<<<(unsigned)tiles, 128 * WN, lds, stream>>>(a, ae, b, be, offsets, G, L, ncols, bl, out);
   return hipGetLastError();
 }
 
@@ -960,11 +1009,13 @@ hipError_t launch_wgrad(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* 
   if (G == 0) return hipSuccess;
   if (N % 256 == 0 && K % 256 == 0) {
     static bool done = false;
-    const size_t lds = (size_t)DmaTile<256, 256>::LDS;
-    hipError_t e = set_lds(k_wgrad_dma, lds, done);
+    constexpr int WN = kDmaWn256;
+    const size_t lds = (size_t)DmaTile<256, 256, WN>::LDS;
+    hipError_t e = set_lds(k_wgrad_dma<WN>, lds, done);
     if (e != hipSuccess) return e;
     const int64_t tiles = (int64_t)G * (N / 256) * (K / 256);
-    k_wgrad_dma<<<(unsigned)tiles, 256, lds, stream>>>(dyT, dyTe, xT, xTe, padded, G, P, N, K, dw);
+    k_wgrad_dma<WN><<<(unsigned)tiles, 128 * WN, lds, stream>>>(dyT, dyTe, xT, xTe, padded, G, P, N,
+                                                                K, dw);
     return hipGetLastError();
   }
   return wgrad_t<128>(dyT, dyTe, xT, xTe, padded, G, P, N, K, dw, stream);
