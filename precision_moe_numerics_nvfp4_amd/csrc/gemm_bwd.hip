@@ -446,6 +446,11 @@ constexpr int SB = 4;                                 // stages per scale block 
 // wavefront columns of a 256 x 256 tile: 4 (eight wavefronts, two per SIMD) or 2
 constexpr int kDmaWn256 = NVFP4MOE_DMA_WN256;
 static_assert(kDmaWn256 == 2 || kDmaWn256 == 4, "2 or 4 wavefront columns");
+#ifndef NVFP4MOE_DMA_PERSIST
+#define NVFP4MOE_DMA_PERSIST 1
+#endif
+constexpr bool kDmaPersist = NVFP4MOE_DMA_PERSIST != 0;
+constexpr size_t kDmaMaxPreBytes = 16384;              // persistent tile-count scan (G < 4096)
 
 // Workgroup tile BM x BN (rows of A x rows of B), 2 x WN wavefronts of
 // (BM/2) x (BN/WN), that is TM x TN MFMA tiles of 32 x 32 each: WN = 2 puts
@@ -501,7 +506,12 @@ struct DmaLoop {
 static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const Operand& B,
                                            int64_t L, f32x16 (&acc)[C::TM][C::TN]) {
   constexpr int TM = C::TM, TN = C::TN, NL = C::NL, NSL = C::NSL, NW = C::NW, NT = C::NT;
-  const int tid = threadIdx.x, lane = tid & 63;
+  // the thread index through an empty asm: everything derived from it is
+  // computed here, per tile, rather than hoisted out of a persistent
+  // kernel's tile loop and held (spilled) across it
+  int tid_ = threadIdx.x;
+  asm volatile("" : "+v"(tid_));
+  const int tid = tid_, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, r32 = lane & 31;
@@ -766,7 +776,9 @@ __device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)
   constexpr int ES = sizeof(OutT);
   constexpr int WC = 32 * TN;                          // columns of a wavefront
   constexpr int RS = WC * ES + 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int tid_ = threadIdx.x;
+  asm volatile("" : "+v"(tid_));                       // per tile (see DmaLoop)
+  const int lane = tid_ & 63, wave = tid_ >> 6;
   const int wm = wave / WN, half = lane >> 5, r32 = lane & 31;
   uint8_t* ep = lsm + wave * (32 * RS);
 #pragma unroll
@@ -796,6 +808,10 @@ __device__ __forceinline__ void store_tile_lds(uint8_t* lsm, const f32x16 (&acc)
   }
 }
 
+// persist: the grid is at most one workgroup per compute unit, each looping
+// over tiles v = blockIdx.x, blockIdx.x + gridDim.x, ...; the tile-count scan
+// then sits in LDS after the ring. Otherwise one tile per workgroup (the
+// scan's LDS is reused by the ring).
 template <bool OUT_BF16, int BM, int BN, int WN>
 __global__ __launch_bounds__(128 * WN, 1) void k_dgrad_dma(const uint8_t* __restrict__ dy,
                                                       const uint8_t* __restrict__ dye,
@@ -803,57 +819,60 @@ __global__ __launch_bounds__(128 * WN, 1) void k_dgrad_dma(const uint8_t* __rest
                                                       const uint8_t* __restrict__ we,
                                                       const int64_t* __restrict__ offsets, int G,
                                                       int64_t L, int64_t ncols, BLayout bl,
-                                                      void* __restrict__ dx) {
+                                                      void* __restrict__ dx, int persist) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
   const int64_t N = L, K = ncols;                 // contraction, output columns
   const int ntn = (int)(K / BN);
-  int g, nt;
-  int64_t row0, row_end;
-  {
-    int* pre = reinterpret_cast<int*>(lsm);
-    tile_prefix(G, [&](int e) { return (int)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * ntn; }, pre);
-    const int total = pre[G];
-    if ((int)blockIdx.x >= total) return;
-    const int t = (int)xcd_tile(blockIdx.x, total);
-    g = tile_group(pre, G, t);
-    const int loc = t - pre[g];
-    const int64_t a = offsets[g];
-    row_end = offsets[g + 1];
-    const int mt = (int)((row_end - a + BM - 1) / BM);
-    // Within a group, tiles go in blocks of 4 n-tiles, m-tiles then n-tiles
-    // inside a block, so the ~32 consecutive tiles one XCD runs together
-    // share 8 A tiles and 4 B tiles in its L2.
-    int mi, ni;
-    block_order(loc, mt, ntn, mi, ni);
-    nt = ni;
-    row0 = a + (int64_t)mi * BM;
-    __syncthreads();
+  int* pre = reinterpret_cast<int*>(persist ? lsm + DmaTile<BM, BN, WN>::LDS : lsm);
+  tile_prefix(G, [&](int e) { return (int)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * ntn; }, pre);
+  const int total = pre[G];
+  for (int v = (int)blockIdx.x;; v += (int)gridDim.x) {
+    if (v >= total) return;
+    int g, nt;
+    int64_t row0, row_end;
+    {
+      const int t = (int)xcd_tile(v, total);
+      g = tile_group(pre, G, t);
+      const int loc = t - pre[g];
+      const int64_t a = offsets[g];
+      row_end = offsets[g + 1];
+      const int mt = (int)((row_end - a + BM - 1) / BM);
+      // Within a group, tiles go in blocks of 4 n-tiles, m-tiles then n-tiles
+      // inside a block, so the ~32 consecutive tiles one XCD runs together
+      // share 8 A tiles and 4 B tiles in its L2.
+      int mi, ni;
+      block_order(loc, mt, ntn, mi, ni);
+      nt = ni;
+      row0 = a + (int64_t)mi * BM;
+      __syncthreads();   // the scan's memory (one tile) or the last epilogue's staging is reused
+    }
+    const int64_t k0 = (int64_t)nt * BN;
+    Operand A{dy, dye, N, 0, row0, row_end};
+    const int64_t br0 = (int64_t)g * bl.row_step + k0;
+    Operand B{w, we, bl.ld, (int64_t)g * bl.c0_step, br0, br0 + BN};
+    constexpr int TM = DmaTile<BM, BN, WN>::TM, TN = DmaTile<BM, BN, WN>::TN;
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    DmaLoop<BM, BN, WN>::run(lsm, A, B, N, acc);
+    const int64_t col0 = k0 + ((threadIdx.x >> 6) % WN) * (BN / WN);
+    if constexpr (OUT_BF16)
+      store_tile_lds<uint16_t, WN>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
+        // non-temporal: the gradients are read back much later, not from this L2
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dx) + (row0 + lr) * K + col0 + col));
+      });
+    else
+      store_tile_lds<float, WN>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4*>(static_cast<float*>(dx) + (row0 + lr) * K + col0 + col));
+      });
+    if (!persist) return;
   }
-  const int64_t k0 = (int64_t)nt * BN;
-  Operand A{dy, dye, N, 0, row0, row_end};
-  const int64_t br0 = (int64_t)g * bl.row_step + k0;
-  Operand B{w, we, bl.ld, (int64_t)g * bl.c0_step, br0, br0 + BN};
-  constexpr int TM = DmaTile<BM, BN, WN>::TM, TN = DmaTile<BM, BN, WN>::TN;
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  DmaLoop<BM, BN, WN>::run(lsm, A, B, N, acc);
-  const int64_t col0 = k0 + ((threadIdx.x >> 6) % WN) * (BN / WN);
-  if constexpr (OUT_BF16)
-    store_tile_lds<uint16_t, WN>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
-      // non-temporal: the gradients are read back much later, not from this L2
-      __builtin_nontemporal_store(
-          v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dx) + (row0 + lr) * K + col0 + col));
-    });
-  else
-    store_tile_lds<float, WN>(lsm, acc, row_end - row0, [&](int lr, int col, const u32x4& v) {
-      __builtin_nontemporal_store(
-          v, reinterpret_cast<u32x4*>(static_cast<float*>(dx) + (row0 + lr) * K + col0 + col));
-    });
 }
 
 template <int WN>
@@ -941,12 +960,24 @@ hipError_t rowxrow_dma(const uint8_t* a, const uint8_t* ae, const uint8_t* b, co
   // 256 x 256 tiles run eight wavefronts (two per SIMD, 2 x 4 of 128 x 64 each),
   // so one wavefront's MFMA chain covers the other's LDS reads and waits
   constexpr int WN = (BM == 256 && BN == 256) ? kDmaWn256 : 2;
+  constexpr size_t ring = (size_t)DmaTile<BM, BN, WN>::LDS;
+  static_assert(ring + kDmaMaxPreBytes <= 160 * 1024, "LDS budget of k_dgrad_dma");
   auto k = out_bf16 ? k_dgrad_dma<true, BM, BN, WN> : k_dgrad_dma<false, BM, BN, WN>;
-  const size_t lds = (size_t)DmaTile<BM, BN, WN>::LDS;
-  hipError_t e = set_lds(k, lds, done[out_bf16]);
+  hipError_t e = set_lds(k, ring + kDmaMaxPreBytes, done[out_bf16]);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((m_cap + BM - 1) / BM + G) * (ncols / BN);   // bound on live tiles
-  k<<<(unsigned)tiles, 128 * WN, lds, stream>>>(a, ae, b, be, offsets, G, L, ncols, bl, out);
+  // Persistent (one workgroup per compute unit, looping over the tiles) when
+  // the bound is well above what the compute units take in one round:
+  // workgroups past the live tiles only start and exit, but the dispatcher
+  // issues them one after another (e.g. a capacity-sized call with 7x as
+  // many tile slots as tiles).
+  const int64_t cus = device_cu_count();
+  const size_t pre_bytes = ((size_t)(G + 1) * 4 + 15) & ~(size_t)15;
+  const bool persist = kDmaPersist && pre_bytes <= kDmaMaxPreBytes && tiles > 2 * cus;
+  const size_t lds = ring + (persist ? pre_bytes : 0);
+  const int64_t grid = persist ? cus : tiles;
+  k<<<(unsigned)grid, 128 * WN, lds, stream>>>(a, ae, b, be, offsets, G, L, ncols, bl, out,
+                                               persist ? 1 : 0);
   return hipGetLastError();
 }
 
