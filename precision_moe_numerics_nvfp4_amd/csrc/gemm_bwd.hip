@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad(const uint8_t* __restrict__ dy
 // loads with the LDS-destination bit), four 64-element stages in flight, so
 // the wavefronts hold no staging registers for them. A stage is BM (A) and
 // BN (B) rows x 64 bytes (16-byte pieces, piece c of row r at position
-// c ^ ((r >> 2) & 3), so the 16 rows of a read phase hit distinct banks).
+// c ^ chunk_key(r), so the rows of a read phase hit distinct banks).
 // Each stage is one 64-deep MFMA step; the fragments of stage kt+1 are read
 // from LDS while the MFMAs of stage kt run.
 //
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad(const uint8_t* __restrict__ dy
 // bytes (the row's scales for 4 stages start at whatever byte alignment the
 // group's contraction offset and the row pitch give; buffer loads address
 // whole dwords), shifts the 8 out with v_alignbyte and writes them to a
-// two-block LDS ring, [block % 2][row][8].
+// two-block LDS ring, [block % 2][row][12] (8 bytes used).
 // Loaded per stage, one byte per lane, they cost one cache line per lane and
 // byte: twice the line traffic of the codes themselves.
 //
@@ -471,7 +471,10 @@ struct DmaTile {
   static constexpr int NSL = (R + NT - 1) / NT;       // scale loads per thread and block
   static constexpr int A0 = 0, B0 = BM * DK;          // code planes [rows][64]
   static constexpr int STAGE = (BM + BN) * DK;
-  static constexpr int SBLK = (NSL * NT) * 8;         // one scale block, spare rows included
+  // a row's 8 scale bytes of a block at a 12-byte pitch (3 dwords: the 32
+  // consecutive rows of a byte read fall in 32 distinct banks)
+  static constexpr int SP = 12;
+  static constexpr int SBLK = (NSL * NT) * SP;        // one scale block, spare rows included
   static constexpr int SC = DS * STAGE;               // scale ring after the code stages
   static constexpr int LDS = SC + 2 * SBLK;
   static_assert(BM % 64 == 0 && BN % (32 * WN) == 0 && BM % (16 * NW) == 0 &&
@@ -543,7 +546,7 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
 #pragma unroll
     for (int i = 0; i < (o ? C::CB : C::CA); ++i) {
       const int row = 16 * (NW * i + wave) + (lane >> 2);
-      const int piece = (lane & 3) ^ ((row >> 2) & 3);
+      const int piece = (lane & 3) ^ chunk_key(row);
       const int rr = row < nrow[o] ? row : 0;
       oq[o][i] = (uint32_t)(rr * ld[o] + c0[o] + piece * 16);
     }
@@ -597,7 +600,9 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
     for (int u = 0; u < NSL; ++u) {
       const u32x2v w = {__builtin_amdgcn_alignbyte(sreg[u][1], sreg[u][0], esh[u]),
                         __builtin_amdgcn_alignbyte(sreg[u][2], sreg[u][1], esh[u])};
-      *reinterpret_cast<u32x2v*>(d + (tid + NT * u) * 8) = w;
+      uint32_t* q = reinterpret_cast<uint32_t*>(d + (tid + NT * u) * C::SP);
+      q[0] = w[0];
+      q[1] = w[1];
     }
   };
 
@@ -608,10 +613,10 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
   const int ra0 = wm * (BM / 2) + r32, rb0 = wn * (BN / WN) + r32;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    fa[c] = C::A0 + ra0 * DK + (((2 * c + half) ^ ((ra0 >> 2) & 3)) << 4);
-    fb[c] = C::B0 + rb0 * DK + (((2 * c + half) ^ ((rb0 >> 2) & 3)) << 4);
+    fa[c] = C::A0 + ra0 * DK + (((2 * c + half) ^ chunk_key(ra0)) << 4);
+    fb[c] = C::B0 + rb0 * DK + (((2 * c + half) ^ chunk_key(rb0)) << 4);
   }
-  const int sa = C::SC + ra0 * 8 + half, sbo = C::SC + (BM + rb0) * 8 + half;
+  const int sa = C::SC + ra0 * C::SP + half, sbo = C::SC + (BM + rb0) * C::SP + half;
   // Fragments: A single-buffered (fragment i of the next stage is read into
   // the registers of this stage's fragment i right after its last MFMA), B
   // double-buffered (every MFMA of a stage row uses all of B). The scale
@@ -680,12 +685,12 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       fa_[i] = frag(pa0, pa1, i * 32 * DK);
-      fas[i] = psa[i * 32 * 8];
+      fas[i] = psa[i * 32 * C::SP];
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       fb_[0][j] = frag(pb0, pb1, j * 32 * DK);
-      fbs[0][j] = psb[j * 32 * 8];
+      fbs[0][j] = psb[j * 32 * C::SP];
     }
   }
   // One stage: the MFMAs of stage kt_read - 1 (B buffer PB) in TM rows of TN;
@@ -711,14 +716,14 @@ static __device__ __forceinline__ void run(uint8_t* lsm, const Operand& A, const
 #pragma unroll
       for (int d = i * PD; d < (i + 1) * PD && d < NL; ++d) issue_one(kt_issue, d);
       fa_[i] = frag(pa0, pa1, i * 32 * DK);
-      fas[i] = psa[i * 32 * 8];
+      fas[i] = psa[i * 32 * C::SP];
       // B fragments of the next stage over the first rows (the first MFMAs of
       // the next stage need all of them)
       static_assert(TN <= TM, "one B fragment per row");
       if (i < TN) {
         const int j = i;
         fb_[QB][j] = frag(pb0, pb1, j * 32 * DK);
-        fbs[QB][j] = psb[j * 32 * 8];
+        fbs[QB][j] = psb[j * 32 * C::SP];
       }
       __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);                // the row's MFMAs
       __builtin_amdgcn_sched_group_barrier(0x020, PD, 0);                // its DMA issues

@@ -327,8 +327,8 @@ __global__ __launch_bounds__(256, 1) void k_fwd(
 // scales of blocks 4h..4h+3 (one 32-bit read).
 //
 // LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits at
-// position c ^ ((r >> 2) & 3), so the 16 lanes of a read phase (16 rows, one
-// chunk) hit 16 distinct 16-byte bank groups. A DMA load writes 16 bytes per
+// position c ^ chunk_key(r), so the lanes of a read phase (consecutive rows,
+// one chunk) hit distinct 16-byte bank groups. A DMA load writes 16 bytes per
 // lane at consecutive positions, so each lane fetches the global chunk that
 // belongs at its position.
 constexpr int LBK = 128;                  // K elements per stage
@@ -338,11 +338,22 @@ constexpr int LT = 256;                   // tile rows (A) and columns (B)
 constexpr int kStageBytes = 2 * LT * LCB;           // one stage's codes, A then B
 constexpr int SBK = 4;                                // stages per scale block
 constexpr int kScaleRow = SBK * LSB;                  // scale bytes of a row per block
-constexpr int kScaleSlot = 2 * LT * kScaleRow;        // one block, A rows then B rows
+// LDS pitch of a row's scale bytes: 36 = 9 dwords, so the 32 consecutive rows
+// a 32-bit read covers (one per lane) fall in 32 distinct banks
+constexpr int kScalePitch = kScaleRow + 4;
+constexpr int kScaleSlot = 2 * LT * kScalePitch;      // one block, A rows then B rows
 constexpr int kScaleRing = 2 * kScaleSlot;            // two blocks
 template <int NS>
 constexpr int kMainLds = NS * kStageBytes + kScaleRing;
 constexpr int kBufWord3 = 0x00020000;     // raw buffer, 32-bit data format
+
+// N dwords to LDS at a 4-byte-aligned address (the scale rows' pitch is not
+// a multiple of 8)
+template <int N, typename V>
+__device__ __forceinline__ void st_dwords(uint8_t* p, const V& v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) reinterpret_cast<uint32_t*>(p)[i] = v[i];
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -442,7 +453,12 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   }
   const int64_t n0 = (int64_t)nt * LT;
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  // the thread index through an empty asm: per-lane values derived from it
+  // are computed per tile rather than hoisted out of the persistent tile
+  // loop and held (spilled) across it
+  int tid_ = threadIdx.x;
+  asm volatile("" : "+v"(tid_));
+  const int tid = tid_, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // uniform per wavefront
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, r32 = lane & 31;
@@ -471,7 +487,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (4 * i + wave) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int c = (lane & 3) ^ chunk_key(r);
     const int ra = r < arows ? r : 0;
     oac[i] = (uint32_t)(ra * KB + c * 16);
     obc[i] = (uint32_t)(r * KB + c * 16);
@@ -529,11 +545,13 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     spiece = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q < 2 ? ras : rbs,
                                                                              off, 0, 0));
   };
+  // thread tid moves 16-byte piece tid % 2 of row q * 128 + tid / 2
+  const int piece_dst = (tid >> 1) * kScalePitch + (tid & 1) * 16;
   auto store_piece = [&](int64_t kt) {
     const int q = (int)(kt % SBK);
     const int64_t blk = kt / SBK + 1;
-    *reinterpret_cast<u32x4*>(lsm + NS * kStageBytes + (blk & 1) * kScaleSlot + q * 4096 +
-                              tid * 16) = spiece;
+    st_dwords<4>(lsm + NS * kStageBytes + (blk & 1) * kScaleSlot + q * 128 * kScalePitch +
+                 piece_dst, spiece);
   };
 
   f32x16 acc[TM][TN];
@@ -555,15 +573,15 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   for (int i = 0; i < TM; ++i) {
     const int r = (2 * i + wm) * 32 + r32;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) fa[i][c] = r * LCB + (((2 * half + c) ^ ((r >> 2) & 3)) << 4);
-    sa_off[i] = NS * kStageBytes + r * kScaleRow + half * 4;
+    for (int c = 0; c < 2; ++c) fa[i][c] = r * LCB + (((2 * half + c) ^ chunk_key(r)) << 4);
+    sa_off[i] = NS * kStageBytes + r * kScalePitch + half * 4;
   }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int r = wn * 128 + j * 32 + r32;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) fb[j][c] = LT * LCB + r * LCB + (((2 * half + c) ^ ((r >> 2) & 3)) << 4);
-    sb_off[j] = NS * kStageBytes + (LT + r) * kScaleRow + half * 4;
+    for (int c = 0; c < 2; ++c) fb[j][c] = LT * LCB + r * LCB + (((2 * half + c) ^ chunk_key(r)) << 4);
+    sb_off[j] = NS * kStageBytes + (LT + r) * kScalePitch + half * 4;
   }
 
   // The wavefront's rows of A: TA of its TM 32-row blocks hold valid rows
@@ -689,7 +707,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
     for (int p = 0; p < NS; ++p) issue(p, nk, 2);
 #pragma unroll
     for (int q = 0; q < SBK; ++q)
-      *reinterpret_cast<u32x4*>(lsm + NS * kStageBytes + q * 4096 + tid * 16) = p0[q];
+      st_dwords<4>(lsm + NS * kStageBytes + q * 128 * kScalePitch + piece_dst, p0[q]);
   }
   asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 landed
   read_chunk(lsm, 0, c0a, c0b);
@@ -851,7 +869,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
       __syncthreads();   // the scan's memory (one tile) or the last epilogue's staging is reused
     }
     const int64_t n0 = (int64_t)nt * LT;
-    const int tid = threadIdx.x, lane = tid & 63;
+    int tid_ = threadIdx.x;
+    asm volatile("" : "+v"(tid_));                     // per tile (see k_fwd_lds4)
+    const int tid = tid_, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int half = lane >> 5, r32 = lane & 31;
@@ -874,7 +894,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = (wave + 8 * i) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int c = (lane & 3) ^ chunk_key(r);
       const int ra = r < arows ? r : 0;
       oac[i] = (uint32_t)(ra * KB + c * 16);
       obc[i] = (uint32_t)(r * KB + c * 16);
@@ -913,11 +933,13 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
       spiece = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(q < 2 ? ras : rbs,
                                                                              off, 0, 0));
     };
+    // thread tid moves 8-byte piece tid % 4 of row q * 128 + tid / 4
+    const int piece_dst = (tid >> 2) * kScalePitch + (tid & 3) * 8;
     auto store_piece = [&](int64_t kt) {
       const int q = (int)(kt % SBK);
       const int64_t blk = kt / SBK + 1;
-      *reinterpret_cast<u32x2*>(lsm + NS * kStageBytes + (blk & 1) * kScaleSlot + q * 4096 +
-                                tid * 8) = spiece;
+      st_dwords<2>(lsm + NS * kStageBytes + (blk & 1) * kScaleSlot + q * 128 * kScalePitch +
+                   piece_dst, spiece);
     };
 
     f32x16 acc[TM][TN];
@@ -934,15 +956,15 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
     for (int i = 0; i < TM; ++i) {
       const int r = (2 * i + wm) * 32 + r32;
       fa[i] = r * LCB;
-      swa[i] = (r >> 2) & 3;
-      sa_off[i] = NS * kStageBytes + r * kScaleRow + half * 4;
+      swa[i] = chunk_key(r);
+      sa_off[i] = NS * kStageBytes + r * kScalePitch + half * 4;
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = wn * 64 + j * 32 + r32;
       fb[j] = LT * LCB + r * LCB;
-      swb[j] = (r >> 2) & 3;
-      sb_off[j] = NS * kStageBytes + (LT + r) * kScaleRow + half * 4;
+      swb[j] = chunk_key(r);
+      sb_off[j] = NS * kStageBytes + (LT + r) * kScalePitch + half * 4;
     }
 
     auto mainloop = [&](auto ta_c) {
@@ -1035,7 +1057,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
         for (int p = 0; p < NS; ++p) issue(p);
 #pragma unroll
         for (int q = 0; q < SBK; ++q)
-          *reinterpret_cast<u32x2*>(lsm + NS * kStageBytes + q * 4096 + tid * 8) = p0[q];
+          st_dwords<2>(lsm + NS * kStageBytes + q * 128 * kScalePitch + piece_dst, p0[q]);
       }
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage 0 landed
       for (int64_t kt = 0; kt < nk; ++kt) {

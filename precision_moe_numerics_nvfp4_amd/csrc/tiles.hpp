@@ -103,6 +103,14 @@ __device__ inline void tile_prefix(int G, Cnt cnt, int* pre) {
   __syncthreads();
 }
 
+// LDS rows of 64 bytes (four 16-byte chunks): chunk c of row r sits at
+// position c ^ chunk_key(r). For one chunk index, any 8 consecutive rows from
+// a multiple of 8 (the 8 lanes of one 128-byte LDS cycle of a 16-byte read)
+// and any 16 from a multiple of 16 (16 lanes over 256 bytes) land in distinct
+// 16-byte bank groups. The key uses row bits 1-3 only, so rows 32 apart
+// share it.
+__device__ __forceinline__ int chunk_key(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
 // Largest g with pre[g] <= t (t < pre[G]); groups with no tiles are skipped.
 __device__ inline int tile_group(const int* pre, int G, int t) {
   int lo = 0, hi = G;            // pre[lo] <= t < pre[hi]
