@@ -928,8 +928,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
     auto load_piece = [&](int64_t kt) {      // the piece stage kt writes
       const int q = (int)(kt % SBK);
       const int64_t blk = kt / SBK + 1;
-      const uint32_t off = (q == 0 ? osc[0] : q == 1 ? osc[1] : q == 2 ? osc[2] : osc[3]) +
-                           (uint32_t)(blk * kScaleRow);
+      // (a branch-free select: a branch here would split the step's schedule)
+      const uint32_t off = osc[0] * (q == 0) + osc[1] * (q == 1) + osc[2] * (q == 2) +
+                           osc[3] * (q == 3) + (uint32_t)(blk * kScaleRow);
       spiece = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(q < 2 ? ras : rbs,
                                                                              off, 0, 0));
     };
@@ -970,17 +971,26 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
     auto mainloop = [&](auto ta_c) {
       constexpr int TA = decltype(ta_c)::value;
       constexpr int TAA = TA > 0 ? TA : 1;
-      u32x4 ca[TAA], cb[TN];
+      // Codes in quarters: quarter q (8 bytes of the lane's 32 per fragment
+      // row) feeds steps 2q and 2q+1; QA holds quarters 0 and 2, QB 1 and 3.
+      // The f16 fragments are double-buffered: step s runs its MFMAs on
+      // buffer s % 2 while converting step s+1's into the other (step 7
+      // converts the next stage's step 0), so the conversions co-issue with
+      // the wavefront's own MFMAs.
+      typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+      u32x2v qa_a[TAA], qa_b[TN], qb_a[TAA], qb_b[TN];
       uint32_t sca[TAA], scb[TN];
       f16x2 sfa[TAA][2], sfb[TN][2];
-      auto read_chunk = [&](const uint8_t* st, int c) {
+      f16x8 fa_[2][TAA], fb_[2][TN];
+      auto read_quarter = [&](const uint8_t* st, int q, u32x2v (&ra)[TAA], u32x2v (&rb)[TN]) {
         if constexpr (TA == 0) return;
+        const int c = q >> 1, o = (q & 1) * 8;
 #pragma unroll
         for (int i = 0; i < TA; ++i)
-          ca[i] = *reinterpret_cast<const u32x4*>(st + fa[i] + (((2 * half + c) ^ swa[i]) << 4));
+          ra[i] = *reinterpret_cast<const u32x2v*>(st + fa[i] + (((2 * half + c) ^ swa[i]) << 4) + o);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          cb[j] = *reinterpret_cast<const u32x4*>(st + fb[j] + (((2 * half + c) ^ swb[j]) << 4));
+          rb[j] = *reinterpret_cast<const u32x2v*>(st + fb[j] + (((2 * half + c) ^ swb[j]) << 4) + o);
       };
       auto read_scales = [&](int64_t kt) {
         if constexpr (TA == 0) return;
@@ -1012,40 +1022,62 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
         const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s2;
         return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       };
-      // step s (0..7): word s % 4 of the chunk in registers, block s / 2 of
-      // the lane's four (scale pair s / 4, element (s / 2) % 2)
-      auto step = [&](int s, auto&& extra, auto nv_c) {
-        constexpr int NV = decltype(nv_c)::value;
+      // the f16 fragments of step s (0..7) into buffer s % 2: dword s % 2 of
+      // quarter s / 2, block s / 2 of the lane's four (scale pair s / 4,
+      // element (s / 2) % 2)
+      auto convert = [&](auto s_c) {
+        constexpr int s = decltype(s_c)::value, B = s & 1, q = s >> 1;
+        if constexpr (TA == 0) return;
+#pragma unroll
+        for (int i = 0; i < TA; ++i)
+          fa_[B][i] = deq((q & 1) ? qb_a[i][s & 1] : qa_a[i][s & 1], sfa[i][(s >> 2) & 1],
+                          (s >> 1) & 1);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          fb_[B][j] = deq((q & 1) ? qb_b[j][s & 1] : qa_b[j][s & 1], sfb[j][(s >> 2) & 1],
+                          (s >> 1) & 1);
+      };
+      // step s: the conversions of step s+1 (program order: before `extra`,
+      // which may replace their sources), then the MFMAs of step s,
+      // interleaved with them
+      auto step = [&](auto s_c, auto&& extra) {
+        constexpr int s = decltype(s_c)::value, B = s & 1;
         if constexpr (TA == 0) {
           extra();
           return;
         }
         __builtin_amdgcn_sched_barrier(0);
-        f16x8 fa_[TAA], fb_[TN];
-#pragma unroll
-        for (int i = 0; i < TA; ++i) fa_[i] = deq(ca[i][s & 3], sfa[i][(s >> 2) & 1], (s >> 1) & 1);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb_[j] = deq(cb[j][s & 3], sfb[j][(s >> 2) & 1], (s >> 1) & 1);
+        convert(std::integral_constant<int, (s + 1) & 7>{});
         extra();
 #pragma unroll
         for (int i = 0; i < TA; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
-        if constexpr (NV > 0) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb_[B][j], fa_[B][i], acc[i][j],
+                                                              0, 0, 0);
+        constexpr int NM = TAA * TN, NVALU = (TAA + TN) * 8, PV = (NVALU + NM - 1) / NM;
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);                 // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);                  // global loads
 #pragma unroll
-          for (int m = 0; m < TA * TN; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          }
+        for (int m = 0; m < NM; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, PV, 0);               // conversions
         }
         __builtin_amdgcn_sched_barrier(0);
       };
       auto none = [] {};
-      using Z = std::integral_constant<int, 0>;
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
+      using S3 = std::integral_constant<int, 3>;
+      using S4 = std::integral_constant<int, 4>;
+      using S5 = std::integral_constant<int, 5>;
+      using S6 = std::integral_constant<int, 6>;
+      using S7 = std::integral_constant<int, 7>;
       static_assert(NS == 3 && SBK == 4, "wait counts assume 3 stages, 4 loads per stage");
       // prologue: scale block 0 (four pieces), the piece stage 0 writes, then
-      // the code stages 0..2 (4 loads each)
+      // the code stages 0..2 (4 loads each); once stage 0 has landed, its
+      // quarter 0 and scales, and step 0's fragments
       {
         u32x2 p0[SBK];
 #pragma unroll
@@ -1060,25 +1092,27 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
           st_dwords<2>(lsm + NS * kStageBytes + q * 128 * kScalePitch + piece_dst, p0[q]);
       }
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage 0 landed
+      read_quarter(lsm, 0, qa_a, qa_b);
+      read_scales(0);
+      cvt_scales();
+      convert(S0{});
       for (int64_t kt = 0; kt < nk; ++kt) {
         const uint8_t* st = lsm + (kt % NS) * kStageBytes;
-        read_chunk(st, 0);
-        read_scales(kt);
-        store_piece(kt);
-        cvt_scales();
-        step(0, none, Z{});
-        step(1, none, Z{});
-        step(2, none, Z{});
-        step(3, none, Z{});
-        read_chunk(st, 1);
-        // every wavefront is done with stage kt; stage kt+1 has landed once
-        // only stage kt+2's four code loads are pending (the scale piece was
-        // issued before them); this stage's piece write is visible
+        const uint8_t* sn = lsm + ((kt + 1) % NS) * kStageBytes;
+        step(S0{}, [&] { store_piece(kt); read_quarter(st, 1, qb_a, qb_b); });
+        step(S1{}, [&] { read_quarter(st, 2, qa_a, qa_b); });
+        step(S2{}, none);
+        step(S3{}, [&] { read_quarter(st, 3, qb_a, qb_b); });
+        // every wavefront is done with stage kt (quarter 3 was its last
+        // read); stage kt+1 has landed once only stage kt+2's four code
+        // loads are pending (the scale piece was issued before them); this
+        // stage's piece write is visible
         asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        step(4, [&] { load_piece(kt + 1); issue(kt + NS); }, std::integral_constant<int, 5>{});
-        step(5, none, Z{});
-        step(6, none, Z{});
-        step(7, none, Z{});
+        step(S4{}, [&] { load_piece(kt + 1); issue(kt + NS); });
+        // quarter 0 and scales of stage kt+1 (past the end: unused bytes)
+        step(S5{}, [&] { read_quarter(sn, 0, qa_a, qa_b); read_scales(kt + 1); });
+        step(S6{}, [&] { cvt_scales(); });
+        step(S7{}, none);
       }
     };
     {
