@@ -253,8 +253,8 @@ def expert_share_forward(args, torch):
     avg = 0.5 * (t1 + t2)
     ach = fl / (avg * 1e-3)
     traffic = measured_traffic("moe_fwd_grouped_gemm_expert_share")
-    roof = {"kernel": "k_fwd_lds4 (256x256 tiles) + k_fwd_stream (short tails), one "
-                      "moe_fwd_grouped_gemm call; both GEMMs of the step",
+    roof = {"kernel": "k_fwd_w8 (256x256 tiles, eight wavefronts, persistent) + k_fwd_stream "
+                      "(short tails), one moe_fwd_grouped_gemm call; both GEMMs of the step",
             "bound": "mfma", "achieved": round(ach / 1e12, 2), "peak": PEAK["f16"] / 1e12,
             "unit": "TFLOP/s", "frac": round(ach / PEAK["f16"], 4), "traffic": traffic,
             "algorithmic_flop_per_launch": fl, "launch_ms_avg": round(avg, 4),
