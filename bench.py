@@ -683,7 +683,7 @@ def hbm_copy_ceiling(torch, flush):
     dst = torch.empty_like(src)
     t = cold_time(torch, lambda: dst.copy_(src), 5, flush)
     acc = torch.empty((), dtype=torch.float32, device="cuda")
-    tr = cold_time(torch, lambda: torch.sum(src, out=acc), 5, flush)
+    tr = cold_time(torch, lambda: torch.sum(src, dim=0, out=acc), 5, flush)
     del src, dst
     return {"copy": {"bytes_moved": 2 << 30, "ms": round(t, 4), "GB/s": round((2 << 30) / t / 1e6, 1),
                      "frac_of_8TB/s": round((2 << 30) / t / 1e-3 / PEAK["hbm"], 4)},
