@@ -79,6 +79,7 @@ def dev_tensor(a, torch):
 STAGE_SOURCE = {
     "moe_fwd_grouped_gemm": "gemm_fwd.hip", "moe_fwd_grouped_gemm_expert_share": "gemm_fwd.hip",
     "moe_bwd_dgrad": "gemm_bwd.hip", "moe_bwd_wgrad": "gemm_bwd.hip",
+    "moe_bwd_dgrad_expert_share": "gemm_bwd.hip", "moe_bwd_wgrad_expert_share": "gemm_bwd.hip",
     "nvfp4_quantize_x": "quant.hip", "nvfp4_quantize_w": "quant.hip",
     "mxfp8_requant_sr_x": "requant.hip", "mxfp8_requant_sr_w": "requant.hip",
     "mxfp8_quantize_dy": "requant.hip", "moe_permute": "permute.hip",
@@ -378,7 +379,7 @@ def small_moe_step(args, torch, flush):
     kernels = {}
     for name, (kind, amount) in work.items():
         kernels[name] = {"warm": rate(kind, amount, warm[name]), "cold": rate(kind, amount, cold[name])}
-        if name in ("moe_fwd_grouped_gemm", "moe_bwd_dgrad"):
+        if name in ("moe_fwd_grouped_gemm", "moe_bwd_dgrad", "moe_bwd_wgrad"):
             kernels[name]["traffic_bytes_per_launch"] = measured_traffic(name)
     # wgrad is rated against the larger of its two bounds
     t_flop = gemm_flop / PEAK["fp8"]
@@ -510,10 +511,35 @@ def ffn_step_bench(torch, reps, x, w1, w2, topk, gate, dout, E, F, e0):
     t_fwd = _time(torch, lambda: L.forward(x, topk, gate), reps)
     t_bwd = _time(torch, lambda: L.backward(dout, gate), reps)
     fl = 6 * 2.0 * M * F * K
+    # the four MXFP8 backward GEMMs one by one (inputs as the step left them);
+    # wgrad rated against the larger of its flop and byte bounds (the float32
+    # dW it writes: E F K 4 bytes)
+    from precision_moe_numerics_nvfp4_amd import binding as B
+    off, poff, P = L.perm["offsets"], L.perm["padded_offsets"], L.P
+    gemms = {
+        "dgrad_down_4096": lambda: B.moe_bwd_dgrad(*L.dy2_8, *L.w2T, off, K, F, dx=L.dh),
+        "wgrad_down": lambda: B.moe_bwd_wgrad(*L.dy2T, *L.hT, poff, K, F, dw=L.dw2),
+        "dgrad_up_1536": lambda: B.moe_bwd_dgrad(*L.dh8, *L.w1T, off, F, K, dx=L.dxp),
+        "wgrad_up": lambda: B.moe_bwd_wgrad(*L.dhT, *L.xT, poff, F, K, dw=L.dw1),
+    }
+    g_fl = 2.0 * M * F * K
+    w_bytes = (K + F) * P * B_MXFP8 + 4.0 * E * F * K
+    per = {}
+    for name, fn in gemms.items():
+        ms = graph_time(torch, fn, reps)
+        r = rate("fp8", g_fl, ms)
+        if name.startswith("wgrad"):
+            t_bound = max(g_fl / PEAK["fp8"], w_bytes / PEAK["hbm"])
+            r.update({"bound": "hbm" if w_bytes / PEAK["hbm"] > g_fl / PEAK["fp8"] else "fp8",
+                      "algorithmic_bytes": w_bytes, "bound_us": round(t_bound * 1e6, 1),
+                      "frac_of_bound": round(t_bound / (ms * 1e-3), 4)})
+        per[name] = r
+    stage = "moe_bwd_dgrad_expert_share", "moe_bwd_wgrad_expert_share"
+    per["traffic_bytes_per_launch"] = {s_: measured_traffic(s_) for s_ in stage}
     del L
     return {"routed_rows": M, "ms_per_step": round(t_step, 4), "ms_forward": round(t_fwd, 4),
             "ms_backward": round(t_bwd, 4), "gemm_TFLOP": round(fl / 1e12, 3),
-            "TFLOP/s": round(fl / t_step / 1e9, 1),
+            "TFLOP/s": round(fl / t_step / 1e9, 1), "backward_gemms": per,
             "note": "step = weight quantize + forward + backward; six grouped GEMMs"}
 
 
