@@ -515,7 +515,8 @@ def ffn_step_bench(torch, reps, x, w1, w2, topk, gate, dout, E, F, e0):
     # wgrad rated against the larger of its flop and byte bounds (the float32
     # dW it writes: E F K 4 bytes)
     from precision_moe_numerics_nvfp4_amd import binding as B
-    off, poff, P = L.perm["offsets"], L.perm["padded_offsets"], L.P
+    off, poff = L.perm["offsets"], L.perm["padded_offsets"]
+    P = int(poff[-1].item())             # the padded token count (the buffers hold capacity)
     gemms = {
         "dgrad_down_4096": lambda: B.moe_bwd_dgrad(*L.dy2_8, *L.w2T, off, K, F, dx=L.dh),
         "wgrad_down": lambda: B.moe_bwd_wgrad(*L.dy2T, *L.hT, poff, K, F, dw=L.dw2),
@@ -534,8 +535,9 @@ def ffn_step_bench(torch, reps, x, w1, w2, topk, gate, dout, E, F, e0):
                       "algorithmic_bytes": w_bytes, "bound_us": round(t_bound * 1e6, 1),
                       "frac_of_bound": round(t_bound / (ms * 1e-3), 4)})
         per[name] = r
-    stage = "moe_bwd_dgrad_expert_share", "moe_bwd_wgrad_expert_share"
-    per["traffic_bytes_per_launch"] = {s_: measured_traffic(s_) for s_ in stage}
+    if (E, F, K) == (48, 1536, 4096):     # the expert share: its counter records
+        stage = "moe_bwd_dgrad_expert_share", "moe_bwd_wgrad_expert_share"
+        per["traffic_bytes_per_launch"] = {s_: measured_traffic(s_) for s_ in stage}
     del L
     return {"routed_rows": M, "ms_per_step": round(t_step, 4), "ms_forward": round(t_fwd, 4),
             "ms_backward": round(t_bwd, 4), "gemm_TFLOP": round(fl / 1e12, 3),
