@@ -734,7 +734,7 @@ def clock_under_load(torch, fn, seconds=2.0):
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True,
                            text=True, timeout=20)
-        rec = r.stdout.strip()[:4000] if r.returncode == 0 else None
+        rec = r.stdout.strip() if r.returncode == 0 else None
     except Exception:
         rec = None
     torch.cuda.synchronize()
@@ -742,10 +742,15 @@ def clock_under_load(torch, fn, seconds=2.0):
         return None
     try:
         data = json.loads(rec)
+        if isinstance(data, dict) and "gpu_data" in data:
+            data = data["gpu_data"]
         d = data[0] if isinstance(data, list) else data
         clk = d.get("clock", d)
-        g = clk.get("gfx_0", clk.get("GFX_0", {}))
-        return {"gfx_0_clk": g.get("clk"), "source": "amd-smi metric -c during forward-GEMM replays"}
+        mhz = [v["clk"]["value"] for k, v in sorted(clk.items())
+               if k.lower().startswith("gfx_") and isinstance(v, dict)
+               and isinstance(v.get("clk"), dict) and isinstance(v["clk"].get("value"), (int, float))]
+        return {"gfx_clk_mhz": mhz, "mean_mhz": round(sum(mhz) / len(mhz), 1) if mhz else None,
+                "source": "amd-smi metric -c during forward-GEMM replays"}
     except Exception:
         return {"raw": rec[:400]}
 
