@@ -60,6 +60,22 @@ def assert_gemm_close(y, ref64, groups, absbound=None, tol=1e-3, what="gemm", el
             assert not viol.any(), f"{what}: {viol.sum()} elements exceed the summation error bound"
 
 
+def worst_elementwise(y, ref64, groups, floor=1e-2):
+    """Largest |y - ref| / |ref| over elements with |ref| >= floor * (the
+    group's max |ref|): the elementwise error a normwise contract allows."""
+    y = np.asarray(y, dtype=np.float64)
+    worst = 0.0
+    for (a, b) in groups:
+        if b <= a:
+            continue
+        r = ref64[a:b]
+        m = np.abs(r).max()
+        big = np.abs(r) >= floor * m
+        if big.any():
+            worst = max(worst, float((np.abs(y[a:b] - r)[big] / np.abs(r[big])).max()))
+    return worst
+
+
 def sr_mean_sd(v, e8):
     """Analytic standard deviation of mean(SR(v)) - mean(v) for float values
     v [R, C] re-quantized to E4M3 with E8M0 block exponents e8 [R, C/32]:

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle_chunks as OC
-from helpers import assert_gemm_close, ensure_built, from_dev, sr_mean_sd, to_dev
+from helpers import assert_gemm_close, ensure_built, from_dev, sr_mean_sd, to_dev, worst_elementwise
 from oracle import formats as F
 from oracle import gemm as GM
 from oracle import mxfp8 as MX
@@ -85,12 +85,18 @@ def _check_full_layer(L, w, dy, fwd_exact_rows=None):
     dx_ref = GM.dgrad_grouped(dq, de, wq8, we8, off, N)
     assert_gemm_close(h(L.dx)[:M], dx_ref.astype(np.float64), groups, what="dgrad",
                       elementwise=False)
+    # (reported, not asserted: the block-scaled MFMA's in-block alignment)
+    print(f"dgrad worst elementwise relative error (|ref| >= 1e-2 max): "
+          f"{worst_elementwise(h(L.dx)[:M], dx_ref.astype(np.float64), groups):.3e}")
     dw_ref = GM.wgrad_grouped(dtq[:, :pt], dte[:, :pt // 32], xq8[:, :pt], xe8[:, :pt // 32], pad)
     dw = h(L.dw)
     for g in range(E):
         if pad[g + 1] > pad[g]:
             assert_gemm_close(dw[g], dw_ref[g].astype(np.float64), [(0, N)], what=f"wgrad[{g}]",
                               elementwise=False)
+    print("wgrad worst elementwise relative error (|ref| >= 1e-2 max): %.3e" % max(
+        worst_elementwise(dw[g], dw_ref[g].astype(np.float64), [(0, N)])
+        for g in range(E) if pad[g + 1] > pad[g]))
     return dict(off=off, pad=pad, xq8=xq8, xe8=xe8, wq8=wq8, we8=we8, ac=ac, asc=asc, ao=ao,
                 wc=wc, ws=ws, wo=wo)
 
