@@ -12,20 +12,23 @@
 // exact products, float32 accumulation. The per-row and per-expert outer
 // scales are applied in the epilogue: y = (acc * s_x[row]) * s_w[g].
 //
-// Structure (large tiles, k_fwd_lds4). A workgroup of 4 wavefronts owns a
-// 256 x 256 tile (tokens x outputs) of one expert; each wavefront owns
-// 128 x 128 (4 x 4 MFMA tiles, 256 accumulator registers, one wavefront per
-// SIMD), its 32-row blocks alternating with the other wavefront row's (block
-// 2i + wm), so a partial tile's rows are spread over all four wavefronts.
-// The K loop moves 128 elements per stage: the stage's raw NVFP4 bytes (64
-// code bytes and 8 scale bytes per row of A and of B) go from global memory
-// straight into LDS by buffer loads with the LDS-destination bit, three
-// stages in flight, so LDS carries 4.5 bits per element and no registers
-// stage the loads. Each wavefront reads the raw codes of its own fragment
-// rows and converts them to f16 right before the MFMAs that use them
-// (v_cvt_scalef32_pk_f16_fp4 at unit scale, then an exact v_pk_mul_f16 by the
-// block's E4M3 scale), interleaved with the previous step's MFMAs so the
-// conversions co-execute with the matrix pipe. One barrier per stage.
+// Structure (large tiles). A workgroup owns a 256 x 256 tile (tokens x
+// outputs) of one expert. The K loop moves 128 elements per stage: the
+// stage's raw NVFP4 code bytes (64 per row of A and of B) go from global
+// memory straight into LDS by buffer loads with the LDS-destination bit,
+// three stages in flight, and the E4M3 block scales through a two-block LDS
+// ring, so LDS carries 4.5 bits per element and no registers stage the loads.
+// The wavefronts convert the raw codes of their own fragment rows to f16
+// (v_cvt_scalef32_pk_f16_fp4 at unit scale, then an exact v_pk_mul_f16 by
+// the block's E4M3 scale) a step ahead of the MFMAs that use them, so the
+// conversions co-issue with the matrix pipe. One barrier per stage.
+// k_fwd_w8 (the default) runs eight wavefronts, two per SIMD, of 128 x 64;
+// k_fwd_lds4 four, one per SIMD, of 128 x 128 (fewer conversions per MFMA,
+// no second wavefront to cover waits; it is also the NVFP4 weight-gradient
+// kernel). A wavefront's 32-row blocks alternate with the other wavefront
+// row's (block 2i + wm), so a partial tile's rows are spread over all SIMDs.
+// Both run persistent (one workgroup per compute unit looping over the
+// tiles) when the bound on live tiles is far above one round.
 //
 // Tile order. Every group's full 256-row tiles first, then the partial last
 // tiles of more than 128 rows, then those of at most 128; each part is split
