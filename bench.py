@@ -426,9 +426,12 @@ def sr_bias_statistic(torch, L, N, E):
         a, b = off[g], off[g + 1]
         vx[:, pad[g]:pad[g] + (b - a)] = X[a:b].t()
     parts.append((vx, sx, L.xT[1][:, :pt // 32]))
-    sw = (_e4m3_to_f32(torch, L.wT[0]) *
-          torch.pow(2.0, L.wT[1].to(torch.float32) - 127).repeat_interleave(32, 1))
-    parts.append((W.t().contiguous(), sw, L.wT[1]))
+    # weights: per-expert blocks [E, K, N] back to [K, E*N]
+    K = W.shape[1]
+    wq8, we8 = (t.reshape(E, K, -1).transpose(0, 1).reshape(K, -1) for t in L.wT)
+    sw = (_e4m3_to_f32(torch, wq8) *
+          torch.pow(2.0, we8.to(torch.float32) - 127).repeat_interleave(32, 1))
+    parts.append((W.t().contiguous(), sw, we8))
     n = 0
     diff = 0.0
     var = 0.0

@@ -39,6 +39,10 @@
  *     GEMM N % 128 == 0 and K % 128 == 0, the re-quantization cols % 128 == 0
  *     and P % 32 == 0, the MXFP8 GEMMs N and K multiples of 128 (each returns
  *     NVFP4MOE_EUNSUPPORTED otherwise);
+ *   - mxfp8_requant_sr writes a weight (per-expert outer scales) as one
+ *     [cols, length] block per expert, [E, K, N] for a weight [E*N, K], so
+ *     moe_bwd_dgrad reads each expert's transposed weight as one contiguous
+ *     block rather than a column slice of a [K, E*N] matrix;
  *   - entry points beyond the seven of the path: the all-MXFP8 forward, the
  *     routed FFN's combine and intermediate quantizer, the 16x16-tile and
  *     NVFP4-backward variants, the one-pass dual dY quantizer and
@@ -66,7 +70,7 @@
 extern "C" {
 #endif
 
-#define NVFP4MOE_ABI_VERSION 2
+#define NVFP4MOE_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define NVFP4MOE_API __attribute__((visibility("default")))
@@ -223,13 +227,21 @@ NVFP4MOE_API int moe_fwd_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_s
  *   [offsets[g], offsets[g+1]) become output columns starting at
  *   padded_offsets[g]; columns up to the next multiple of 32 are zero. For a
  *   weight [E*N, K] use offsets = padded_offsets = {0, N, 2N, ...} (N % 32 == 0).
- * out_e4m3 [cols, P], out_e8m0 [cols, P/32]; P is the row pitch (P % 32 == 0,
- *   P >= padded_offsets[G]); columns >= padded_offsets[G] are untouched.
+ * NVFP4MOE_OUTER_PER_ROW (activations): out_e4m3 [cols, P], out_e8m0
+ *   [cols, P/32]; P is the row pitch (P % 32 == 0, P >= padded_offsets[G]);
+ *   columns >= padded_offsets[G] are untouched.
+ * NVFP4MOE_OUTER_PER_GROUP (weights): one block per group, group g's
+ *   [cols, L_g] (L_g = padded_offsets[g+1] - padded_offsets[g]) at element
+ *   cols * padded_offsets[g], row pitch L_g, its E8M0 [cols, L_g/32] at
+ *   cols * padded_offsets[g] / 32: for a weight [E*N, K] the transposed
+ *   weights [E, K, N] that moe_bwd_dgrad reads. Padded offsets must then be
+ *   multiples of 32.
  * Block of 32 along the output row: e = smallest exponent with
  *   max|v| <= 448*2^e (clamped to [-127,127]); y = v*2^-e; element rounded to
  *   E4M3 stochastically with the 16-bit draw of Philox4x32-10 keyed by
  *   (seed lo, seed hi), counter (q lo, q hi, tag, 0), q = idx>>3, for the
- *   output's linear index idx = col*P + p (half idx&1 of word (idx&7)>>1).
+ *   logical index idx = col*P + p of output column col, padded position p
+ *   (half idx&1 of word (idx&7)>>1), in both layouts.
  * Requires cols % 128 == 0.
  */
 NVFP4MOE_API int mxfp8_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,
@@ -276,11 +288,12 @@ NVFP4MOE_API int mxfp8_quantize_dual(const void* x, int x_dtype, int64_t rows, i
  * Pages: "Inkling 2 Small uses four-bit training ..." (ai-primer), sections
  * "NVFP4 forward, MXFP8 backward" and "Stochastic rounding across transposes".
  *
- * dy: MXFP8 [m_cap, N] (blocks along N); w: MXFP8 [K, G*N] (requantized weight,
- * blocks along G*N); offsets[G+1] (device).
- * dx[r, k] = sum_n dy[r, n] * w[k, g*N + n] for rows r of group g, float32
+ * dy: MXFP8 [m_cap, N] (blocks along N); w: MXFP8 [G, K, N] (each expert's
+ * transposed weight contiguous, blocks along N, as mxfp8_requant_sr writes a
+ * weight with NVFP4MOE_OUTER_PER_GROUP); offsets[G+1] (device).
+ * dx[r, k] = sum_n dy[r, n] * w[g, k, n] for rows r of group g, float32
  * accumulation; dx [m_cap, K] float32 or bfloat16; rows >= offsets[G] untouched.
- * Requires N % 128 == 0, K % 128 == 0, G * N <= 16711935 (tile offsets are
+ * Requires N % 128 == 0, K % 128 == 0, N <= 16711935 (tile offsets are
  * 32-bit); otherwise NVFP4MOE_EUNSUPPORTED.
  */
 NVFP4MOE_API int moe_bwd_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0,

@@ -264,8 +264,11 @@ def moe_fwd_grouped_gemm(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer,
 
 def mxfp8_requant_sr(codes, scales, outer, offsets, padded_offsets, P, seed, tag,
                      rows_per_group=None, out=None, out_e8=None):
-    """Saved NVFP4 [rows, cols] -> MXFP8 [cols, P] (+ E8M0 [cols, P/32]) with
-    stochastic rounding, grouped transpose per offsets/padded_offsets."""
+    """Saved NVFP4 [rows, cols] -> MXFP8 with stochastic rounding, grouped
+    transpose per offsets/padded_offsets: activations (per-row outer scales)
+    [cols, P] (+ E8M0 [cols, P/32]); weights (rows_per_group) per-expert blocks
+    [G * cols, rows_per_group] (+ [G * cols, rows_per_group/32]), P = G *
+    rows_per_group."""
     torch = _torch()
     _dev(codes, "codes", torch.uint8, 2)
     _dev(scales, "scales", torch.uint8, 2)
@@ -275,10 +278,18 @@ def mxfp8_requant_sr(codes, scales, outer, offsets, padded_offsets, P, seed, tag
     rows, cols = codes.shape[0], codes.shape[1] * 2
     G = offsets.shape[0] - 1
     dev = codes.device
+    if rows_per_group is None:
+        shape = (cols, P)
+    else:
+        if P != G * rows_per_group:
+            raise ValueError("mxfp8_requant_sr: weights need P == G * rows_per_group")
+        shape = (G * cols, rows_per_group)
     if out is None:
-        out = torch.empty((cols, P), dtype=torch.uint8, device=dev)
+        out = torch.empty(shape, dtype=torch.uint8, device=dev)
     if out_e8 is None:
-        out_e8 = torch.empty((cols, P // 32), dtype=torch.uint8, device=dev)
+        out_e8 = torch.empty((shape[0], shape[1] // 32), dtype=torch.uint8, device=dev)
+    if out.numel() < shape[0] * shape[1] or out_e8.numel() < shape[0] * (shape[1] // 32):
+        raise ValueError("mxfp8_requant_sr: output buffers too small")
     mode = _OUTER_PER_ROW if rows_per_group is None else _OUTER_PER_GROUP
     st = lib().mxfp8_requant_sr(_ptr(codes), _ptr(scales), _ptr(outer), mode,
                                 0 if rows_per_group is None else int(rows_per_group), rows, cols,
@@ -323,7 +334,8 @@ def mxfp8_quantize(x, orientation="rowwise", offsets=None, padded_offsets=None, 
 
 
 def moe_bwd_dgrad(dy_e4m3, dy_e8m0, w_e4m3, w_e8m0, offsets, N, K, out_dtype=None, dx=None):
-    """dX [m_cap, K] from dY8 [m_cap, N] and W8 [K, G*N] (MXFP8)."""
+    """dX [m_cap, K] from dY8 [m_cap, N] and W8 [G*K, N] (MXFP8, each expert's
+    transposed weight [K, N] contiguous, as mxfp8_requant_sr writes it)."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
     for t, n in ((dy_e4m3, "dy_e4m3"), (dy_e8m0, "dy_e8m0"), (w_e4m3, "w_e4m3"),

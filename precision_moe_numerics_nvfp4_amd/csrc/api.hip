@@ -146,9 +146,11 @@ int mxfp8_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* o
   REQUIRE(cols % 128 == 0 && P % 32 == 0, NVFP4MOE_EUNSUPPORTED);
   REQUIRE(aligned16(codes) && aligned16(out_e4m3), NVFP4MOE_EUNSUPPORTED);
   REQUIRE((reinterpret_cast<uintptr_t>(scales) & 7u) == 0, NVFP4MOE_EUNSUPPORTED);
+  // weights (per-group outer scales): each group's block [cols, length]
+  // contiguous, the layout dgrad reads
   return hip_status(launch_requant_sr(codes, scales, outer, per_group ? rows_per_group : 0, rows,
-                                      cols, offsets, padded_offsets, G, P, seed, tag, out_e4m3,
-                                      out_e8m0, as_stream(stream)));
+                                      cols, offsets, padded_offsets, G, P, per_group, seed, tag,
+                                      out_e4m3, out_e8m0, as_stream(stream)));
 }
 
 int mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int orientation,
@@ -186,7 +188,7 @@ int moe_bwd_dgrad(const uint8_t* dy_e4m3, const uint8_t* dy_e8m0, const uint8_t*
   if (G == 0 || m_cap == 0 || K == 0) return NVFP4MOE_OK;
   REQUIRE(dy_e4m3 && dy_e8m0 && w_e4m3 && w_e8m0 && offsets && dx, NVFP4MOE_EINVAL);
   REQUIRE(N % 128 == 0 && K % 128 == 0 && N > 0, NVFP4MOE_EUNSUPPORTED);
-  REQUIRE((int64_t)G * N <= kMaxGemmRowBytes, NVFP4MOE_EUNSUPPORTED);
+  REQUIRE(N <= kMaxGemmRowBytes, NVFP4MOE_EUNSUPPORTED);
   REQUIRE(aligned16(dy_e4m3) && aligned16(w_e4m3) && aligned16(dx), NVFP4MOE_EUNSUPPORTED);
   return hip_status(launch_dgrad(dy_e4m3, dy_e8m0, w_e4m3, w_e8m0, offsets, G, m_cap, N, K, dx,
                                  dx_dtype == NVFP4MOE_BF16, as_stream(stream)));

@@ -18,7 +18,7 @@
 // Both GEMMs are "row x row" contractions: each operand is stored with the
 // contraction dimension contiguous (that is what the re-quantization's
 // transpose is for), so one main loop serves both:
-//   dgrad: dX[r, k]    = sum_n dY8[r, n] * W8[k, g*N + n]    (rows r of expert g)
+//   dgrad: dX[r, k]    = sum_n dY8[r, n] * W8[g, k, n]       (rows r of expert g)
 //   wgrad: dW[g, n, k] = sum_p dYT8[n, p] * XT8[k, p]        (p in g's padded segment)
 // The dgrad kernels take the second operand's layout as parameters (row
 // stride, and per group a contraction offset and a row offset), which also
@@ -1026,9 +1026,11 @@ hipError_t wgrad_t(const uint8_t* dyT, const uint8_t* dyTe, const uint8_t* xT, c
 hipError_t launch_dgrad(const uint8_t* dy, const uint8_t* dye, const uint8_t* w,
                         const uint8_t* we, const int64_t* offsets, int G, int64_t m_cap,
                         int64_t N, int64_t K, void* dx, bool dx_bf16, hipStream_t stream) {
-  // W8 [K, G*N]: group g's rows are all K, its contraction starts at g*N
-  return launch_rowxrow(dy, dye, w, we, offsets, G, m_cap, N, K, BLayout{(int64_t)G * N, N, 0},
-                        dx, dx_bf16, stream);
+  // W8 [G, K, N]: group g's K rows start at row g*K, row stride N, the
+  // contraction from 0 (each expert's block contiguous: a tile's 256 rows
+  // span 256 N bytes, not 256 G N)
+  return launch_rowxrow(dy, dye, w, we, offsets, G, m_cap, N, K, BLayout{N, 0, K}, dx, dx_bf16,
+                        stream);
 }
 
 hipError_t launch_fwd_mxfp8(const uint8_t* x, const uint8_t* xe, const uint8_t* w,

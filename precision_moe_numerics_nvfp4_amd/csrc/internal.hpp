@@ -50,8 +50,9 @@ hipError_t launch_permute(const int32_t* topk_ids, int64_t T, int k, int e0, int
 hipError_t launch_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,
                              int64_t rows_per_group /* 0 = per row */, int64_t rows,
                              int64_t cols, const int64_t* offsets,
-                             const int64_t* padded_offsets, int G, int64_t P, uint64_t seed,
-                             uint32_t tag, uint8_t* out_e4m3, uint8_t* out_e8m0,
+                             const int64_t* padded_offsets, int G, int64_t P,
+                             bool blocked /* group g's [cols, length] block at cols * padded[g] */,
+                             uint64_t seed, uint32_t tag, uint8_t* out_e4m3, uint8_t* out_e8m0,
                              hipStream_t stream);
 hipError_t launch_mxfp8_quantize_colwise(const void* x, bool bf16, int64_t rows, int64_t cols,
                                          const int64_t* offsets,

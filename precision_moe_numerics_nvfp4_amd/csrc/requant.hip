@@ -190,7 +190,8 @@ __device__ __forceinline__ int64_t xcd_band(int64_t w, int64_t live) {
 // row_out [rows, cols] and row_e8 [rows, cols/32] at the source row.
 // NVO: NVFP4 output instead (codes to out, E4M3 scales to out_e8, group maxima
 // as float bits in gbits); BLK: each group's part written as its own
-// [cols, group length] block.
+// [cols, group length] block (MXFP8: starting at element cols * padded[g];
+// NVFP4, groups of equal length: at element g * cols * length).
 template <Src S, bool SR, bool ROWS = false, bool NVO = false, bool BLK = false>
 __global__ __launch_bounds__(256) void k_transpose_mx(
     const void* __restrict__ src, const uint8_t* __restrict__ src_scales,
@@ -408,10 +409,26 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
     }
     return;
   }
-  const int64_t PB = P / 32;
   const int64_t kt = k0 + 8 * kc;                // first output row of this thread
-  uint8_t* o8 = out + kt * P + p;
-  uint8_t* oe = out_e8 + kt * PB + (p >> 5);
+  // output position: [cols, P], or with BLK group g's block [cols, glen] at
+  // cols * padded[g] (a 32-token chunk never straddles groups); the draw index
+  // is the [cols, P] position either way
+  int64_t ostep, estep;
+  uint8_t* o8;
+  uint8_t* oe;
+  if constexpr (BLK) {
+    const int g = grp_of[8 * pc];
+    const int64_t pg = padded[g], glen = padded[g + 1] - pg;
+    ostep = glen;
+    estep = glen / 32;
+    o8 = out + cols * pg + kt * glen + (p - pg);
+    oe = out_e8 + cols * (pg / 32) + kt * estep + ((p - pg) >> 5);
+  } else {
+    ostep = P;
+    estep = P / 32;
+    o8 = out + kt * P + p;
+    oe = out_e8 + kt * estep + (p >> 5);
+  }
   uint64_t q = (uint64_t)kt * (uint64_t)(P >> 3) + (uint64_t)(p >> 3);   // Philox counter
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -436,8 +453,8 @@ __global__ __launch_bounds__(256) void k_transpose_mx(
       *reinterpret_cast<uint2*>(o8) = make_uint2(lo, hi);
       if ((pc & 3) == 0) *oe = (uint8_t)code;
     }
-    o8 += P;
-    oe += PB;
+    o8 += ostep;
+    oe += estep;
     q += (uint64_t)(P >> 3);
   }
 }
@@ -489,8 +506,12 @@ hipError_t run_nv(const void* src, const uint8_t* sc, const float* so, int64_t r
 
 hipError_t launch_requant_sr(const uint8_t* codes, const uint8_t* scales, const float* outer,
                              int64_t rpg, int64_t rows, int64_t cols, const int64_t* offsets,
-                             const int64_t* padded, int G, int64_t P, uint64_t seed,
+                             const int64_t* padded, int G, int64_t P, bool blocked, uint64_t seed,
                              uint32_t tag, uint8_t* out, uint8_t* out_e8, hipStream_t stream) {
+  if (blocked)
+    return run<Src::NVFP4, true, false, false, true>(codes, scales, outer, rpg, rows, cols,
+                                                     offsets, padded, G, P, seed, tag, out,
+                                                     out_e8, stream);
   return run<Src::NVFP4, true>(codes, scales, outer, rpg, rows, cols, offsets, padded, G, P, seed,
                                tag, out, out_e8, stream);
 }

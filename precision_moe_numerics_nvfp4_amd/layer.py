@@ -48,7 +48,7 @@ class ExpertLayerStep:
         # backward
         self.w_off = torch.arange(E + 1, dtype=i64, device=dev) * N
         self.xT = (e(K, self.P), e(K, self.P // 32))
-        self.wT = (e(K, E * N), e(K, E * N // 32))
+        self.wT = (e(E * K, N), e(E * K, N // 32))           # per expert [K, N]
         self.dy8 = (e(cap, N), e(cap, N // 32))
         self.dyT = (e(N, self.P), e(N, self.P // 32))
         self.dx = e(cap, K, dt=out_dtype)
@@ -148,10 +148,10 @@ class ExpertFFNStep:
         self.dy2 = e(cap, K, dt=bf)
         self.dgate = torch.zeros((T, k), dtype=f32, device=dev)
         self.dy2_8, self.dy2T = mx(cap, K), mx(K, P)
-        self.hT, self.w2T = mx(F, P), mx(F, E * K)
+        self.hT, self.w2T = mx(F, P), mx(E * F, K)          # weights: per expert blocks
         self.dh = e(cap, F, dt=bf)
         self.dh8, self.dhT = mx(cap, F), mx(F, P)
-        self.xT, self.w1T = mx(K, P), mx(K, E * F)
+        self.xT, self.w1T = mx(K, P), mx(E * K, F)
         self.dxp = e(cap, K, dt=bf)
         self.dw1 = e(E, F, K, dt=f32)
         self.dw2 = e(E, K, F, dt=f32)

@@ -60,6 +60,21 @@ def assert_gemm_close(y, ref64, groups, absbound=None, tol=1e-3, what="gemm", el
             assert not viol.any(), f"{what}: {viol.sum()} elements exceed the summation error bound"
 
 
+def w8_blocked(a, G):
+    """A re-quantized weight in the oracle's [K, G*N] arrangement (or its
+    E8M0 bytes [K, G*N/32]) -> the library's per-expert blocks [G*K, N]."""
+    a = np.asarray(a)
+    K, GN = a.shape
+    return np.ascontiguousarray(a.reshape(K, G, GN // G).transpose(1, 0, 2)).reshape(G * K, GN // G)
+
+
+def w8_tokenwise(a, G):
+    """The inverse of w8_blocked: [G*K, N] -> [K, G*N]."""
+    a = np.asarray(a)
+    GK, N = a.shape
+    return np.ascontiguousarray(a.reshape(G, GK // G, N).transpose(1, 0, 2)).reshape(GK // G, G * N)
+
+
 def worst_elementwise(y, ref64, groups, floor=1e-2):
     """Largest |y - ref| / |ref| over elements with |ref| >= floor * (the
     group's max |ref|): the elementwise error a normwise contract allows."""

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     from precision_moe_numerics_nvfp4_amd import binding
-    assert L.nvfp4moe_abi_version() == 2
+    assert L.nvfp4moe_abi_version() == 3
     for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported size or alignment"),
                     (3, "workspace too small"), (4, "HIP launch or runtime error"), (99, "unknown status")]:
         assert binding.status_string(s) == text
@@ -86,7 +86,7 @@ def test_gemm_and_requant_argument_errors(L):
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 40, 128, 128, FAKE, None) == EUNSUP
     assert w(None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, FAKE, None) == EINVAL
     # 32-bit tile offsets and the in-kernel group ranking bound the sizes
-    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 8192, 64, 2048, 256, FAKE, 0, None) == EUNSUP
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 16711936, 256, FAKE, 0, None) == EUNSUP
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16711936 + 32 - 16711936 % 32, 128, 128, FAKE,
              None) == EUNSUP
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 16385, 64, 128, 128, FAKE, None) == EUNSUP

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import oracle_chunks as OC
-from helpers import assert_gemm_close, ensure_built, from_dev, sr_mean_sd, to_dev, worst_elementwise
+from helpers import (assert_gemm_close, ensure_built, from_dev, sr_mean_sd, to_dev, w8_tokenwise,
+                     worst_elementwise)
 from oracle import formats as F
 from oracle import gemm as GM
 from oracle import mxfp8 as MX
@@ -76,7 +77,8 @@ def _check_full_layer(L, w, dy, fwd_exact_rows=None):
     assert np.array_equal(h(L.xT[1])[:, :pt // 32], xe8[:, :pt // 32])
     woff = np.arange(E + 1) * N
     wq8, we8 = MX.requant_sr(wc, ws, wo, woff, woff, E * N, L.seed, 1, rows_per_group=N)
-    assert np.array_equal(h(L.wT[0]), wq8) and np.array_equal(h(L.wT[1]), we8)
+    assert np.array_equal(w8_tokenwise(h(L.wT[0]), E), wq8)
+    assert np.array_equal(w8_tokenwise(h(L.wT[1]), E), we8)
     dq, de = MX.quantize_rowwise(dy[:M])
     assert np.array_equal(h(L.dy8[0])[:M], dq) and np.array_equal(h(L.dy8[1])[:M], de)
     dtq, dte = MX.quantize_colwise_grouped(dy[:M], off, pad, P)
@@ -125,9 +127,9 @@ def test_small_moe_forward_and_backward_workload(torch_nv):
     sr_x = MX.dequantize(from_dev(L.xT[0])[:, :pt], from_dev(L.xT[1])[:, :pt // 32])
     N, E = w["N"], w["E"]
     v_w = Q.dequantize(r["wc"], r["ws"], r["wo"], rows_per_group=N).T.astype(np.float64)
-    sr_w = MX.dequantize(from_dev(L.wT[0]), from_dev(L.wT[1]))
+    sr_w = MX.dequantize(w8_tokenwise(from_dev(L.wT[0]), E), w8_tokenwise(from_dev(L.wT[1]), E))
     e_x = from_dev(L.xT[1])[:, :pt // 32]
-    e_w = from_dev(L.wT[1])
+    e_w = w8_tokenwise(from_dev(L.wT[1]), E)
     total = 0
     for v, sr, e in ((v_x, sr_x, e_x), (v_w, sr_w, e_w)):
         bias = (sr - v).mean()

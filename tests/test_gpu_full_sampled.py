@@ -15,7 +15,7 @@ the output is bfloat16.
 import numpy as np
 import pytest
 
-from helpers import ensure_built, from_dev, to_dev
+from helpers import ensure_built, from_dev, to_dev, w8_tokenwise
 from oracle import ffn as FF
 from oracle import formats as F
 from oracle import gemm as GM
@@ -178,7 +178,7 @@ def test_expert_ffn_full_size_sampled(nv, shape):
         assert np.array_equal(y8h[0][samp], r8[0]) and np.array_equal(y8h[1][samp], r8[1]), name
         yTh = tuple(h(a) for a in yT)
         sTh = tuple(h(a) for a in sT)
-        wTh = tuple(h(a) for a in wT)
+        wTh = tuple(w8_tokenwise(h(a), E) for a in wT)     # [K, E*N] as the oracle
         pt = int(poff[-1])
         woff = np.arange(E + 1, dtype=np.int64) * Nout
         for c0 in sorted({0, (Nout // 2) // 32 * 32, Nout - 32}):

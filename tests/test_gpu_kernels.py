@@ -25,7 +25,7 @@ must match bit for bit.
 import numpy as np
 import pytest
 
-from helpers import assert_gemm_close, ensure_built, from_dev, to_dev
+from helpers import assert_gemm_close, ensure_built, from_dev, to_dev, w8_blocked
 from oracle import ffn as FF
 from oracle import formats as F
 from oracle import gemm as GM
@@ -264,8 +264,11 @@ def test_requant_sr_weights(nv, E, N, K):
                                   E * N, seed, tag, rows_per_group=N)
     _sync()
     rq, re = MX.requant_sr(qc, qs, qo, off, off, E * N, seed, tag, rows_per_group=N)
-    assert np.array_equal(from_dev(out), rq)
-    assert np.array_equal(from_dev(oe), re)
+    # the library stores each expert's transposed block [K, N] contiguously:
+    # the oracle's [K, E*N] values, rearranged
+    assert from_dev(out).shape == (E * K, N)
+    assert np.array_equal(from_dev(out), w8_blocked(rq, E))
+    assert np.array_equal(from_dev(oe), w8_blocked(re, E))
 
 
 # ------------------------------------------------------------------ dY quantize
@@ -472,7 +475,8 @@ def test_dgrad(nv, counts, N, K, extra):
     dde = torch.zeros((cap, N // 32), dtype=torch.uint8, device="cuda")
     dde[:M] = to_dev(de)
     dx = torch.full((cap, K), float("nan"), dtype=torch.float32, device="cuda")
-    nv.moe_bwd_dgrad(ddq, dde, to_dev(wq), to_dev(we), to_dev(off), N, K, dx=dx)
+    nv.moe_bwd_dgrad(ddq, dde, to_dev(w8_blocked(wq, G)), to_dev(w8_blocked(we, G)), to_dev(off), N,
+                     K, dx=dx)
     _sync()
     got = from_dev(dx)
     assert np.all(np.isnan(got[M:]))
@@ -581,7 +585,8 @@ def test_backward_gemms_exact_case(nv):
     wT = r.integers(-4, 5, (K, G * N)).astype(np.float32)
     dq, de = _mx(dy)
     wq, we = _mx(wT)
-    dx = nv.moe_bwd_dgrad(to_dev(dq), to_dev(de), to_dev(wq), to_dev(we), to_dev(off), N, K)
+    dx = nv.moe_bwd_dgrad(to_dev(dq), to_dev(de), to_dev(w8_blocked(wq, G)),
+                          to_dev(w8_blocked(we, G)), to_dev(off), N, K)
     _sync()
     assert np.array_equal(from_dev(dx), GM.dgrad_grouped(dq, de, wq, we, off, N, accum="fp64").astype(np.float32))
     P = int(pad[-1])
