@@ -835,6 +835,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
   const int ntn = (int)(N / LT);
   int* pre = reinterpret_cast<int*>(persist ? lsm + kMainLds<NS> : lsm);      // [3G+1]
+  // the tile's 256 per-row outer scales, loaded by DMA with the first stage
+  float* rscale = reinterpret_cast<float*>(
+      lsm + kMainLds<NS> + (persist ? ((3 * G + 1) * 4 + 15) & ~15 : 0));
   tile_prefix(3 * G, [&](int e) {
     const int part = e / G, gg = e - part * G;
     const int64_t m = offsets[gg + 1] - offsets[gg], rem = m % LT;
@@ -892,6 +895,15 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
         first_lane_ptr(bs + brow0 * KSB), (short)0, (int)(uint32_t)(LT * KSB), kBufWord3);
     const __amdgpu_buffer_rsrc_t rnull = __builtin_amdgcn_make_buffer_rsrc(
         first_lane_ptr(bc), (short)0, 0, kBufWord3);
+    // per-row outer scales of rows row0 .. row0+255 into LDS (0 past the
+    // group), issued before the first stage so the prologue's wait covers it
+    if (wave < LT / 64) {
+      const __amdgpu_buffer_rsrc_t rao = __builtin_amdgcn_make_buffer_rsrc(
+          first_lane_ptr(ao + row0), (short)0, (int)(uint32_t)(arows * 4), kBufWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rao, (lds_void*)(rscale + wave * 64), 4,
+                                               (uint32_t)((wave * 64 + lane) * 4), 0, 0, 0);
+    }
+    const float sw = bo[g];
     // code DMA: A instructions m = wave, wave + 8 (rows 16m .. 16m+15), B the same
     uint32_t oac[2], obc[2];
 #pragma unroll
@@ -1135,12 +1147,10 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
     constexpr int ES = OUT_BF16 ? 2 : 4;
     constexpr int RS = 64 * ES + 16;
     uint8_t* ep = lsm + wave * (32 * RS);
-    const float sw = bo[g];
     const int64_t col0 = n0 + wn * 64;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int64_t row = row0 + (2 * i + wm) * 32 + r32;
-      const float sx = row < row_end ? ao[row] : 0.0f;
+      const float sx = rscale[(2 * i + wm) * 32 + r32];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -1182,6 +1192,8 @@ constexpr bool kFwdW8 = NVFP4MOE_FWD_W8 != 0;
 constexpr int kPersistFactor = 2;            // bound on tiles above this many per CU
 constexpr size_t kMaxPreBytes = 16384;       // tile-count scan kept in LDS (G <= 1365)
 static_assert(kMainLds<3> + kMaxPreBytes <= 160 * 1024, "LDS budget of k_fwd_lds4");
+constexpr size_t kW8RowScaleBytes = LT * 4;   // k_fwd_w8's per-row outer scales
+static_assert(kMainLds<3> + kMaxPreBytes + kW8RowScaleBytes <= 160 * 1024, "LDS budget of k_fwd_w8");
 
 template <int NS>
 hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
@@ -1225,13 +1237,13 @@ hipError_t launch_w8(const uint8_t* ac, const uint8_t* as, const float* ao, cons
   const size_t pre_bytes = ((size_t)(3 * G + 1) * 4 + 15) & ~(size_t)15;
   const bool persist = kFwdPersist && pre_bytes <= kMaxPreBytes &&
                        tiles > (int64_t)kPersistFactor * cus;
-  const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0);
+  const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0) + kW8RowScaleBytes;
   auto k = y_bf16 ? k_fwd_w8<NS, true> : k_fwd_w8<NS, false>;
   static bool attr_set[2] = {false, false};
   if (!attr_set[y_bf16]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)((size_t)kMainLds<NS> + kMaxPreBytes));
+                                       (int)((size_t)kMainLds<NS> + kMaxPreBytes + kW8RowScaleBytes));
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
