@@ -596,3 +596,50 @@ def test_backward_gemms_exact_case(nv):
     dw = nv.moe_bwd_wgrad(to_dev(dyq), to_dev(dye), to_dev(xq), to_dev(xe), to_dev(pad), N, K)
     _sync()
     assert np.array_equal(from_dev(dw), GM.wgrad_grouped(dyq, dye, xq, xe, pad, accum="fp64").astype(np.float32))
+
+
+# ------------------------------------------------------------------ launch-configuration determinism
+
+def test_forward_and_dgrad_bits_independent_of_launch_mode(nv):
+    """The same inputs in a buffer just past the routed rows (one workgroup
+    per tile) and in a capacity-sized buffer (a persistent grid, one
+    workgroup per compute unit looping over the tiles) give the same bits:
+    each output element is accumulated by one tile in the same order in both
+    launch modes. Groups: whole 256-row tiles, a 200-row partial tile and a
+    4-row tail."""
+    import torch
+    counts, K, N = [512, 200, 260, 768], 1024, 512
+    ac, asc, ao, wc, ws, wo, off = _fwd_counts_case(990, counts, K, N)
+    M = int(off[-1])
+    outs = []
+    for cap in (M + 40, 70000):              # tile bound below / above twice the compute units
+        dac = torch.zeros((cap, K // 2), dtype=torch.uint8, device="cuda")
+        dac[:M] = to_dev(ac)
+        das = torch.zeros((cap, K // 16), dtype=torch.uint8, device="cuda")
+        das[:M] = to_dev(asc)
+        dao = torch.zeros((cap,), dtype=torch.float32, device="cuda")
+        dao[:M] = to_dev(ao)
+        y = nv.moe_fwd_grouped_gemm(dac, das, dao, to_dev(wc), to_dev(ws), to_dev(wo), to_dev(off))
+        yb = nv.moe_fwd_grouped_gemm(dac, das, dao, to_dev(wc), to_dev(ws), to_dev(wo), to_dev(off),
+                                     out_dtype=torch.bfloat16)
+        _sync()
+        outs.append((from_dev(y)[:M], from_dev(yb)[:M]))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1], outs[1][1])
+    # dgrad over the same groups: contraction N = 512, output K = 1024
+    G = len(counts)
+    dy = gen.normal(991, 3, (M, N), std=1e-3)
+    wT = gen.normal(992, 1, (K, G * N), std=0.02)
+    dq, de = _mx(dy)
+    wq, we = _mx(wT)
+    w8, e8 = to_dev(w8_blocked(wq, G)), to_dev(w8_blocked(we, G))
+    dxs = []
+    for cap in (M + 33, 70000):
+        ddq = torch.zeros((cap, N), dtype=torch.uint8, device="cuda")
+        ddq[:M] = to_dev(dq)
+        dde = torch.zeros((cap, N // 32), dtype=torch.uint8, device="cuda")
+        dde[:M] = to_dev(de)
+        dx = nv.moe_bwd_dgrad(ddq, dde, w8, e8, to_dev(off), N, K)
+        _sync()
+        dxs.append(from_dev(dx)[:M])
+    assert np.array_equal(dxs[0].view(np.uint32), dxs[1].view(np.uint32))
