@@ -271,6 +271,35 @@ def test_requant_sr_weights(nv, E, N, K):
     assert np.array_equal(from_dev(oe), w8_blocked(re, E))
 
 
+def test_requant_sr_per_group_blocks_uneven(nv):
+    """The per-group (weight) mode through the C ABI with transpose groups of
+    different padded lengths (64, 160, 96) and short groups: group g's block
+    [cols, L_g] starts at element cols * padded[g], its E8M0 bytes at
+    cols * padded[g] / 32, and every byte equals the oracle's [cols, P]
+    result at the same (column, padded position), padding zeros included."""
+    import torch
+    from precision_moe_numerics_nvfp4_amd import binding as B
+    rows, cols, rpg = 256, 256, 64
+    w = gen.to_bf16_bits(gen.normal(470, 1, (rows, cols), std=0.02))
+    qc, qs, qo = Q.quantize(w, rows_per_group=rpg)
+    off = np.array([0, 40, 170, 256], dtype=np.int64)
+    pad = np.array([0, 64, 224, 320], dtype=np.int64)
+    P, G, seed, tag = 320, 3, 0x5EED0007, 1
+    out = torch.full((cols * P,), 0xCD, dtype=torch.uint8, device="cuda")
+    oe = torch.full((cols * P // 32,), 0xCD, dtype=torch.uint8, device="cuda")
+    dc, ds, do, doff, dpad = to_dev(qc), to_dev(qs), to_dev(qo), to_dev(off), to_dev(pad)
+    st = B.lib().mxfp8_requant_sr(B._ptr(dc), B._ptr(ds), B._ptr(do), 1, rpg, rows, cols,
+                                  B._ptr(doff), B._ptr(dpad), G, P, seed, tag, B._ptr(out),
+                                  B._ptr(oe), B._stream(dc))
+    assert st == 0
+    _sync()
+    rq, re = MX.requant_sr(qc, qs, qo, off, pad, P, seed, tag, rows_per_group=rpg)
+    want_q = np.concatenate([rq[:, pad[g]:pad[g + 1]].reshape(-1) for g in range(G)])
+    want_e = np.concatenate([re[:, pad[g] // 32:pad[g + 1] // 32].reshape(-1) for g in range(G)])
+    assert np.array_equal(from_dev(out), want_q)
+    assert np.array_equal(from_dev(oe), want_e)
+
+
 # ------------------------------------------------------------------ dY quantize
 
 @pytest.mark.parametrize("bf16,rows,cols", [(True, 100, 256), (False, 64, 512), (True, 1, 32), (True, 513, 2048)])
