@@ -254,8 +254,9 @@ def expert_share_forward(args, torch):
     avg = 0.5 * (t1 + t2)
     ach = fl / (avg * 1e-3)
     traffic = measured_traffic("moe_fwd_grouped_gemm_expert_share")
-    roof = {"kernel": "k_fwd_w8 (256x256 tiles, eight wavefronts, persistent) + k_fwd_stream "
-                      "(short tails), one moe_fwd_grouped_gemm call; both GEMMs of the step",
+    roof = {"kernel": "moe_fwd_grouped_gemm, 256x256 persistent tiles: k_fwd_lds4 (four "
+                      "wavefronts) for GEMM1 (K = 4096), k_fwd_w8 (eight wavefronts) for GEMM2 "
+                      "(K = 1536), k_fwd_stream for short tails; both GEMMs of the step",
             "bound": "mfma", "achieved": round(ach / 1e12, 2), "peak": PEAK["f16"] / 1e12,
             "unit": "TFLOP/s", "frac": round(ach / PEAK["f16"], 4), "traffic": traffic,
             "algorithmic_flop_per_launch": fl, "launch_ms_avg": round(avg, 4),
