@@ -393,6 +393,9 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   // scan of tile counts kept in LDS past the stage buffers); otherwise one
   // tile per workgroup (the scan's memory is then reused by the stages).
   int* pre = reinterpret_cast<int*>(persist ? lsm + kMainLds<NS> : lsm);      // [3G+1]
+  // the tile's 256 per-row outer scales (not WG), loaded by DMA with the first stage
+  float* rscale = reinterpret_cast<float*>(
+      lsm + kMainLds<NS> + (persist ? ((3 * G + 1) * 4 + 15) & ~15 : 0));
   int nfull = 0, nbig = 0, total = 0;
   if constexpr (!WG) {
     tile_prefix(3 * G, [&](int e) {
@@ -482,6 +485,14 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
       first_lane_ptr(bc + brow0 * KB + cb0), (short)0, (int)(uint32_t)(LT * KB), kBufWord3);
   const __amdgpu_buffer_rsrc_t rbs = __builtin_amdgcn_make_buffer_rsrc(
       first_lane_ptr(bs + brow0 * KSB + sb0), (short)0, (int)(uint32_t)(LT * KSB), kBufWord3);
+  if constexpr (!WG) {
+    // rows row0 .. row0+255 (0 past the group), one wavefront per 64 rows,
+    // issued before the first stage so the prologue's wait covers it
+    const __amdgpu_buffer_rsrc_t rao = __builtin_amdgcn_make_buffer_rsrc(
+        first_lane_ptr(ao + row0), (short)0, (int)(uint32_t)(arows * 4), kBufWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rao, (lds_void*)(rscale + wave * 64), 4,
+                                             (uint32_t)((wave * 64 + lane) * 4), 0, 0, 0);
+  }
 
   // DMA offsets of this lane: code instruction i of wavefront w fills rows
   // (4i + w) * 16 + lane / 4 at position lane % 4. Rows past the group end
@@ -769,8 +780,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   const int64_t obase = WG ? (int64_t)g * N * K : 0;    // WG: expert g's dW
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t row = row0 + (2 * i + wm) * 32 + r32;
-    const float sx = WG ? ao[g] : (row < row_end ? ao[row] : 0.0f);
+    const float sx = WG ? ao[g] : rscale[(2 * i + wm) * 32 + r32];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -1193,8 +1203,8 @@ constexpr int64_t kLds4MinK = 4096;          // contraction from which k_fwd_lds
 constexpr int kPersistFactor = 2;            // bound on tiles above this many per CU
 constexpr size_t kMaxPreBytes = 16384;       // tile-count scan kept in LDS (G <= 1365)
 static_assert(kMainLds<3> + kMaxPreBytes <= 160 * 1024, "LDS budget of k_fwd_lds4");
-constexpr size_t kW8RowScaleBytes = LT * 4;   // k_fwd_w8's per-row outer scales
-static_assert(kMainLds<3> + kMaxPreBytes + kW8RowScaleBytes <= 160 * 1024, "LDS budget of k_fwd_w8");
+constexpr size_t kRowScaleBytes = LT * 4;     // a tile's per-row outer scales
+static_assert(kMainLds<3> + kMaxPreBytes + kRowScaleBytes <= 160 * 1024, "LDS budget of the tiles");
 
 template <int NS>
 hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
@@ -1212,13 +1222,13 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
   const size_t pre_bytes = ((size_t)(3 * G + 1) * 4 + 15) & ~(size_t)15;
   const bool persist = kFwdPersist && pre_bytes <= kMaxPreBytes &&
                        tiles > (int64_t)kPersistFactor * cus;
-  const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0);
+  const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0) + kRowScaleBytes;
   auto k = y_bf16 ? k_fwd_lds4<NS, true> : k_fwd_lds4<NS, false>;
   static bool attr_set[2] = {false, false};
   if (!attr_set[y_bf16]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)((size_t)kMainLds<NS> + kMaxPreBytes));
+                                       (int)((size_t)kMainLds<NS> + kMaxPreBytes + kRowScaleBytes));
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
@@ -1238,13 +1248,13 @@ hipError_t launch_w8(const uint8_t* ac, const uint8_t* as, const float* ao, cons
   const size_t pre_bytes = ((size_t)(3 * G + 1) * 4 + 15) & ~(size_t)15;
   const bool persist = kFwdPersist && pre_bytes <= kMaxPreBytes &&
                        tiles > (int64_t)kPersistFactor * cus;
-  const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0) + kW8RowScaleBytes;
+  const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0) + kRowScaleBytes;
   auto k = y_bf16 ? k_fwd_w8<NS, true> : k_fwd_w8<NS, false>;
   static bool attr_set[2] = {false, false};
   if (!attr_set[y_bf16]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)((size_t)kMainLds<NS> + kMaxPreBytes + kW8RowScaleBytes));
+                                       (int)((size_t)kMainLds<NS> + kMaxPreBytes + kRowScaleBytes));
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
