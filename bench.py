@@ -55,8 +55,10 @@ FLUSH_BYTES = 512 << 20                  # scratch written between cold timings
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the shader clock takes some 50 ms of load to settle: 100 warmup steps
+    # of the headline (~80 ms), then 200 timed (~160 ms)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", choices=["fwd-share", "small-step", "stream", "ffn-share", "ffn-small",
                                        "nvfp4-bwd"], default=None,
@@ -248,7 +250,7 @@ def expert_share_forward(args, torch):
     fl = 2.0 * M * F * K                                # per GEMM
     value = 2 * fl / (ms_step * 1e-3) / 1e12
     # per-launch times on the launch stream (HIP events around graph replays)
-    reps = max(args.steps, 10)
+    reps = max(min(args.steps, 50), 10)
     t1 = graph_time(torch, gemm1, reps)
     t2 = graph_time(torch, gemm2, reps)
     avg = 0.5 * (t1 + t2)
@@ -357,7 +359,7 @@ def small_moe_step(args, torch, flush):
         graph.replay()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
-    reps = max(args.steps, 10)
+    reps = max(min(args.steps, 50), 10)
     warm = {name: graph_time(torch, fn, reps) for name, fn in stages}
     cold = {name: cold_time(torch, fn, 10, flush) for name, fn in stages}
 
@@ -962,7 +964,7 @@ def main():
     if not os.path.exists(binding.LIB_PATH):
         raise RuntimeError(f"{binding.LIB_PATH} is not built; run python -m "
                            "precision_moe_numerics_nvfp4_amd.build first")
-    reps = max(args.steps, 10)
+    reps = max(min(args.steps, 50), 10)          # graph replays per kernel timing
     if args.only in ("ffn-share", "ffn-small", "nvfp4-bwd"):
         rec = (nvfp4_backward_compare(torch, reps) if args.only == "nvfp4-bwd"
                else ffn_workload(torch, args.only, reps))

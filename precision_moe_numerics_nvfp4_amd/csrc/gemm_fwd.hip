@@ -30,11 +30,18 @@
 // Both run persistent (one workgroup per compute unit looping over the
 // tiles) when the bound on live tiles is far above one round.
 //
-// Tile order. Every group's full 256-row tiles first, then the partial last
-// tiles of more than 128 rows, then those of at most 128; each part is split
-// into 8 contiguous ranges, one per XCD (workgroup w runs on XCD w % 8), and
-// within a group the tiles go in blocks of 4 n-tiles, m-tile fastest, so the
-// workgroups an XCD runs together share weight and activation tiles in its L2.
+// Tile order. Five parts: every group's full 256-row tiles, then the partial
+// last tiles by their count of 64-row blocks (4, 3, 2, 1), the costliest
+// first (a partial tile runs MFMAs only for its valid row blocks). Each part
+// is split into 8 contiguous ranges, one per XCD (workgroup w runs on XCD
+// w % 8), and within a group the tiles go in blocks of 4 n-tiles, m-tile
+// fastest, so the workgroups an XCD runs together share weight and
+// activation tiles in its L2. An XCD's list is its range of part 0, then of
+// part 1, and so on; its workgroups take the list a round at a time, in
+// reverse order in odd rounds, so the workgroup that drew one of a round's
+// costlier tiles draws one of the next round's cheaper ones (the static
+// round-robin left the most loaded compute unit 14-19% above the mean at
+// the expert share's shapes).
 //
 // Other kernels. k_fwd_stream streams the weights for groups of a few rows
 // (decode: 16-row units), and takes the short tails of the 256-row tiles in a
@@ -350,6 +357,29 @@ template <int NS>
 constexpr int kMainLds = NS * kStageBytes + kScaleRing;
 constexpr int kBufWord3 = 0x00020000;     // raw buffer, 32-bit data format
 
+// Parts of the live-tile order (see "Tile order" above): part 0 the full
+// m-tiles, part p = 1..4 the partial last m-tiles with 5 - p 64-row blocks.
+constexpr int kParts = 5;
+__device__ __forceinline__ int tiles_in_part(int64_t m, int part) {
+  const int64_t rem = m % LT;
+  return part == 0 ? (int)(m / LT) : (rem != 0 && (int)((rem + 63) / 64) == kParts - part);
+}
+
+// Element i of XCD x's list (x of nx ranges): its range of part 0, then of
+// part 1, ... up to part nparts - 1, each part's tiles being pre[p*G] ..
+// pre[(p+1)*G] - 1; -1 past the list's end.
+__device__ __forceinline__ int xcd_list_tile(const int* pre, int G, int nparts, int x, int nx,
+                                             int i) {
+  for (int p = 0; p < nparts; ++p) {
+    const int a = pre[p * G], n = pre[(p + 1) * G] - a;
+    const int q = n / nx, r = n - q * nx;
+    const int c = q + (x < r ? 1 : 0);
+    if (i < c) return a + x * q + (x < r ? x : r) + i;
+    i -= c;
+  }
+  return -1;
+}
+
 // N dwords to LDS at a 4-byte-aligned address (the scale rows' pitch is not
 // a multiple of 8)
 template <int N, typename V>
@@ -381,62 +411,55 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   constexpr int TM = 4, TN = 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
 
-  // Tiles: every group's full 256-row tiles first (group, n-tile, m-tile
-  // fastest), then the partial last m-tiles of more than 128 rows, then those
-  // of at most 128; each part is split XCD-contiguously. Workgroups are
-  // dispatched in index order, so when the tiles outnumber the compute units
-  // the ones left for a second round are the cheapest (a partial tile runs
-  // MFMAs only for its valid row blocks).
+  // Tiles in the order described at the top of the file (not WG).
   const int ntn = (int)(N / LT);
-  // persist: the grid is at most one workgroup per compute unit and
-  // workgroup w runs the tiles w, w + gridDim, ... in the order above (the
-  // scan of tile counts kept in LDS past the stage buffers); otherwise one
-  // tile per workgroup (the scan's memory is then reused by the stages).
-  int* pre = reinterpret_cast<int*>(persist ? lsm + kMainLds<NS> : lsm);      // [3G+1]
+  // persist: the grid is at most one workgroup per compute unit and each
+  // workgroup loops over its XCD's list (the scan of tile counts kept in LDS
+  // past the stage buffers); otherwise one tile per workgroup (the scan's
+  // memory is then reused by the stages; the grid covers the longest list).
+  int* pre = reinterpret_cast<int*>(persist ? lsm + kMainLds<NS> : lsm);      // [5G+1]
   // the tile's 256 per-row outer scales (not WG), loaded by DMA with the first stage
   float* rscale = reinterpret_cast<float*>(
-      lsm + kMainLds<NS> + (persist ? ((3 * G + 1) * 4 + 15) & ~15 : 0));
-  int nfull = 0, nbig = 0, total = 0;
+      lsm + kMainLds<NS> + (persist ? ((kParts * G + 1) * 4 + 15) & ~15 : 0));
+  int nparts = 0;
   if constexpr (!WG) {
-    tile_prefix(3 * G, [&](int e) {
+    tile_prefix(kParts * G, [&](int e) {
       const int part = e / G, gg = e - part * G;
-      const int64_t m = offsets[gg + 1] - offsets[gg], rem = m % LT;
-      const int n = part == 0 ? (int)(m / LT)
-                  : part == 1 ? (rem > LT / 2 ? 1 : 0) : (rem != 0 && rem <= LT / 2 ? 1 : 0);
-      return n * ntn;
+      return tiles_in_part(offsets[gg + 1] - offsets[gg], part) * ntn;
     }, pre);
     // tail_cus > 0 (the compute-unit count): when the full and larger
-    // partial tiles fit in one round of workgroups and the short tails would
-    // start a second one, the tails are left to the streaming kernel launched
-    // right after this one (it takes the same decision)
-    nfull = pre[G];
-    nbig = pre[2 * G];
-    const int all = pre[3 * G];
-    total = tail_cus > 0 && nbig <= tail_cus && all > tail_cus ? nbig : all;
+    // partial tiles (parts 0-2, more than 128 rows) fit in one round of
+    // workgroups and the short tails would start a second one, the tails are
+    // left to the streaming kernel launched right after this one (it takes
+    // the same decision)
+    const int nbig = pre[3 * G], all = pre[kParts * G];
+    nparts = tail_cus > 0 && nbig <= tail_cus && all > tail_cus ? 3 : kParts;
   }
-  for (int v = (int)blockIdx.x;; v += (int)gridDim.x) {
+  // workgroup b is the j-th of its XCD's workgroups (nx XCDs when the grid
+  // is a multiple of 8, else one list)
+  const int nx = (gridDim.x & 7) == 0 ? 8 : 1, per = (int)gridDim.x / nx;
+  const int xcd = (int)blockIdx.x % nx, j0 = (int)blockIdx.x / nx;
+  for (int v = (int)blockIdx.x, round = 0;; v += (int)gridDim.x, ++round) {
   int g, nt;
   int64_t row0, row_end;
   if constexpr (WG) {
     // tiles expert by expert; inside an expert, blocks of 4 output-column
     // tiles with the output-row tile fastest
     const int nrt = (int)(N / LT), nct = (int)(K / LT);
-    const int per = nrt * nct, total_wg = G * per;
+    const int pg = nrt * nct, total_wg = G * pg;
     if (v >= total_wg) return;
     const int tt = (int)xcd_tile(v, total_wg);
-    g = tt / per;
+    g = tt / pg;
     int mi, ni;
-    block_order(tt - g * per, nrt, nct, mi, ni);
+    block_order(tt - g * pg, nrt, nct, mi, ni);
     nt = ni;
     row0 = (int64_t)mi * LT;
     row_end = row0 + LT;
   } else {
-    if (v >= total) return;
-    const int t = v;
-    const int tt = t < nfull ? (int)xcd_tile(t, nfull)
-                 : t < nbig  ? nfull + (int)xcd_tile(t - nfull, nbig - nfull)
-                             : nbig + (int)xcd_tile(t - nbig, total - nbig);
-    const int e = tile_group(pre, 3 * G, tt);
+    const int j = (round & 1) ? per - 1 - j0 : j0;
+    const int tt = xcd_list_tile(pre, G, nparts, xcd, nx, round * per + j);
+    if (tt < 0) return;
+    const int e = tile_group(pre, kParts * G, tt);
     const int loc = tt - pre[e];
     g = e % G;
     const int64_t o0 = offsets[g];
@@ -844,30 +867,27 @@ __global__ __launch_bounds__(512, 1) void k_fwd_w8(
   constexpr int TM = 4, TN = 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
   const int ntn = (int)(N / LT);
-  int* pre = reinterpret_cast<int*>(persist ? lsm + kMainLds<NS> : lsm);      // [3G+1]
+  int* pre = reinterpret_cast<int*>(persist ? lsm + kMainLds<NS> : lsm);      // [5G+1]
   // the tile's 256 per-row outer scales, loaded by DMA with the first stage
   float* rscale = reinterpret_cast<float*>(
-      lsm + kMainLds<NS> + (persist ? ((3 * G + 1) * 4 + 15) & ~15 : 0));
-  tile_prefix(3 * G, [&](int e) {
+      lsm + kMainLds<NS> + (persist ? ((kParts * G + 1) * 4 + 15) & ~15 : 0));
+  tile_prefix(kParts * G, [&](int e) {
     const int part = e / G, gg = e - part * G;
-    const int64_t m = offsets[gg + 1] - offsets[gg], rem = m % LT;
-    const int n = part == 0 ? (int)(m / LT)
-                : part == 1 ? (rem > LT / 2 ? 1 : 0) : (rem != 0 && rem <= LT / 2 ? 1 : 0);
-    return n * ntn;
+    return tiles_in_part(offsets[gg + 1] - offsets[gg], part) * ntn;
   }, pre);
-  const int nfull = pre[G], nbig = pre[2 * G], all = pre[3 * G];
-  const int total = tail_cus > 0 && nbig <= tail_cus && all > tail_cus ? nbig : all;
+  const int nbig = pre[3 * G], all = pre[kParts * G];
+  const int nparts = tail_cus > 0 && nbig <= tail_cus && all > tail_cus ? 3 : kParts;
+  const int nx = (gridDim.x & 7) == 0 ? 8 : 1, per = (int)gridDim.x / nx;
+  const int xcd = (int)blockIdx.x % nx, j0 = (int)blockIdx.x / nx;
 
-  for (int v = (int)blockIdx.x;; v += (int)gridDim.x) {
-    if (v >= total) return;
+  for (int round = 0;; ++round) {
     int g, nt;
     int64_t row0, row_end;
     {
-      const int t = v;
-      const int tt = t < nfull ? (int)xcd_tile(t, nfull)
-                   : t < nbig  ? nfull + (int)xcd_tile(t - nfull, nbig - nfull)
-                               : nbig + (int)xcd_tile(t - nbig, total - nbig);
-      const int e = tile_group(pre, 3 * G, tt);
+      const int j = (round & 1) ? per - 1 - j0 : j0;
+      const int tt = xcd_list_tile(pre, G, nparts, xcd, nx, round * per + j);
+      if (tt < 0) return;
+      const int e = tile_group(pre, kParts * G, tt);
       const int loc = tt - pre[e];
       g = e % G;
       const int64_t o0 = offsets[g];
@@ -1201,10 +1221,17 @@ constexpr bool kFwdPersist = NVFP4MOE_FWD_PERSIST != 0;
 constexpr bool kFwdW8 = NVFP4MOE_FWD_W8 != 0;
 constexpr int64_t kLds4MinK = 4096;          // contraction from which k_fwd_lds4 runs instead
 constexpr int kPersistFactor = 2;            // bound on tiles above this many per CU
-constexpr size_t kMaxPreBytes = 16384;       // tile-count scan kept in LDS (G <= 1365)
+constexpr size_t kMaxPreBytes = 16384;       // tile-count scan kept in LDS (G <= 818)
 static_assert(kMainLds<3> + kMaxPreBytes <= 160 * 1024, "LDS budget of k_fwd_lds4");
 constexpr size_t kRowScaleBytes = LT * 4;     // a tile's per-row outer scales
 static_assert(kMainLds<3> + kMaxPreBytes + kRowScaleBytes <= 160 * 1024, "LDS budget of the tiles");
+constexpr int kMaxTileGroups = 4096;         // the scan of 5G + 1 counts fits the stage buffers
+static_assert((kParts * kMaxTileGroups + 1) * 4 <= kMainLds<3>, "tile-count scan of one tile");
+
+// Grid of the one-tile-per-workgroup mode for a bound of `tiles` live tiles:
+// a multiple of 8 with room for the longest XCD list (each of the five parts
+// adds at most one tile above an even split).
+inline int64_t one_tile_grid(int64_t tiles) { return (tiles + 8 * kParts + 7) / 8 * 8; }
 
 template <int NS>
 hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
@@ -1219,7 +1246,7 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
   // (e.g. a capacity-sized down-projection: 17152 workgroups for 2336 tiles).
   // The tile-count scan then stays in LDS beside the stages.
   const int64_t cus = device_cu_count();
-  const size_t pre_bytes = ((size_t)(3 * G + 1) * 4 + 15) & ~(size_t)15;
+  const size_t pre_bytes = ((size_t)(kParts * G + 1) * 4 + 15) & ~(size_t)15;
   const bool persist = kFwdPersist && pre_bytes <= kMaxPreBytes &&
                        tiles > (int64_t)kPersistFactor * cus;
   const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0) + kRowScaleBytes;
@@ -1232,7 +1259,7 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
-  const int64_t grid = persist ? cus : tiles;
+  const int64_t grid = persist ? cus : one_tile_grid(tiles);
   k<<<(unsigned)grid, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, 0,
                                           tail_cus, persist ? 1 : 0);
   return hipGetLastError();
@@ -1245,7 +1272,7 @@ hipError_t launch_w8(const uint8_t* ac, const uint8_t* as, const float* ao, cons
                      hipStream_t stream) {
   const int64_t tiles = ((m_cap + LT - 1) / LT + G) * (N / LT);   // bound on live tiles
   const int64_t cus = device_cu_count();
-  const size_t pre_bytes = ((size_t)(3 * G + 1) * 4 + 15) & ~(size_t)15;
+  const size_t pre_bytes = ((size_t)(kParts * G + 1) * 4 + 15) & ~(size_t)15;
   const bool persist = kFwdPersist && pre_bytes <= kMaxPreBytes &&
                        tiles > (int64_t)kPersistFactor * cus;
   const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0) + kRowScaleBytes;
@@ -1258,7 +1285,7 @@ hipError_t launch_w8(const uint8_t* ac, const uint8_t* as, const float* ao, cons
     if (e != hipSuccess) return e;
     attr_set[y_bf16] = true;
   }
-  const int64_t grid = persist ? cus : tiles;
+  const int64_t grid = persist ? cus : one_tile_grid(tiles);
   k<<<(unsigned)grid, 512, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, tail_cus,
                                           persist ? 1 : 0);
   return hipGetLastError();
@@ -1608,7 +1635,7 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
     return launch_stream(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, false,
                          stream);
   // 32-row tiles, the wavefronts split N
-  if (m_cap <= 64 * (int64_t)G || N % 256 != 0 || G > 8192)
+  if (m_cap <= 64 * (int64_t)G || N % 256 != 0 || G > kMaxTileGroups)
     return launch_cfg<32, 128, 1, 4>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
                                      stream);
   // 256 x 256 tiles; when the partial last m-tiles of at most 128 rows would
