@@ -257,8 +257,7 @@ def expert_share_forward(args, torch):
     ach = fl / (avg * 1e-3)
     traffic = measured_traffic("moe_fwd_grouped_gemm_expert_share")
     roof = {"kernel": "moe_fwd_grouped_gemm, 256x256 persistent tiles: k_fwd_lds4 (four "
-                      "wavefronts) for GEMM1 (K = 4096), k_fwd_w8 (eight wavefronts) for GEMM2 "
-                      "(K = 1536), k_fwd_stream for short tails; both GEMMs of the step",
+                      "wavefronts of 128x128) for both GEMMs, k_fwd_stream for short tails",
             "bound": "mfma", "achieved": round(ach / 1e12, 2), "peak": PEAK["f16"] / 1e12,
             "unit": "TFLOP/s", "frac": round(ach / PEAK["f16"], 4), "traffic": traffic,
             "algorithmic_flop_per_launch": fl, "launch_ms_avg": round(avg, 4),

@@ -22,13 +22,15 @@
 // (v_cvt_scalef32_pk_f16_fp4 at unit scale, then an exact v_pk_mul_f16 by
 // the block's E4M3 scale) a step ahead of the MFMAs that use them, so the
 // conversions co-issue with the matrix pipe. One barrier per stage.
-// k_fwd_w8 (the default) runs eight wavefronts, two per SIMD, of 128 x 64;
-// k_fwd_lds4 four, one per SIMD, of 128 x 128 (fewer conversions per MFMA,
-// no second wavefront to cover waits; it is also the NVFP4 weight-gradient
-// kernel). A wavefront's 32-row blocks alternate with the other wavefront
-// row's (block 2i + wm), so a partial tile's rows are spread over all SIMDs.
-// Both run persistent (one workgroup per compute unit looping over the
-// tiles) when the bound on live tiles is far above one round.
+// k_fwd_lds4 runs four wavefronts, one per SIMD, of 128 x 128 (it is also the
+// NVFP4 weight-gradient kernel); an eight-wavefront form (two per SIMD, 128 x
+// 64 each, so one's waits overlap the other's MFMAs, but 6 conversions per 4
+// MFMAs where this one has 4 per 4) measured 3-6% slower at contractions of
+// 1024 and 1536 and 2-4% at 4096, and was removed. A wavefront's 32-row
+// blocks alternate with the other wavefront row's (block 2i + wm), so a
+// partial tile's rows are spread over all SIMDs. It runs persistent (one
+// workgroup per compute unit looping over the tiles) when the bound on live
+// tiles is far above one round.
 //
 // Tile order. Five parts: every group's full 256-row tiles, then the partial
 // last tiles by their count of 64-row blocks (4, 3, 2, 1), the costliest
@@ -839,387 +841,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd_lds4(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Large tiles, two wavefronts per SIMD (k_fwd_w8). The 256 x 256 tile and its
-// LDS layout are k_fwd_lds4's (raw NVFP4 codes by DMA, three stages in
-// flight; the scale ring; the tile order, the persistent mode), but eight
-// wavefronts share it: wavefront w owns tile rows of blocks 2i + w / 4 and the
-// 64 columns (w % 4) * 64 .., a 128 x 64 piece (4 x 2 MFMA tiles, 128
-// accumulator registers), so two wavefronts share each SIMD and one's DMA
-// issues, conversions and barrier waits overlap the other's MFMAs. Each
-// wavefront converts its own fragments right before the MFMAs that use them;
-// the A fragments are converted by four wavefronts, the weight fragments by
-// two.
-//
-// Per stage: read chunk 0 of the lane's rows and the stage's scales, write
-// the scale piece loaded a stage earlier, steps 0-3, read chunk 1 (the
-// stage's last LDS read), barrier (stage kt+1 landed, every wavefront done
-// with stage kt), load the next scale piece and issue stage kt+3's codes into
-// stage kt's buffer, steps 4-7.
-constexpr int kW8Waves = 8;
-
-template <int NS, bool OUT_BF16>
-__global__ __launch_bounds__(512, 1) void k_fwd_w8(
-    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ao,
-    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bo,
-    const int64_t* __restrict__ offsets, int G, int64_t N, int64_t K, void* __restrict__ y,
-    int tail_cus, int persist) {
-  constexpr int TM = 4, TN = 2;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
-  const int ntn = (int)(N / LT);
-  int* pre = reinterpret_cast<int*>(persist ? lsm + kMainLds<NS> : lsm);      // [5G+1]
-  // the tile's 256 per-row outer scales, loaded by DMA with the first stage
-  float* rscale = reinterpret_cast<float*>(
-      lsm + kMainLds<NS> + (persist ? ((kParts * G + 1) * 4 + 15) & ~15 : 0));
-  tile_prefix(kParts * G, [&](int e) {
-    const int part = e / G, gg = e - part * G;
-    return tiles_in_part(offsets[gg + 1] - offsets[gg], part) * ntn;
-  }, pre);
-  const int nbig = pre[3 * G], all = pre[kParts * G];
-  const int nparts = tail_cus > 0 && nbig <= tail_cus && all > tail_cus ? 3 : kParts;
-  const int nx = (gridDim.x & 7) == 0 ? 8 : 1, per = (int)gridDim.x / nx;
-  const int xcd = (int)blockIdx.x % nx, j0 = (int)blockIdx.x / nx;
-
-  for (int round = 0;; ++round) {
-    int g, nt;
-    int64_t row0, row_end;
-    {
-      const int j = (round & 1) ? per - 1 - j0 : j0;
-      const int tt = xcd_list_tile(pre, G, nparts, xcd, nx, round * per + j);
-      if (tt < 0) return;
-      const int e = tile_group(pre, kParts * G, tt);
-      const int loc = tt - pre[e];
-      g = e % G;
-      const int64_t o0 = offsets[g];
-      row_end = offsets[g + 1];
-      const int64_t fm = (row_end - o0) / LT;
-      if (e < G) {
-        int mi, ni;
-        block_order(loc, (int)fm, ntn, mi, ni);
-        nt = ni;
-        row0 = o0 + (int64_t)mi * LT;
-      } else {
-        nt = loc;
-        row0 = o0 + fm * LT;
-      }
-      __syncthreads();   // the scan's memory (one tile) or the last epilogue's staging is reused
-    }
-    const int64_t n0 = (int64_t)nt * LT;
-    int tid_ = threadIdx.x;
-    asm volatile("" : "+v"(tid_));                     // per tile (see k_fwd_lds4)
-    const int tid = tid_, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
-    const int half = lane >> 5, r32 = lane & 31;
-    const int64_t KB = K / 2, KSB = K / 16;
-    const int arows = __builtin_amdgcn_readfirstlane(
-        (int)(row_end - row0 < LT ? row_end - row0 : LT));
-    const __amdgpu_buffer_rsrc_t rac = __builtin_amdgcn_make_buffer_rsrc(
-        first_lane_ptr(ac + row0 * KB), (short)0, (int)(uint32_t)(arows * KB), kBufWord3);
-    const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
-        first_lane_ptr(as + row0 * KSB), (short)0, (int)(uint32_t)(arows * KSB), kBufWord3);
-    const int64_t brow0 = (int64_t)g * N + n0;
-    const __amdgpu_buffer_rsrc_t rbc = __builtin_amdgcn_make_buffer_rsrc(
-        first_lane_ptr(bc + brow0 * KB), (short)0, (int)(uint32_t)(LT * KB), kBufWord3);
-    const __amdgpu_buffer_rsrc_t rbs = __builtin_amdgcn_make_buffer_rsrc(
-        first_lane_ptr(bs + brow0 * KSB), (short)0, (int)(uint32_t)(LT * KSB), kBufWord3);
-    const __amdgpu_buffer_rsrc_t rnull = __builtin_amdgcn_make_buffer_rsrc(
-        first_lane_ptr(bc), (short)0, 0, kBufWord3);
-    // per-row outer scales of rows row0 .. row0+255 into LDS (0 past the
-    // group), issued before the first stage so the prologue's wait covers it
-    if (wave < LT / 64) {
-      const __amdgpu_buffer_rsrc_t rao = __builtin_amdgcn_make_buffer_rsrc(
-          first_lane_ptr(ao + row0), (short)0, (int)(uint32_t)(arows * 4), kBufWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rao, (lds_void*)(rscale + wave * 64), 4,
-                                               (uint32_t)((wave * 64 + lane) * 4), 0, 0, 0);
-    }
-    const float sw = bo[g];
-    // code DMA: A instructions m = wave, wave + 8 (rows 16m .. 16m+15), B the same
-    uint32_t oac[2], obc[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = (wave + 8 * i) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ chunk_key(r);
-      const int ra = r < arows ? r : 0;
-      oac[i] = (uint32_t)(ra * KB + c * 16);
-      obc[i] = (uint32_t)(r * KB + c * 16);
-    }
-    // scale pieces: in stage-group q a thread moves 8 bytes, piece tid % 4 of
-    // row q * 128 + tid / 4 of the 512 (A rows, then B rows)
-    uint32_t osc[SBK];
-#pragma unroll
-    for (int q = 0; q < SBK; ++q) {
-      const int r = (q & 1) * 128 + (tid >> 2);
-      const int rr = q < 2 ? (r < arows ? r : 0) : r;
-      osc[q] = (uint32_t)(rr * KSB + (tid & 3) * 8);
-    }
-    const int64_t nk = K / LBK;
-    auto issue = [&](int64_t kt) {
-      uint8_t* st = lsm + (kt % NS) * kStageBytes;
-      const bool real = kt < nk;
-      const int so = (int)((real ? kt : 0) * LCB);
-      const __amdgpu_buffer_rsrc_t xac = real ? rac : rnull, xbc = real ? rbc : rnull;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xac, (lds_void*)(st + (wave + 8 * i) * 1024), 16,
-                                                 oac[i], so, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xbc, (lds_void*)(st + LT * LCB + (wave + 8 * i) * 1024), 16, obc[i], so, 0, 0);
-    };
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 spiece;
-    auto load_piece = [&](int64_t kt) {      // the piece stage kt writes
-      const int q = (int)(kt % SBK);
-      const int64_t blk = kt / SBK + 1;
-      // (a branch-free select: a branch here would split the step's schedule)
-      const uint32_t off = osc[0] * (q == 0) + osc[1] * (q == 1) + osc[2] * (q == 2) +
-                           osc[3] * (q == 3) + (uint32_t)(blk * kScaleRow);
-      spiece = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(q < 2 ? ras : rbs,
-                                                                             off, 0, 0));
-    };
-    // thread tid moves 8-byte piece tid % 4 of row q * 128 + tid / 4
-    const int piece_dst = (tid >> 2) * kScalePitch + (tid & 3) * 8;
-    auto store_piece = [&](int64_t kt) {
-      const int q = (int)(kt % SBK);
-      const int64_t blk = kt / SBK + 1;
-      st_dwords<2>(lsm + NS * kStageBytes + (blk & 1) * kScaleSlot + q * 128 * kScalePitch +
-                   piece_dst, spiece);
-    };
-
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    // fragment rows: A blocks 2i + wm, B columns wn * 64 + 32 j
-    int fa[TM], fb[TN], sa_off[TM], sb_off[TN], swa[TM], swb[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = (2 * i + wm) * 32 + r32;
-      fa[i] = r * LCB;
-      swa[i] = chunk_key(r);
-      sa_off[i] = NS * kStageBytes + r * kScalePitch + half * 4;
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = wn * 64 + j * 32 + r32;
-      fb[j] = LT * LCB + r * LCB;
-      swb[j] = chunk_key(r);
-      sb_off[j] = NS * kStageBytes + (LT + r) * kScalePitch + half * 4;
-    }
-
-    auto mainloop = [&](auto ta_c) {
-      constexpr int TA = decltype(ta_c)::value;
-      constexpr int TAA = TA > 0 ? TA : 1;
-      // Codes in quarters: quarter q (8 bytes of the lane's 32 per fragment
-      // row) feeds steps 2q and 2q+1; QA holds quarters 0 and 2, QB 1 and 3.
-      // The f16 fragments are double-buffered: step s runs its MFMAs on
-      // buffer s % 2 while converting step s+1's into the other (step 7
-      // converts the next stage's step 0), so the conversions co-issue with
-      // the wavefront's own MFMAs.
-      typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-      u32x2v qa_a[TAA], qa_b[TN], qb_a[TAA], qb_b[TN];
-      uint32_t sca[TAA], scb[TN];
-      f16x2 sfa[TAA][2], sfb[TN][2];
-      f16x8 fa_[2][TAA], fb_[2][TN];
-      auto read_quarter = [&](const uint8_t* st, int q, u32x2v (&ra)[TAA], u32x2v (&rb)[TN]) {
-        if constexpr (TA == 0) return;
-        const int c = q >> 1, o = (q & 1) * 8;
-#pragma unroll
-        for (int i = 0; i < TA; ++i)
-          ra[i] = *reinterpret_cast<const u32x2v*>(st + fa[i] + (((2 * half + c) ^ swa[i]) << 4) + o);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          rb[j] = *reinterpret_cast<const u32x2v*>(st + fb[j] + (((2 * half + c) ^ swb[j]) << 4) + o);
-      };
-      auto read_scales = [&](int64_t kt) {
-        if constexpr (TA == 0) return;
-        const uint8_t* sc = lsm + ((kt / SBK) & 1) * kScaleSlot + (kt % SBK) * LSB;
-#pragma unroll
-        for (int i = 0; i < TA; ++i) sca[i] = *reinterpret_cast<const uint32_t*>(sc + sa_off[i]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) scb[j] = *reinterpret_cast<const uint32_t*>(sc + sb_off[j]);
-      };
-      auto cvt_scales = [&]() {        // E4M3 -> f16, exact
-        if constexpr (TA == 0) return;
-#pragma unroll
-        for (int i = 0; i < TA; ++i) {
-          sfa[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sca[i], 1.0f, false);
-          sfa[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sca[i], 1.0f, true);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          sfb[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scb[j], 1.0f, false);
-          sfb[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scb[j], 1.0f, true);
-        }
-      };
-      auto deq = [&](uint32_t x, f16x2 sp, int hi) -> f16x8 {
-        const _Float16 S = hi ? sp[1] : sp[0];
-        const f16x2 s2 = {S, S};
-        const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s2;
-        const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s2;
-        const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s2;
-        const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s2;
-        return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      };
-      // the f16 fragments of step s (0..7) into buffer s % 2: dword s % 2 of
-      // quarter s / 2, block s / 2 of the lane's four (scale pair s / 4,
-      // element (s / 2) % 2)
-      auto convert = [&](auto s_c) {
-        constexpr int s = decltype(s_c)::value, B = s & 1, q = s >> 1;
-        if constexpr (TA == 0) return;
-#pragma unroll
-        for (int i = 0; i < TA; ++i)
-          fa_[B][i] = deq((q & 1) ? qb_a[i][s & 1] : qa_a[i][s & 1], sfa[i][(s >> 2) & 1],
-                          (s >> 1) & 1);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          fb_[B][j] = deq((q & 1) ? qb_b[j][s & 1] : qa_b[j][s & 1], sfb[j][(s >> 2) & 1],
-                          (s >> 1) & 1);
-      };
-      // step s: the conversions of step s+1 (program order: before `extra`,
-      // which may replace their sources), then the MFMAs of step s,
-      // interleaved with them
-      auto step = [&](auto s_c, auto&& extra) {
-        constexpr int s = decltype(s_c)::value, B = s & 1;
-        if constexpr (TA == 0) {
-          extra();
-          return;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        convert(std::integral_constant<int, (s + 1) & 7>{});
-        extra();
-#pragma unroll
-        for (int i = 0; i < TA; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb_[B][j], fa_[B][i], acc[i][j],
-                                                              0, 0, 0);
-        constexpr int NM = TAA * TN, NVALU = (TAA + TN) * 8, PV = (NVALU + NM - 1) / NM;
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);                 // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);                  // global loads
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, PV, 0);               // conversions
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      };
-      auto none = [] {};
-      using S0 = std::integral_constant<int, 0>;
-      using S1 = std::integral_constant<int, 1>;
-      using S2 = std::integral_constant<int, 2>;
-      using S3 = std::integral_constant<int, 3>;
-      using S4 = std::integral_constant<int, 4>;
-      using S5 = std::integral_constant<int, 5>;
-      using S6 = std::integral_constant<int, 6>;
-      using S7 = std::integral_constant<int, 7>;
-      static_assert(NS == 3 && SBK == 4, "wait counts assume 3 stages, 4 loads per stage");
-      // prologue: scale block 0 (four pieces), the piece stage 0 writes, then
-      // the code stages 0..2 (4 loads each); once stage 0 has landed, its
-      // quarter 0 and scales, and step 0's fragments
-      {
-        u32x2 p0[SBK];
-#pragma unroll
-        for (int q = 0; q < SBK; ++q)
-          p0[q] = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_raw_buffer_load_b64(q < 2 ? ras : rbs, osc[q], 0, 0));
-        load_piece(0);
-#pragma unroll
-        for (int p = 0; p < NS; ++p) issue(p);
-#pragma unroll
-        for (int q = 0; q < SBK; ++q)
-          st_dwords<2>(lsm + NS * kStageBytes + q * 128 * kScalePitch + piece_dst, p0[q]);
-      }
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage 0 landed
-      read_quarter(lsm, 0, qa_a, qa_b);
-      read_scales(0);
-      cvt_scales();
-      convert(S0{});
-      for (int64_t kt = 0; kt < nk; ++kt) {
-        const uint8_t* st = lsm + (kt % NS) * kStageBytes;
-        const uint8_t* sn = lsm + ((kt + 1) % NS) * kStageBytes;
-        step(S0{}, [&] { store_piece(kt); read_quarter(st, 1, qb_a, qb_b); });
-        step(S1{}, [&] { read_quarter(st, 2, qa_a, qa_b); });
-        step(S2{}, none);
-        step(S3{}, [&] { read_quarter(st, 3, qb_a, qb_b); });
-        // every wavefront is done with stage kt (quarter 3 was its last
-        // read); stage kt+1 has landed once only stage kt+2's four code
-        // loads are pending (the scale piece was issued before them); this
-        // stage's piece write is visible
-        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        step(S4{}, [&] { load_piece(kt + 1); issue(kt + NS); });
-        // quarter 0 and scales of stage kt+1 (past the end: unused bytes)
-        step(S5{}, [&] { read_quarter(sn, 0, qa_a, qa_b); read_scales(kt + 1); });
-        step(S6{}, [&] { cvt_scales(); });
-        step(S7{}, none);
-      }
-    };
-    {
-      const int nblk = (arows + 31) >> 5;
-      const int act = nblk > wm ? (nblk - wm + 1) >> 1 : 0;
-      if (act >= 4) mainloop(std::integral_constant<int, 4>{});
-      else if (act == 3) mainloop(std::integral_constant<int, 3>{});
-      else if (act == 2) mainloop(std::integral_constant<int, 2>{});
-      else if (act == 1) mainloop(std::integral_constant<int, 1>{});
-      else mainloop(std::integral_constant<int, 0>{});
-    }
-
-    // Epilogue: acc[i][j][4q+v] = Y[row, col], row = (2i + wm)*32 + lane%32,
-    // col = wn*64 + j*32 + 8q + 4*half + v; each wavefront stages one 32-row
-    // block at a time in LDS and writes it out 16 bytes per lane along rows.
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");   // stage buffers are free
-    constexpr int ES = OUT_BF16 ? 2 : 4;
-    constexpr int RS = 64 * ES + 16;
-    uint8_t* ep = lsm + wave * (32 * RS);
-    const int64_t col0 = n0 + wn * 64;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const float sx = rscale[(2 * i + wm) * 32 + r32];
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float vv[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) vv[t] = __fmul_rn(__fmul_rn(acc[i][j][4 * q + t], sx), sw);
-          uint8_t* d = ep + r32 * RS + (j * 32 + 8 * q + 4 * half) * ES;
-          if constexpr (OUT_BF16) {
-            *reinterpret_cast<uint2*>(d) = make_uint2(pk_bf16(vv[0], vv[1]), pk_bf16(vv[2], vv[3]));
-          } else {
-            *reinterpret_cast<float4*>(d) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-          }
-        }
-      constexpr int PPR = 64 * ES / 16;                  // pieces per row
-#pragma unroll
-      for (int it = 0; it < 32 * PPR / 64; ++it) {
-        const int pc = it * 64 + lane, r = pc / PPR, c = pc % PPR;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(ep + r * RS + c * 16);
-        const int64_t orow = row0 + (2 * i + wm) * 32 + r;
-        if (orow < row_end)
-          __builtin_nontemporal_store(
-              val, reinterpret_cast<u32x4*>(static_cast<uint8_t*>(y) + (orow * N + col0) * ES +
-                                            c * 16));
-      }
-    }
-    if (!persist) return;
-  }
-}
-
 #ifndef NVFP4MOE_FWD_PERSIST
 #define NVFP4MOE_FWD_PERSIST 1
 #endif
 constexpr bool kFwdPersist = NVFP4MOE_FWD_PERSIST != 0;
-#ifndef NVFP4MOE_FWD_W8
-#define NVFP4MOE_FWD_W8 1
-#endif
-constexpr bool kFwdW8 = NVFP4MOE_FWD_W8 != 0;
-constexpr int64_t kLds4MinK = 4096;          // contraction from which k_fwd_lds4 runs instead
 constexpr int kPersistFactor = 2;            // bound on tiles above this many per CU
 constexpr size_t kMaxPreBytes = 16384;       // tile-count scan kept in LDS (G <= 818)
 static_assert(kMainLds<3> + kMaxPreBytes <= 160 * 1024, "LDS budget of k_fwd_lds4");
@@ -1262,32 +887,6 @@ hipError_t launch_lds4(const uint8_t* ac, const uint8_t* as, const float* ao, co
   const int64_t grid = persist ? cus : one_tile_grid(tiles);
   k<<<(unsigned)grid, 256, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, 0,
                                           tail_cus, persist ? 1 : 0);
-  return hipGetLastError();
-}
-
-template <int NS>
-hipError_t launch_w8(const uint8_t* ac, const uint8_t* as, const float* ao, const uint8_t* bc,
-                     const uint8_t* bs, const float* bo, const int64_t* offsets, int G,
-                     int64_t m_cap, int64_t N, int64_t K, void* y, bool y_bf16, int tail_cus,
-                     hipStream_t stream) {
-  const int64_t tiles = ((m_cap + LT - 1) / LT + G) * (N / LT);   // bound on live tiles
-  const int64_t cus = device_cu_count();
-  const size_t pre_bytes = ((size_t)(kParts * G + 1) * 4 + 15) & ~(size_t)15;
-  const bool persist = kFwdPersist && pre_bytes <= kMaxPreBytes &&
-                       tiles > (int64_t)kPersistFactor * cus;
-  const size_t lds = (size_t)kMainLds<NS> + (persist ? pre_bytes : 0) + kRowScaleBytes;
-  auto k = y_bf16 ? k_fwd_w8<NS, true> : k_fwd_w8<NS, false>;
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[y_bf16]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)((size_t)kMainLds<NS> + kMaxPreBytes + kRowScaleBytes));
-    if (e != hipSuccess) return e;
-    attr_set[y_bf16] = true;
-  }
-  const int64_t grid = persist ? cus : one_tile_grid(tiles);
-  k<<<(unsigned)grid, 512, lds, stream>>>(ac, as, ao, bc, bs, bo, offsets, G, N, K, y, tail_cus,
-                                          persist ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1646,14 +1245,8 @@ hipError_t launch_fwd_grouped_gemm(const uint8_t* ac, const uint8_t* as, const f
   const bool tails = ((m_cap + LT - 1) / LT + G) * (N / LT) > (int64_t)device_cu_count() &&
                      K % SK_K == 0 && N % SK_N == 0 && G <= SK_MAXG &&
                      (int64_t)G * (LT / 2 / SK_T) * (N / SK_N) < (int64_t)1 << 31;
-  // eight wavefronts below K = 4096; at 4096 and above the four-wavefront
-  // tile (fewer conversions per MFMA, one wavefront per SIMD) measured 2-4%
-  // faster (4096 -> 1536 and 2048-wide shapes), at K = 1536 the same
-  const bool w8 = kFwdW8 && K < kLds4MinK;
-  hipError_t e = w8 ? launch_w8<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
-                                   tails ? (int)device_cu_count() : 0, stream)
-                    : launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y,
-                                     y_bf16, tails ? (int)device_cu_count() : 0, stream);
+  hipError_t e = launch_lds4<3>(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16,
+                                tails ? (int)device_cu_count() : 0, stream);
   if (e != hipSuccess || !tails) return e;
   return launch_stream(ac, as, ao, bc, bs, bo, offsets, G, m_cap, N, K, y, y_bf16, true, stream);
 }

@@ -1,5 +1,5 @@
-"""Host replay of the 256 x 256 forward kernels' tile order (k_fwd_lds4 and
-k_fwd_w8 in csrc/gemm_fwd.hip): every live tile must be run exactly once,
+"""Host replay of the 256 x 256 forward kernel's tile order (k_fwd_lds4 in
+csrc/gemm_fwd.hip): every live tile must be run exactly once,
 by the persistent grid (one workgroup per compute unit, each looping over
 its XCD's list, reversed in odd rounds) and by the one-tile-per-workgroup
 grid (round 0 only), with and without the short tails left to the streaming
