@@ -924,6 +924,7 @@ constexpr int SK_XS = SK_WS + SK_N * SK_SB;   // [16][32] activation scales
 constexpr int SK_STAGE = SK_XS + SK_T * SK_SB;
 constexpr int SK_DMA = 5;                     // DMA instructions per stage and wavefront
 constexpr int SK_RED = 4 * 64 * 16;           // partial sums of the upper K halves
+constexpr int SK_USC = 8 * 128 * 4;           // output scales of 8 units: [8][64 rows + 64 x group]
 constexpr int SK_MAXG = 1024;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -946,7 +947,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
     int tail) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lsm[];
   float* red = reinterpret_cast<float*>(lsm + SK_S * SK_STAGE);      // [4][64 lanes][4]
-  int64_t* off = reinterpret_cast<int64_t*>(lsm + SK_S * SK_STAGE + SK_RED);   // [G+1]
+  // a unit's 16 row scales and its expert's scale, by DMA with its first stage
+  float* usc = reinterpret_cast<float*>(lsm + SK_S * SK_STAGE + SK_RED);        // [8][128]
+  int64_t* off = reinterpret_cast<int64_t*>(lsm + SK_S * SK_STAGE + SK_RED + SK_USC);   // [G+1]
   int* pre = reinterpret_cast<int*>(off + G + 1);                     // [G+1]
   const int nnb = (int)(N / SK_N);
   for (int e = threadIdx.x; e <= G; e += 512) off[e] = offsets[e];
@@ -1030,7 +1033,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
   // Past the end of the stream the last stage is re-issued with offsets
   // outside the ranges (zeros, no memory traffic), keeping the count per stage.
   int ij = 0, ist = 0, ibuf = 0;
-  __amdgpu_buffer_rsrc_t rwc, rws, rxc, rxs;
+  __amdgpu_buffer_rsrc_t rwc, rws, rxc, rxs, rxo, rgo;
   int ixrows = 0;
   auto set_unit = [&](int j) {
     const Unit u = unit(j);
@@ -1044,10 +1047,20 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
                                             (int)(uint32_t)(ixrows * KB), kBufWord3);
     rxs = __builtin_amdgcn_make_buffer_rsrc(first_lane_ptr(as + u.row0 * KSB), (short)0,
                                             (int)(uint32_t)(ixrows * KSB), kBufWord3);
+    rxo = __builtin_amdgcn_make_buffer_rsrc(first_lane_ptr(ao + u.row0), (short)0,
+                                            (int)(uint32_t)(ixrows * 4), kBufWord3);
+    rgo = __builtin_amdgcn_make_buffer_rsrc(first_lane_ptr(bo + u.g), (short)0, 4, kBufWord3);
   };
   set_unit(0);
   auto issue = [&]() {
     const uint32_t away = ij < nunits ? 0u : 0x40000000u;
+    // the first stage of a unit also brings the unit's output scales (wave 0:
+    // row r's at slot + r, rows past the unit read 0; the expert's at slot + 64
+    // + lane); issued after the stage's loads, so each wait that covers the
+    // stage covers them, and read at the unit's last stage
+    const bool first = ist == 0 && ij < nunits;
+    float* uslot = usc + (ij & 7) * 128;
+    const __amdgpu_buffer_rsrc_t uxo = rxo, ugo = rgo;
     uint8_t* sb = lsm + ibuf * SK_STAGE;
     const int cofs = ist * SK_RB, sofs = ist * SK_SB;
 #pragma unroll
@@ -1066,6 +1079,11 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
       const int xr = xrow_s < ixrows ? xrow_s : 0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_void*)(sb + SK_XS + (wave & 1) * 256), 4,
                                                (uint32_t)(xr * KSB + sdw) + away, sofs, 0, 0);
+    }
+    if (first && wave == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(uxo, (lds_void*)uslot, 4, (uint32_t)(lane * 4), 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ugo, (lds_void*)(uslot + 64), 4, 0u, 0, 0, 0);
     }
     ibuf = ibuf + 1 == SK_S ? 0 : ibuf + 1;
     if (ij < nunits && ++ist == nst) {
@@ -1097,28 +1115,12 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
   // compute cursor: stage cst of unit cj, in ring buffer cbuf
   int cj = 0, cst = 0, cbuf = 0;
   Unit cu = unit(0);
-  float sx = 0.0f, sg = 0.0f;
   for (int i = 0; i < nall; ++i) {
     // stage i has landed once only the 3 younger stages' loads are pending,
     // and every wavefront is done with the buffer that stage i+4 reuses
     asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory");
     issue();
     const int st = cst;
-    if (st == 0) {
-      // a new unit: its output scales, through scalar loads (uniform
-      // addresses), which a vector-memory wait would otherwise have to
-      // cover together with every load in flight
-      float sr[SK_T];
-#pragma unroll
-      for (int t = 0; t < SK_T; ++t) {
-        const int64_t row = rfl64(cu.row0 + t < cu.row_end ? cu.row0 + t : cu.row0);
-        sr[t] = __builtin_nontemporal_load(ao + row);
-      }
-      sx = sr[0];
-#pragma unroll
-      for (int t = 1; t < SK_T; ++t) sx = r == t ? sr[t] : sx;
-      sg = bo[cu.g];
-    }
     const uint8_t* sb = lsm + cbuf * SK_STAGE;
     cbuf = cbuf + 1 == SK_S ? 0 : cbuf + 1;
     u32x4 wv[2], xv[2];
@@ -1149,6 +1151,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_stream(
       if (wk == 0) {
         acc += *reinterpret_cast<const f32x4*>(red + (wn * 64 + lane) * 4);
         const Unit u = cu;
+        const float sx = usc[(cj & 7) * 128 + r], sg = usc[(cj & 7) * 128 + 64];
         const int64_t row = u.row0 + r;
         if (row < u.row_end) {
           float o[4];
@@ -1182,7 +1185,7 @@ hipError_t launch_stream(const uint8_t* ac, const uint8_t* as, const float* ao, 
                          int64_t m_cap, int64_t N, int64_t K, void* y, bool y_bf16,
                          bool tail, hipStream_t stream) {
   auto k = y_bf16 ? k_fwd_stream<true> : k_fwd_stream<false>;
-  const size_t base = (size_t)SK_S * SK_STAGE + SK_RED;
+  const size_t base = (size_t)SK_S * SK_STAGE + SK_RED + SK_USC;
   const size_t lds = base + (size_t)(G + 1) * (sizeof(int64_t) + sizeof(int));
   static bool attr_set[2] = {false, false};
   if (!attr_set[y_bf16]) {
